@@ -1,0 +1,230 @@
+/*
+ * nq.h -- C ABI of libnq.so: fused normalization + FP8 / NVFP4 activation
+ * quantization for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (title, then the section in brackets):
+ *   [FUSE]  "Fusing RMSNorm and FP8 Quantization Under torch.compile"
+ *   [LNQ]   "feat: fused FP8 quantization output for LayerNorm"
+ *           (FlashInfer pull request 3962)
+ *   [NVFP4] "RMSNorm nvfp4 quant fusion for DS V3.2 / Kimi-K2.5"
+ *           (TensorRT-LLM pull request 14848)
+ *   [GRP]   "per_token_group_quant_8bit: multiply by reciprocal instead of
+ *           dividing per element" (vLLM pull request 61343)
+ *   [GRAPH] "RMSNorm/FusedRMSNorm + Quant kernels cuda graph fixes"
+ *           (FlashInfer pull request 2459)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Types.  bf16 tensors are passed as uint16_t bit patterns; OCP FP8 e4m3fn
+ *   codes (largest finite 448, no infinities), packed E2M1 pairs and e4m3
+ *   block-scale codes as uint8_t; scales as IEEE float.
+ * Layout.  Every matrix is row-major.  A leading dimension `ld_*` is the
+ *   distance between consecutive rows, in elements of that tensor, and must
+ *   be >= the row length that is read or written.  A row stride larger than
+ *   the row length reads a column slice in place.
+ * Memory.  Every pointer is a device pointer (hipMalloc / PyTorch CUDA
+ *   memory) owned by the caller.  The library never allocates, frees or
+ *   synchronizes; all work is enqueued on `stream` (a hipStream_t passed as
+ *   void*; NULL selects the null stream).  Scale pointers are read on the
+ *   device when the kernel runs, never on the host, so every call can be
+ *   captured into a hipGraph and a scale updated between replays is honoured
+ *   ([LNQ] "Tests"; [GRAPH] "Description").
+ * Errors.  Arguments are checked on the host before anything is enqueued.  A
+ *   non-zero status means nothing was launched, except NQ_ERR_LAUNCH, which
+ *   reports a failed launch.  M == 0 is a no-op that returns NQ_OK.
+ *   Misaligned pointers or strides are not errors: they select a slower
+ *   element-wise path with identical results.
+ * Device-side preconditions (documented, not checked: checking would need a
+ *   host synchronization): inputs and scales are finite, static scales and
+ *   the NVFP4 global scale are > 0, and no group or row has a non-zero
+ *   absolute maximum below 448 * 2^-126 (so every derived scale is a normal
+ *   binary32 number).
+ * Aliasing.  No output may overlap an input or another output, except that
+ *   residual_out may be exactly residual_in (same pointer, same ld: in-place
+ *   residual update, [FUSE] "FAQ").  Overlap is judged on address ranges.
+ * Threads.  The library keeps no mutable global state; calls are thread-safe.
+ */
+#ifndef NQ_H
+#define NQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int nq_status;
+
+#define NQ_OK 0
+#define NQ_ERR_NULL (-1)        /* a mandatory pointer is NULL */
+#define NQ_ERR_SHAPE (-2)       /* M < 0, d <= 0, d above NQ_MAX_D, d % 16 for NVFP4, K % group */
+#define NQ_ERR_STRIDE (-3)      /* a leading dimension is smaller than the row length */
+#define NQ_ERR_ALIAS (-4)       /* an output overlaps an input or another output */
+#define NQ_ERR_LAUNCH (-5)      /* the HIP launch failed (hipGetLastError) */
+#define NQ_ERR_ARG (-6)         /* an argument value is outside its domain (eps, mode, group) */
+
+/* Largest row length any entry point accepts. */
+#define NQ_MAX_D 32768
+
+/* Group-quant scale encodings ([GRP] "Overview", "Details"). */
+#define NQ_SCALE_FP32 0         /* s = amax / 448 */
+#define NQ_SCALE_UE8M0 1        /* s = amax / 448 rounded up to a power of two */
+
+/*
+ * Fused (residual-add +) RMSNorm + per-token FP8 e4m3.
+ * Defined by [FUSE] "TL;DR", "Where norm+quant sits" and "FAQ"; the static
+ * variant's one-element device scale by [GRAPH] "Description", "Changes".
+ *
+ * Per row m (0 <= m < M) and column i (0 <= i < d):
+ *   z_i  = bf16(x_i + r_i)        binary32 add, one bf16 rounding (RNE);
+ *                                 z_i = x_i when residual_in is NULL
+ *   residual_out_i = z_i          (bit-exact; may update residual_in in place)
+ *   rstd = 1 / sqrt(sum_i z_i^2 / d + eps)
+ *   y_i  = (z_i * rstd) * gamma_i kept in fp32 registers, never rounded to bf16
+ *   dynamic (static_scale == NULL):
+ *     s = max_i |y_i| / 448  -> scale_out[m];  q_i = e4m3(y_i / s)  (0 if s == 0)
+ *   static (static_scale != NULL):
+ *     q_i = e4m3(y_i * (1 / static_scale[0]))  i.e. out = y / scale
+ *   norm_out_i = bf16(y_i)        only when norm_out != NULL
+ * e4m3() clamps to [-448, 448] and rounds to nearest-even.
+ *
+ *   x            [M, d] bf16, row stride ld_x               (read)
+ *   residual_in  [M, d] bf16, row stride ld_r, or NULL       (read)
+ *   residual_out [M, d] bf16, row stride ld_ro; NULL iff residual_in is NULL
+ *   gamma        [d] fp32                                   (read)
+ *   eps          > 0 added inside the square root
+ *   static_scale one fp32 on the device, or NULL for dynamic per-token scales
+ *   q_out        [M, d] e4m3 codes, row stride ld_q          (written)
+ *   scale_out    [M] fp32 per-token scales; required when dynamic, unused
+ *                (may be NULL) when static
+ *   norm_out     [M, d] bf16, row stride ld_n, or NULL
+ */
+nq_status nq_fused_add_rmsnorm_quant_fp8(
+    const uint16_t* x, int64_t ld_x,
+    const uint16_t* residual_in, int64_t ld_r,
+    uint16_t* residual_out, int64_t ld_ro,
+    const float* gamma, float eps,
+    const float* static_scale,
+    uint8_t* q_out, int64_t ld_q,
+    float* scale_out,
+    uint16_t* norm_out, int64_t ld_n,
+    int64_t M, int64_t d, void* stream);
+
+/*
+ * LayerNorm + static per-tensor FP8 e4m3.
+ * Defined by [LNQ] "Description" (the scale divides: out = normed / scale)
+ * and the review thread; the scale is a one-element device tensor read when
+ * the kernel runs ([LNQ] "Tests"; [GRAPH] "Changes").
+ *
+ * Per row:
+ *   mu   = sum_i x_i / d
+ *   c_i  = x_i - mu
+ *   rstd = 1 / sqrt(sum_i c_i^2 / d + eps)      (population variance)
+ *   y_i  = ((c_i * rstd) * gamma_i) + beta_i    (no fused multiply-add)
+ *   q_i  = e4m3(y_i * (1 / scale[0]))
+ *
+ *   x      [M, d] bf16, row stride ld_x
+ *   gamma, beta [d] fp32
+ *   scale  one fp32 on the device (> 0)
+ *   q_out  [M, d] e4m3 codes, row stride ld_q
+ */
+nq_status nq_layernorm_quant_fp8(
+    const uint16_t* x, int64_t ld_x,
+    const float* gamma, const float* beta, float eps,
+    const float* scale,
+    uint8_t* q_out, int64_t ld_q,
+    int64_t M, int64_t d, void* stream);
+
+/*
+ * Per-token-group FP8 e4m3 with one reciprocal per group.
+ * Defined by [GRP] "Overview", "Details" and the commit message: scales are
+ * amax / 448 per group of `group_size` contiguous elements, and elements are
+ * multiplied by the correctly rounded reciprocal of the scale.
+ *
+ * Per row m and group g (K / group_size groups per row):
+ *   amax = max |x_i| over the group
+ *   NQ_SCALE_FP32:  s = amax / 448
+ *   NQ_SCALE_UE8M0: s = amax / 448 rounded up to a power of two
+ *                   (unchanged when already a power of two or zero)
+ *   inv  = 1 / s (0 when s == 0);  q_i = e4m3(x_i * inv)
+ *   scale_out[m * (K / group_size) + g] = s
+ *
+ *   x          [M, K] bf16, row stride ld_x
+ *   group_size 128 (the only size the pages use); K % group_size == 0
+ *   q_out      [M, K] e4m3 codes, row stride ld_q
+ *   scale_out  [M, K / group_size] fp32, dense row-major
+ */
+nq_status nq_per_token_group_quant_fp8(
+    const uint16_t* x, int64_t ld_x, int64_t M, int64_t K,
+    int32_t group_size, int32_t scale_mode,
+    uint8_t* q_out, int64_t ld_q, float* scale_out, void* stream);
+
+/*
+ * (Residual-add +) RMSNorm + NVFP4: packed E2M1 elements with one e4m3 scale
+ * per 16 elements and a global fp32 decode scale.
+ * Defined by [NVFP4] "Description" and the commit notes (optional residual,
+ * row-strided column-slice input, d % 16 == 0, optional bf16 norm_out, a
+ * fresh or in-place residual).  The block-scale formula is printed on no
+ * page; this library uses:
+ *   z, residual_out, rstd, y_i   exactly as nq_fused_add_rmsnorm_quant_fp8
+ *   G    = 1 / global_scale[0]                    (encode scale)
+ *   per block b of 16 elements:
+ *     sf_b = e4m3((max |y_i| / 6) * G)            -> block_scale
+ *     m_b  = G / value(sf_b)  (0 when sf_b decodes to 0)
+ *     q_i  = e2m1(y_i * m_b)  (clamped to [-6, 6], nearest-even)
+ *   so that y_i ~= value(q_i) * value(sf_b) * global_scale[0].
+ * Packing: byte k of a block holds element 2k in bits 0-3 and element 2k+1
+ * in bits 4-7; E2M1 bit 3 is the sign, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
+ *
+ *   x            [M, d] bf16, row stride ld_x (may be a column slice)
+ *   residual_in  [M, d] bf16, row stride ld_r, or NULL (residual-less)
+ *   residual_out [M, d] bf16, row stride ld_ro; NULL iff residual_in is NULL
+ *   gamma        [d] fp32
+ *   global_scale one fp32 on the device (> 0)
+ *   q_packed     [M, d/2] bytes, row stride ld_q (in bytes)
+ *   block_scale  [M, d/16] e4m3 codes, row stride ld_sf, linear layout
+ *   norm_out     [M, d] bf16, row stride ld_n, or NULL
+ */
+nq_status nq_rmsnorm_quant_nvfp4(
+    const uint16_t* x, int64_t ld_x,
+    const uint16_t* residual_in, int64_t ld_r,
+    uint16_t* residual_out, int64_t ld_ro,
+    const float* gamma, float eps,
+    const float* global_scale,
+    uint8_t* q_packed, int64_t ld_q,
+    uint8_t* block_scale, int64_t ld_sf,
+    uint16_t* norm_out, int64_t ld_n,
+    int64_t M, int64_t d, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* nq_status_string(nq_status status);
+
+/* Library version string, e.g. "nq 0.1.0 gfx950" (static storage). */
+const char* nq_version(void);
+
+/*
+ * Diagnostics (not part of the quantization path).
+ *
+ * nq_diag_codec: applies, element by element on the device, the exact device
+ * conversion routine the kernels use, so its rounding can be compared with an
+ * independent host implementation.  kind:
+ *   NQ_CODEC_E4M3: out[i] = e4m3 code of in[i]   (clamp to +-448, nearest-even)
+ *   NQ_CODEC_E2M1: out[i] = E2M1 code of in[i]   (clamp to +-6, nearest-even)
+ *   NQ_CODEC_BF16: out16[i] = bf16 bits of in[i] (nearest-even)
+ * `out` is uint8_t for the 8-bit formats and uint16_t for bf16.
+ *
+ * nq_diag_copy: copies `bytes` (a multiple of 16, both pointers 16-byte
+ * aligned) with 128-bit loads and stores, a bandwidth reference for the same
+ * HBM the quantization kernels stream through.
+ */
+#define NQ_CODEC_E4M3 0
+#define NQ_CODEC_E2M1 1
+#define NQ_CODEC_BF16 2
+nq_status nq_diag_codec(int32_t kind, const float* in, void* out, int64_t n, void* stream);
+nq_status nq_diag_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NQ_H */

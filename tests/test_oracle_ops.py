@@ -1,0 +1,430 @@
+"""Pins of the oracle's operations against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself:
+  * an independent binary64 recomputation written here with PyTorch/numpy
+    (the exact result within its rounding bound),
+  * PyTorch's bf16 add and float8_e4m3fn cast (library routines),
+  * closed forms and special cases (constant rows, all-zero rows/groups),
+  * invariants and statistics the pages state (tests/golden/page_figures.json).
+A plausible slip in the oracle -- a dropped residual, eps outside the square
+root, a mean over d-1, a transposed gamma, a divide where a reciprocal is
+meant, a wrong group boundary -- fails at least one of them.
+
+Pages: [FUSE] "Fusing RMSNorm and FP8 Quantization Under torch.compile";
+[LNQ] "feat: fused FP8 quantization output for LayerNorm"; [NVFP4] "RMSNorm
+nvfp4 quant fusion for DS V3.2 / Kimi-K2.5"; [GRP] "per_token_group_quant_8bit:
+multiply by reciprocal instead of dividing per element".
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from fp4_quantization_amd import workloads as W
+from fp4_quantization_amd import traffic
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+DELTA = 2.0 ** -17  # relative width of the "too close to a rounding boundary to call" band
+
+
+def bf(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16)
+
+
+def torch_e4m3(v) -> np.ndarray:
+    t = torch.from_numpy(np.clip(np.asarray(v, np.float32), -448, 448))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e4m3_value(codes) -> np.ndarray:
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+
+
+def robust_codes(q64: np.ndarray):
+    """e4m3 code of a binary64 quotient, and whether it is unambiguous: the
+    code is the same at q*(1-DELTA) and q*(1+DELTA)."""
+    lo = torch_e4m3((q64 * (1 - DELTA)).astype(np.float32))
+    hi = torch_e4m3((q64 * (1 + DELTA)).astype(np.float32))
+    return hi, lo == hi
+
+
+def ref64_rms(x_bits, r_bits, gamma, eps, d):
+    """Independent binary64 RMSNorm: z from PyTorch's bf16 add."""
+    x = bf(x_bits[:, :d])
+    z = (x + bf(r_bits[:, :d])) if r_bits is not None else x
+    z64 = z.double().numpy()
+    rstd = 1.0 / np.sqrt((z64 * z64).mean(axis=1) + eps)
+    return z, z64 * rstd[:, None] * gamma[:d].astype(np.float64)[None, :]
+
+
+def same_value(a, b):
+    """e4m3 codes equal as values (+0 and -0 are the same number)."""
+    a = np.asarray(a); b = np.asarray(b)
+    return (a == b) | (((a & 0x7F) == 0) & ((b & 0x7F) == 0))
+
+
+# --------------------------------------------- O2 fused add+RMSNorm+FP8 ----
+
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+@pytest.mark.parametrize("wl", ["small", "2816"])
+def test_rmsnorm_fp8_matches_binary64(orc, wl, eps):
+    w = W.rms_small() if wl == "small" else W.rms_2816(M=128)
+    d = w["d"]
+    o = orc.fused_add_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], eps, want_y=True)
+    z, y64 = ref64_rms(w["x"], w["residual"], w["gamma"], eps, d)
+    # residual: bit-exact with PyTorch's bf16 add ([FUSE] "FAQ": 0.000 difference)
+    assert np.array_equal(o["residual_out"], z.view(torch.int16).numpy().view(np.uint16))
+    # y within a few binary32 roundings of the binary64 value
+    assert np.max(np.abs(o["y"] - y64) / np.maximum(np.abs(y64), 1e-30)) < 1e-6
+    s64 = np.abs(y64).max(axis=1) / 448.0
+    assert np.max(np.abs(o["scale"] - s64) / s64) < 1e-6
+    codes, ok = robust_codes(y64 / s64[:, None])
+    assert ok.mean() > 0.999
+    assert np.all(same_value(o["q"][ok], codes[ok]))
+
+
+def test_rmsnorm_fp8_absmax_maps_to_448_and_scale_definition(orc):
+    """The absmax element of every row codes to +-448 and scale = amax/448
+    (one binary32 division of the row's fp32 absmax)."""
+    for w in (W.rms_small(), W.rms_2816(M=64)):
+        o = orc.fused_add_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], w["eps"], want_y=True)
+        y = o["y"]
+        arg = np.abs(y).argmax(axis=1)
+        top = o["q"][np.arange(y.shape[0]), arg]
+        assert np.all((top & 0x7F) == 0x7E)
+        amax = np.abs(y).max(axis=1).astype(np.float32)
+        assert np.array_equal(o["scale"], (amax / np.float32(448.0)).astype(np.float32))
+        assert np.all(np.abs(e4m3_value(o["q"])) <= 448.0)
+
+
+def test_rmsnorm_fp8_round_trip_bound(orc):
+    """|dec(q)*s - y| <= half an e4m3 ulp of y/s, times s (plus binary32 slack)."""
+    w = W.rms_2816(M=32)
+    o = orc.fused_add_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], w["eps"], want_y=True)
+    y = o["y"].astype(np.float64)
+    s = o["scale"].astype(np.float64)[:, None]
+    v = np.abs(y / s)
+    ulp = np.where(v >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(v, 2.0 ** -6))) - 3), 2.0 ** -9)
+    err = np.abs(e4m3_value(o["q"]).astype(np.float64) * s - y)
+    assert np.all(err <= 0.5 * ulp * s * (1 + 1e-6) + 1e-12)
+
+
+def test_rmsnorm_fp8_static_scale_is_divisor(orc):
+    """Static: q = E4(y * (1/scale)) -- out = normed / scale ([LNQ]
+    "Description"; scale_inv = 1/scale[0] in [GRAPH] "Changes")."""
+    w = W.rms_small()
+    for scale in (0.01, 0.05, 1.0, 10.0):
+        o = orc.fused_add_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], w["eps"],
+                                            static_scale=scale, want_y=True)
+        inv = np.float32(1.0) / np.float32(scale)
+        assert np.array_equal(o["q"], torch_e4m3(o["y"] * inv))
+        _, y64 = ref64_rms(w["x"], w["residual"], w["gamma"], w["eps"], w["d"])
+        codes, ok = robust_codes(y64 / scale)
+        assert np.all(same_value(o["q"][ok], codes[ok]))
+
+
+def test_rmsnorm_fp8_residual_less_and_strided(orc):
+    w = W.rms_rows(8, 1536, 0, 1.0, seed=5, residual=False, ld=2112)
+    o = orc.fused_add_rmsnorm_quant_fp8(w["x"], None, w["gamma"], 1e-6, d=1536, want_y=True)
+    _, y64 = ref64_rms(w["x"], None, w["gamma"], 1e-6, 1536)
+    assert o["residual_out"] is None
+    assert np.max(np.abs(o["y"] - y64) / np.abs(y64)) < 1e-6
+
+
+def test_rmsnorm_fp8_constant_row_and_zero_row(orc):
+    d = 256
+    x = np.zeros((3, d), np.uint16)
+    x[0] = W.to_bf16_bits(np.full(d, 0.75, np.float32))
+    x[1] = W.to_bf16_bits(np.full(d, -3.0, np.float32))
+    g = np.ones(d, np.float32)
+    o = orc.fused_add_rmsnorm_quant_fp8(x, None, g, 1e-6)
+    assert np.all(o["q"][0] == 0x7E) and np.all(o["q"][1] == 0xFE)
+    assert o["scale"][2] == 0.0 and np.all(o["q"][2] == 0)
+
+
+def test_per_token_quant_divides_per_element(orc):
+    """Per-token FP8 keeps one division per element ([GRP] "Details": per-token
+    FP8 keeps exact per-element division).  Rows are built from fp32 values
+    for which RN(y/s) and RN(y * RN(1/s)) fall on different sides of an e4m3
+    rounding boundary; the oracle must give the division's code."""
+    rng = np.random.default_rng(11)
+    found = []
+    while len(found) < 8:
+        amax = np.float32(rng.uniform(1.0, 2.0))
+        s = amax / np.float32(448.0)
+        inv = np.float32(1.0) / s
+        y = rng.uniform(-amax, amax, 200_000).astype(np.float32)
+        qd = torch_e4m3(y / s)
+        qm = torch_e4m3(y * inv)
+        bad = np.nonzero(qd != qm)[0]
+        if bad.size:
+            found.append((amax, y[bad[:16]]))
+    for amax, ys in found:
+        row = np.concatenate([[amax], ys]).astype(np.float32)[None, :]
+        o = orc.quant_fp8_rows(row)
+        s = amax / np.float32(448.0)
+        assert o["scale"][0] == s
+        assert np.array_equal(o["q"][0], torch_e4m3(row[0] / s))
+        assert not np.array_equal(o["q"][0], torch_e4m3(row[0] * (np.float32(1.0) / s)))
+
+
+def test_rmsnorm_fp8_norm_out_is_bf16_of_y(orc):
+    w = W.rms_small(M=8)
+    o = orc.fused_add_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], w["eps"],
+                                        want_y=True, want_norm_out=True)
+    assert np.array_equal(o["norm_out"], W.to_bf16_bits(o["y"]))
+
+
+# ---------------------------- fused vs unfused statistics ([FUSE] Gating) ---
+
+@pytest.mark.parametrize("wl", ["small", "2816"])
+def test_fused_vs_unfused_statistics(orc, wl):
+    w = W.rms_small() if wl == "small" else W.rms_2816(M=256)
+    f = orc.fused_add_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], w["eps"], want_y=True)
+    u = orc.unfused_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], w["eps"])
+    differ = ~same_value(f["q"], u["q"])
+    frac = differ.mean()
+    g = GOLDEN["fused_vs_unfused_codes_differ_frac"]
+    a = GOLDEN["fused_vs_unfused_code_agreement_frac"]
+    # The page states this one quantity twice: 2-3% of codes differ, and
+    # 96.7-97.8% agree.  Accept the union of the two ranges (2.0-3.3%
+    # differing), each widened by half a unit of its last printed digit.
+    lo = min(g["min"], 1 - a["max"]) - 0.0005
+    hi = max(g["max"], 1 - a["min"]) + 0.0005
+    assert lo <= frac <= hi, frac
+    # never more than one code step apart (same sign, adjacent magnitude)
+    fi = f["q"].astype(np.int32); ui = u["q"].astype(np.int32)
+    assert np.all(np.abs((fi & 0x7F) - (ui & 0x7F))[differ] == 1)
+    # scale error of the bf16-sourced scale: bounded by bf16's unit roundoff
+    # 2^-8 for every row; "under 0.3%" holds for the typical (median) row
+    rel = np.abs(u["scale"] - f["scale"]) / f["scale"]
+    assert rel.max() <= 2.0 ** -8
+    assert np.median(rel) < GOLDEN["fused_vs_unfused_scale_rel_err_max"]["value"]
+    # the fused codes are closer to the fp32 ground truth in aggregate
+    # ([FUSE] "Accuracy went up")
+    y = f["y"].astype(np.float64)
+    ef = np.abs(e4m3_value(f["q"]) * f["scale"][:, None] - y).sum()
+    eu = np.abs(e4m3_value(u["q"]) * u["scale"][:, None] - y).sum()
+    assert ef < eu
+
+
+# -------------------------------------------------- O3 LayerNorm static ----
+
+@pytest.mark.parametrize("eps", [1e-5, 0.25])
+def test_layernorm_fp8_matches_binary64(orc, eps):
+    w = W.layernorm_rows(M=96, d=1024)
+    o = orc.layernorm_quant_fp8(w["x"], w["gamma"], w["beta"], eps, w["scale"], want_y=True)
+    x64 = bf(w["x"]).double().numpy()
+    mu = x64.mean(axis=1, keepdims=True)
+    c = x64 - mu
+    rstd = 1.0 / np.sqrt((c * c).mean(axis=1, keepdims=True) + eps)
+    y64 = c * rstd * w["gamma"].astype(np.float64) + w["beta"].astype(np.float64)
+    # y_i sums two terms, so bound the error against the size of the terms;
+    # mu is rounded to binary32 once, which shifts every c_i by up to
+    # |mu| * 2^-24 in absolute terms
+    g64 = np.abs(w["gamma"]).astype(np.float64)
+    bound = (2e-6 * (np.abs(c * rstd) * g64 + np.abs(w["beta"]))
+             + 2.0 ** -24 * np.abs(mu) * rstd * g64 * 1.01)
+    assert np.all(np.abs(o["y"] - y64) <= bound)
+    codes, ok = robust_codes(y64 / w["scale"])
+    assert ok.mean() > 0.99
+    assert np.all(same_value(o["q"][ok], codes[ok]))
+
+
+def test_layernorm_constant_row_gives_beta(orc):
+    """c_i = 0 exactly, so y = beta and q = E4(beta * (1/scale))."""
+    d = 512
+    rng = np.random.default_rng(9)
+    x = np.tile(W.to_bf16_bits(np.full(d, 0.3, np.float32)), (2, 1))
+    g = (1 + rng.standard_normal(d)).astype(np.float32)
+    b = rng.standard_normal(d).astype(np.float32)
+    o = orc.layernorm_quant_fp8(x, g, b, 1e-5, 0.05, want_y=True)
+    assert np.array_equal(o["y"][0], b)
+    inv = np.float32(1) / np.float32(0.05)
+    assert np.array_equal(o["q"][0], torch_e4m3(b * inv))
+
+
+# --------------------------------------------------- O4 group quant --------
+
+def test_group_fp32_scale_and_reciprocal_statistic(orc):
+    """fp32 scales = amax/448 per 128-group; codes from x * RN(1/s); against
+    per-element division they differ by one code on ~0.05% ([GRP])."""
+    w = W.group_t3(M=1024)
+    o = orc.per_token_group_quant_fp8(w["x"], 128, ue8m0=False)
+    x = W.bf16_bits_to_f32(w["x"])
+    g = x.reshape(1024, 32, 128)
+    amax = np.abs(g).max(axis=2)
+    assert np.array_equal(o["scale"], (amax / np.float32(448)).astype(np.float32))
+    s = o["scale"][:, :, None]
+    inv = np.where(s > 0, np.float32(1) / np.where(s > 0, s, 1), 0).astype(np.float32)
+    assert np.array_equal(o["q"].reshape(g.shape), torch_e4m3(g * inv))
+    div = torch_e4m3(g / s).reshape(o["q"].shape)
+    differ = o["q"] != div
+    fig = GOLDEN["group_quant_divide_vs_reciprocal_flip_frac"]
+    assert fig["min"] <= differ.mean() <= fig["max"], differ.mean()
+    step = np.abs((o["q"].astype(int) & 0x7F) - (div.astype(int) & 0x7F))
+    assert step.max() == GOLDEN["group_quant_divide_vs_reciprocal_max_ulp"]["value"]
+    # the absmax element of every group is +-448
+    arg = np.abs(g).argmax(axis=2)
+    top = np.take_along_axis(o["q"].reshape(g.shape), arg[:, :, None], axis=2)
+    assert np.all((top & 0x7F) == 0x7E)
+
+
+def test_group_ue8m0_invariants(orc):
+    """UE8M0: s a power of two, the smallest with amax/s <= 448, and divide
+    == reciprocal bit for bit ([GRP] commit message, "Details")."""
+    w = W.group_t3(M=512)
+    o = orc.per_token_group_quant_fp8(w["x"], 128, ue8m0=True)
+    s = o["scale"].astype(np.float64)
+    m, e = np.frexp(s)
+    assert np.all(m == 0.5)  # exact powers of two
+    x = W.bf16_bits_to_f32(w["x"]).reshape(512, 32, 128)
+    amax = np.abs(x).max(axis=2).astype(np.float64)
+    assert np.all(amax / s <= 448.0)
+    assert np.all(amax / (s / 2) > 448.0 * (1 - 2.0 ** -23))
+    div = torch_e4m3(x / o["scale"][:, :, None].astype(np.float32)).reshape(o["q"].shape)
+    assert np.array_equal(o["q"], div)
+
+
+def test_group_exact_power_of_two_scales(orc):
+    """A group whose amax/448 is already a power of two keeps it in UE8M0
+    mode (amax 448 -> s = 1, amax 56 -> s = 1/8); fp32 mode gives the same."""
+    x = np.zeros((2, 256), np.float32)
+    x[0, :128] = np.linspace(-448, 300, 128)
+    x[0, 128:] = np.linspace(-20, 56, 128)
+    x[1, :128] = np.linspace(-10, 100, 128)  # 100/448 = 0.223 -> 0.25
+    bits = W.to_bf16_bits(x)
+    for ue in (True, False):
+        o = orc.per_token_group_quant_fp8(bits, 128, ue8m0=ue)
+        assert o["scale"][0].tolist() == [1.0, 0.125]
+    o = orc.per_token_group_quant_fp8(bits, 128, ue8m0=True)
+    assert o["scale"][1, 0] == 0.25
+    assert o["scale"][1, 1] == 0.0
+
+
+def test_group_zero_group_and_layout(orc):
+    x = W.group_t3(M=4, K=512)["x"].copy()
+    x[1, 128:256] = 0
+    o = orc.per_token_group_quant_fp8(x, 128)
+    assert o["scale"].shape == (4, 4)
+    assert o["scale"][1, 1] == 0 and np.all(o["q"][1, 128:256] == 0)
+    # each group uses only its own 128 elements: perturbing one group changes
+    # only that group's scale
+    x2 = x.copy()
+    x2[2, 300] = W.to_bf16_bits(np.array([1000.0], np.float32))[0]
+    o2 = orc.per_token_group_quant_fp8(x2, 128)
+    changed = o2["scale"] != o["scale"]
+    assert changed.sum() == 1 and changed[2, 2]
+
+
+# --------------------------------------------------- O5 NVFP4 --------------
+
+E2 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def unpack_e2m1(q):
+    lo, hi = q & 0xF, q >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(q.shape[0], -1)
+    val = E2[codes & 7] * np.where(codes & 8, -1.0, 1.0)
+    return codes, val
+
+
+def test_nvfp4_global_argmax_block_saturates_exactly(orc):
+    """With s_g = amax_global / (448 * 6), the block holding the global
+    absmax gets scale code 0x7E and that element codes to +-6."""
+    w = W.nvfp4_7168(M=16)
+    pre = orc.fused_add_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], w["eps"], want_y=True)
+    y = pre["y"]
+    sg = float(np.float32(np.abs(y).max()) / np.float32(2688.0))
+    o = orc.rmsnorm_quant_nvfp4(w["x"], w["residual"], w["gamma"], w["eps"], sg, want_y=True)
+    assert np.array_equal(o["y"], y)
+    assert np.array_equal(o["residual_out"], pre["residual_out"])
+    m, i = np.unravel_index(np.abs(y).argmax(), y.shape)
+    assert o["sf"][m, i // 16] == 0x7E
+    codes, _ = unpack_e2m1(o["q"])
+    assert codes[m, i] & 7 == 7
+    assert np.all(o["sf"] <= 0x7E)
+
+
+def test_nvfp4_round_trip_and_binary64(orc):
+    """Dequantized values lie within half an E2M1 step (times the block
+    scale) of y wherever the element did not saturate, and the block
+    scales are the e4m3 codes of (amax_b/6) * G from a binary64 y."""
+    w = W.nvfp4_7168(M=8)
+    sg = W.NVFP4_NOMINAL_GLOBAL_SCALE
+    o = orc.rmsnorm_quant_nvfp4(w["x"], w["residual"], w["gamma"], w["eps"], sg, want_y=True)
+    y = o["y"].astype(np.float64)
+    sfd = e4m3_value(o["sf"]).astype(np.float64)
+    _, qv = unpack_e2m1(o["q"])
+    scale = np.repeat(sfd, 16, axis=1) * sg
+    v = np.abs(y) / np.where(scale > 0, scale, 1)
+    step = np.where(v < 2, 0.5, np.where(v < 4, 1.0, 2.0))
+    unsat = v <= 6.0
+    err = np.abs(qv * scale - y)
+    assert np.all(err[unsat] <= 0.5 * step[unsat] * scale[unsat] * (1 + 1e-5))
+    _, y64 = ref64_rms(w["x"], w["residual"], w["gamma"], w["eps"], w["d"])
+    amax_b = np.abs(y64).reshape(8, -1, 16).max(axis=2)
+    codes, ok = robust_codes(amax_b / 6.0 / sg)
+    assert ok.mean() > 0.99
+    assert np.all(o["sf"][ok] == codes[ok])
+
+
+def test_nvfp4_zero_block_and_packing(orc):
+    d = 64
+    x = np.zeros((2, d), np.uint16)
+    vals = np.zeros(d, np.float32)
+    vals[16:32] = np.linspace(-3, 3, 16)
+    x[0] = W.to_bf16_bits(vals)
+    g = np.ones(d, np.float32)
+    o = orc.rmsnorm_quant_nvfp4(x, None, g, 1e-6, 1.0 / 448.0, want_y=True)
+    assert np.all(o["sf"][0, [0, 2, 3]] == 0) and np.all(o["q"][0, 0:8] == 0)
+    assert np.all(o["sf"][1] == 0) and np.all(o["q"][1] == 0)
+    # element 2k in the low nibble: the block's first element is the most
+    # negative value, so its code carries the sign bit in the low nibble
+    assert (o["q"][0, 8] & 0x8) and not (o["q"][0, 15] & 0x80)
+
+
+def test_nvfp4_mode_b_quantizes_bf16_of_y(orc):
+    """Mode B reproduces quantizing the bf16 norm_out ([NVFP4] commit notes:
+    re-quantizing the returned norm_out gives the same codes)."""
+    w = W.nvfp4_slice(M=4)
+    sg = W.NVFP4_NOMINAL_GLOBAL_SCALE
+    b = orc.rmsnorm_quant_nvfp4(w["x"], None, w["gamma"], w["eps"], sg, d=1536,
+                                mode_b=True, want_norm_out=True)
+    # feed bf16(y) back through the residual-less path with gamma = 1 and a
+    # row already normalized: not an identity, so compare block by block on
+    # the codec directly instead
+    yb = W.bf16_bits_to_f32(b["norm_out"]).reshape(4, -1, 16)
+    amax = np.abs(yb).max(axis=2)
+    G = np.float32(1) / np.float32(sg)
+    sf = orc.e4m3_encode((amax / np.float32(6)) * G)
+    assert np.array_equal(sf, b["sf"])
+    sfd = orc.e4m3_decode(sf)
+    mult = np.where(sfd > 0, G / np.where(sfd > 0, sfd, 1), 0).astype(np.float32)
+    codes = orc.e2m1_encode(yb * mult[:, :, None]).reshape(4, -1)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    assert np.array_equal(packed, b["q"])
+
+
+# ------------------------------------------------ byte model pins ----------
+
+def test_byte_model_matches_page_figures():
+    d = GOLDEN["fused_rmsnorm_fp8_traffic_saved_bytes_per_token"]["hidden"]
+    unf = traffic.unfused_add_rmsnorm_fp8_per_row(d)
+    fus = traffic.fused_add_rmsnorm_fp8_with_norm_out_per_row(d)
+    saved = unf - fus
+    fig = GOLDEN["fused_rmsnorm_fp8_traffic_saved_bytes_per_token"]
+    assert abs(saved - fig["value"]) <= fig["rel_tol"] * fig["value"]
+    frac = GOLDEN["fused_rmsnorm_fp8_traffic_saved_frac"]
+    assert abs(saved / unf - frac["value"]) <= frac["abs_tol"]
+    M = 1 << 20
+    rd, wr = traffic.layernorm_fp8(M, 4096)
+    assert round((rd + wr) / (M * 4096)) == GOLDEN["layernorm_quant_bytes_per_element_fused"]["value"]
+    assert traffic.unfused_layernorm_fp8_per_element() == GOLDEN["layernorm_quant_bytes_per_element_unfused"]["value"]
+    g = GOLDEN["group_quant_bandwidth_at_101us_TBps"]
+    tbps = traffic.total(traffic.group_fp8(g["M"], g["K"], g["group"])) / (g["us"] * 1e-6) / 1e12
+    assert abs(tbps - g["value"]) <= g["abs_tol"]
+    # the headline workload: M=8192, d=2816 moves 161,524,736 bytes
+    assert traffic.total(traffic.fused_add_rmsnorm_fp8(8192, 2816)) == 161_524_736
