@@ -18,6 +18,7 @@ def __getattr__(name):
     # Lazy: `fp4_quantization_amd.nq_*` resolves through the binding, which
     # loads libnq.so (and fails loudly when it is absent).
     if name.startswith("nq_") or name in ("nq", "NQError"):
-        from . import nq as _nq
+        import importlib
+        _nq = importlib.import_module(__name__ + ".nq")
         return _nq if name == "nq" else getattr(_nq, name)
     raise AttributeError(name)

@@ -1,0 +1,60 @@
+// nq_host.hpp -- host-side argument checks shared by the C-ABI entry points.
+// Everything here runs before any HIP call, so a rejected call enqueues
+// nothing and the checks work on a machine without a GPU.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/nq.h"
+
+namespace nq {
+
+// Address range [lo, hi) touched by a row-major [rows, cols] view with row
+// stride `ld` (elements of `esize` bytes).  Empty when rows or cols is 0.
+struct Region {
+    uintptr_t lo = 0, hi = 0;
+};
+
+inline Region region(const void* p, int64_t rows, int64_t ld, int64_t cols, int64_t esize)
+{
+    Region r;
+    if (!p || rows <= 0 || cols <= 0) return r;
+    r.lo = (uintptr_t)p;
+    r.hi = r.lo + (uintptr_t)(((rows - 1) * ld + cols) * esize);
+    return r;
+}
+
+inline bool overlaps(const Region& a, const Region& b)
+{
+    return a.hi > a.lo && b.hi > b.lo && a.lo < b.hi && b.lo < a.hi;
+}
+
+inline bool aligned(const void* p, uintptr_t bytes) { return ((uintptr_t)p % bytes) == 0; }
+
+// Bounds that keep every byte offset computed by a kernel inside int64.
+constexpr int64_t kMaxRows = int64_t(1) << 40;
+constexpr int64_t kMaxLd = int64_t(1) << 40;
+
+inline bool bad_ld(int64_t ld, int64_t cols) { return ld < cols || ld > kMaxLd; }
+
+// Rejects any output region overlapping an input region or another output
+// region.  `allow_exact` names one (input, output) pair that may coincide
+// exactly (in-place residual update).
+template <int NI, int NO>
+inline bool any_alias(const Region (&in)[NI], const Region (&out)[NO], int exact_in = -1,
+                      int exact_out = -1)
+{
+    for (int o = 0; o < NO; ++o) {
+        for (int i = 0; i < NI; ++i) {
+            if (!overlaps(out[o], in[i])) continue;
+            if (i == exact_in && o == exact_out && out[o].lo == in[i].lo && out[o].hi == in[i].hi)
+                continue;
+            return true;
+        }
+        for (int p = o + 1; p < NO; ++p)
+            if (overlaps(out[o], out[p])) return true;
+    }
+    return false;
+}
+
+} // namespace nq

@@ -1,0 +1,191 @@
+// nq_rmsnorm_nvfp4.hip -- (residual-add +) RMSNorm + NVFP4 for gfx950:
+// packed E2M1 elements, one e4m3 scale per 16 elements, a global fp32 scale.
+//
+// Pages: [NVFP4] "RMSNorm nvfp4 quant fusion for DS V3.2 / Kimi-K2.5"
+// ("Description": the norm is computed in registers and the packed E2M1 +
+// per-block e4m3 representation is emitted in the same pass; a residual-less
+// variant reads a row-strided column slice in place; commit notes: optional
+// bf16 norm output, a fresh residual buffer, hidden % 16 == 0, loop bounds
+// uniform across the lanes that shuffle together).
+//
+// The row is held in registers exactly as in the per-token FP8 kernel.  A
+// 16-element block is two adjacent chunks, owned by lanes t and t^1 of the
+// same load instruction, so the block maximum is one cross-lane exchange.
+// Lanes past the end of the row still execute every exchange with zeros
+// (d % 16 == 0 keeps both halves of a block on the same side of the end).
+#include "nq_device.hpp"
+#include "nq_host.hpp"
+#include "nq_rows.hpp"
+
+namespace nq {
+
+struct RmsFp4Args {
+    const uint16_t* x;
+    const uint16_t* r;
+    uint16_t* ro;
+    const float* gamma;
+    const float* global_scale;
+    uint8_t* q;        // [M, d/2]
+    uint8_t* sf;       // [M, d/16]
+    uint16_t* norm_out;
+    int64_t ld_x, ld_r, ld_ro, ld_q, ld_sf, ld_n;
+    int64_t M;
+    int d;
+    float eps;
+};
+
+// VEC additionally needs 4-byte aligned packed-code rows (one dword per chunk).
+template <int TEAM, int CPL, bool VEC>
+__global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
+{
+    using S = TeamShape<TEAM>;
+    __shared__ double lds_sum[S::kWaves];
+
+    const int t = threadIdx.x % TEAM;
+    const int64_t row = (int64_t)blockIdx.x * S::kRows + threadIdx.x / TEAM;
+    const bool row_ok = row < a.M;
+    const int64_t rr = row_ok ? row : 0;
+    const int d = a.d;
+    const bool has_r = a.r != nullptr;
+    const uint16_t* xr = a.x + rr * a.ld_x;
+    const uint16_t* rrow = has_r ? a.r + rr * a.ld_r : nullptr;
+
+    uint4 xw[CPL], rw[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int e = (j * TEAM + t) * 8;
+        const bool ok = row_ok && e < d;
+        xw[j] = load_bf16x8<VEC>(xr, e, d, ok);
+        rw[j] = has_r ? load_bf16x8<VEC>(rrow, e, d, ok) : make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    float z[CPL][8];
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int e = (j * TEAM + t) * 8;
+        const bool ok = row_ok && e < d;
+        float xv[8];
+        unpack_bf16x8(xw[j], xv);
+        if (has_r) {
+            float rv[8];
+            unpack_bf16x8(rw[j], rv);
+            uint32_t p[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) p[k] = pack_bf16x2(xv[2 * k] + rv[2 * k], xv[2 * k + 1] + rv[2 * k + 1]);
+            const uint4 zw = make_uint4(p[0], p[1], p[2], p[3]);
+            store_bf16x8<VEC>(a.ro + rr * a.ld_ro, e, d, ok, zw);
+            unpack_bf16x8(zw, z[j]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) z[j][k] = xv[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const double zd = (double)z[j][k];
+            acc = fma(zd, zd, acc);
+        }
+    }
+    acc = team_sum<TEAM>(acc, lds_sum);
+    const float ms = (float)(acc / (double)d);
+    const float rstd = 1.0f / sqrtf(ms + a.eps);
+    const float G = 1.0f / a.global_scale[0];  // encode scale
+
+    uint8_t* qr = a.q + rr * a.ld_q;
+    uint8_t* sfr = a.sf + rr * a.ld_sf;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int e = (j * TEAM + t) * 8;
+        const bool ok = row_ok && e < d;
+        float g[8];
+        load_f32x8<VEC>(a.gamma, e, d, ok, g);
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float n = z[j][k] * rstd;
+            z[j][k] = n * g[k];
+            amax = fmaxf(amax, fabsf(z[j][k]));
+        }
+        if (a.norm_out) {
+            const uint4 nw = make_uint4(pack_bf16x2(z[j][0], z[j][1]), pack_bf16x2(z[j][2], z[j][3]),
+                                        pack_bf16x2(z[j][4], z[j][5]), pack_bf16x2(z[j][6], z[j][7]));
+            store_bf16x8<VEC>(a.norm_out + rr * a.ld_n, e, d, ok, nw);
+        }
+        // Block of 16 = this chunk and the partner lane's.
+        amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+        const float per = amax / kE2M1Max;
+        const uint32_t sf = e4m3x4(per * G, 0.0f, 0.0f, 0.0f) & 0xFFu;
+        const float sfd = e4m3_value(sf);
+        const float mult = sfd > 0.0f ? G / sfd : 0.0f;
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = z[j][k] * mult;
+        const uint32_t codes = e2m1x8(v);
+        if (ok) {
+            if constexpr (VEC) {
+                *reinterpret_cast<uint32_t*>(qr + e / 2) = codes;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) qr[e / 2 + k] = (uint8_t)(codes >> (8 * k));
+            }
+            if ((t & 1) == 0) sfr[e / 16] = (uint8_t)sf;
+        }
+    }
+}
+
+template <int TEAM, int CPL, bool VEC>
+struct RmsFp4Kernel {
+    static void launch(const RmsFp4Args& a, dim3 grid, dim3 block, hipStream_t s)
+    {
+        hipLaunchKernelGGL((k_add_rmsnorm_nvfp4<TEAM, CPL, VEC>), grid, block, 0, s, a);
+    }
+};
+
+} // namespace nq
+
+using namespace nq;
+
+extern "C" nq_status nq_rmsnorm_quant_nvfp4(
+    const uint16_t* x, int64_t ld_x,
+    const uint16_t* residual_in, int64_t ld_r,
+    uint16_t* residual_out, int64_t ld_ro,
+    const float* gamma, float eps,
+    const float* global_scale,
+    uint8_t* q_packed, int64_t ld_q,
+    uint8_t* block_scale, int64_t ld_sf,
+    uint16_t* norm_out, int64_t ld_n,
+    int64_t M, int64_t d, void* stream)
+{
+    if (M < 0 || d <= 0 || d > NQ_MAX_D || d % 16 != 0 || M > kMaxRows) return NQ_ERR_SHAPE;
+    if (!(eps >= 0.0f) || eps > 1e30f) return NQ_ERR_ARG;
+    if (bad_ld(ld_x, d) || bad_ld(ld_q, d / 2) || bad_ld(ld_sf, d / 16)) return NQ_ERR_STRIDE;
+    if (residual_in && (bad_ld(ld_r, d) || bad_ld(ld_ro, d))) return NQ_ERR_STRIDE;
+    if (norm_out && bad_ld(ld_n, d)) return NQ_ERR_STRIDE;
+    if (M == 0) return NQ_OK;  // empty tensors may carry NULL data pointers
+    if (!x || !gamma || !global_scale || !q_packed || !block_scale) return NQ_ERR_NULL;
+    if ((residual_in == nullptr) != (residual_out == nullptr)) return NQ_ERR_NULL;
+
+    const Region in[] = {region(x, M, ld_x, d, 2), region(residual_in, M, ld_r, d, 2),
+                         region(gamma, 1, d, d, 4), region(global_scale, 1, 1, 1, 4)};
+    const Region out[] = {region(residual_out, M, ld_ro, d, 2), region(q_packed, M, ld_q, d / 2, 1),
+                          region(block_scale, M, ld_sf, d / 16, 1), region(norm_out, M, ld_n, d, 2)};
+    if (any_alias(in, out, /*exact_in=*/1, /*exact_out=*/0)) return NQ_ERR_ALIAS;
+
+    bool vec = aligned(x, 16) && ld_x % 8 == 0 && aligned(gamma, 16) && aligned(q_packed, 4) &&
+               ld_q % 4 == 0;
+    if (residual_in)
+        vec = vec && aligned(residual_in, 16) && ld_r % 8 == 0 && aligned(residual_out, 16) &&
+              ld_ro % 8 == 0;
+    if (norm_out) vec = vec && aligned(norm_out, 16) && ld_n % 8 == 0;
+
+    const RowShape shape = pick_row_shape(M, d, vec);
+    if (shape.team == 0) return NQ_ERR_SHAPE;
+
+    RmsFp4Args a;
+    a.x = x; a.r = residual_in; a.ro = residual_out; a.gamma = gamma;
+    a.global_scale = global_scale; a.q = q_packed; a.sf = block_scale; a.norm_out = norm_out;
+    a.ld_x = ld_x; a.ld_r = ld_r; a.ld_ro = ld_ro; a.ld_q = ld_q; a.ld_sf = ld_sf; a.ld_n = ld_n;
+    a.M = M; a.d = (int)d; a.eps = eps;
+    if (!launch_row_shape<RmsFp4Kernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
+    return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
+}

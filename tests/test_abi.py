@@ -1,0 +1,159 @@
+"""CPU checks of the C ABI: the library loads, exports every function
+include/nq.h declares, and rejects bad arguments on the host before any HIP
+call (so these run without a GPU).  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nq.h")
+LIB = os.path.join(ROOT, "fp4_quantization_amd", "libnq.so")
+
+NQ_OK, NQ_ERR_NULL, NQ_ERR_SHAPE, NQ_ERR_STRIDE, NQ_ERR_ALIAS, NQ_ERR_ARG = 0, -1, -2, -3, -4, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libnq.so is not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(LIB)
+    v, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    L.nq_fused_add_rmsnorm_quant_fp8.argtypes = [v, i64, v, i64, v, i64, v, f32, v, v, i64, v, v, i64, i64, i64, v]
+    L.nq_layernorm_quant_fp8.argtypes = [v, i64, v, v, f32, v, v, i64, i64, i64, v]
+    L.nq_per_token_group_quant_fp8.argtypes = [v, i64, i64, i64, i32, i32, v, i64, v, v]
+    L.nq_rmsnorm_quant_nvfp4.argtypes = [v, i64, v, i64, v, i64, v, f32, v, v, i64, v, i64, v, i64, i64, i64, v]
+    L.nq_diag_codec.argtypes = [i32, v, v, i64, v]
+    L.nq_diag_copy.argtypes = [v, v, i64, v]
+    L.nq_status_string.restype = ctypes.c_char_p
+    L.nq_version.restype = ctypes.c_char_p
+    return L
+
+
+def test_header_declares_the_four_entry_points():
+    fns = declared_functions()
+    for name in ("nq_fused_add_rmsnorm_quant_fp8", "nq_layernorm_quant_fp8",
+                 "nq_per_token_group_quant_fp8", "nq_rmsnorm_quant_nvfp4", "nq_status_string"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [f for f in declared_functions() if not hasattr(lib, f)]
+    assert not missing, missing
+
+
+def test_status_strings_and_version(lib):
+    assert lib.nq_status_string(0) == b"ok"
+    for s in (-1, -2, -3, -4, -5, -6):
+        assert lib.nq_status_string(s) not in (b"ok", b"unknown status")
+    assert lib.nq_status_string(123) == b"unknown status"
+    assert b"gfx950" in lib.nq_version()
+
+
+# Fake device addresses: every call below is rejected (or is a no-op with
+# M = 0) before anything dereferences them or touches HIP.
+X, R, RO, G, B, S, Q, SC, N = (0x10_0000 * (i + 1) for i in range(9))
+
+
+def rms(lib, **kw):
+    a = dict(x=X, ld_x=256, r=R, ld_r=256, ro=RO, ld_ro=256, g=G, eps=1e-6, ss=None, q=Q, ld_q=256,
+             sc=SC, n=None, ld_n=0, M=4, d=256)
+    a.update(kw)
+    return lib.nq_fused_add_rmsnorm_quant_fp8(a["x"], a["ld_x"], a["r"], a["ld_r"], a["ro"], a["ld_ro"],
+                                              a["g"], a["eps"], a["ss"], a["q"], a["ld_q"], a["sc"],
+                                              a["n"], a["ld_n"], a["M"], a["d"], None)
+
+
+def test_rmsnorm_fp8_validation(lib):
+    assert rms(lib, M=0) == NQ_OK
+    assert rms(lib, M=0, ro=R) == NQ_OK           # exact in-place residual allowed
+    assert rms(lib, x=None) == NQ_ERR_NULL
+    assert rms(lib, g=None) == NQ_ERR_NULL
+    assert rms(lib, q=None) == NQ_ERR_NULL
+    assert rms(lib, sc=None) == NQ_ERR_NULL        # dynamic needs scale_out
+    assert rms(lib, ro=None) == NQ_ERR_NULL        # residual_in without residual_out
+    assert rms(lib, r=None, M=0, ro=None) == NQ_OK  # residual-less
+    assert rms(lib, d=0) == NQ_ERR_SHAPE
+    assert rms(lib, M=-1) == NQ_ERR_SHAPE
+    assert rms(lib, d=32769, ld_x=40000, ld_r=40000, ld_ro=40000, ld_q=40000) == NQ_ERR_SHAPE
+    assert rms(lib, ld_x=255) == NQ_ERR_STRIDE
+    assert rms(lib, ld_q=100) == NQ_ERR_STRIDE
+    assert rms(lib, n=N, ld_n=10) == NQ_ERR_STRIDE
+    assert rms(lib, eps=-1.0) == NQ_ERR_ARG
+    assert rms(lib, eps=float("nan")) == NQ_ERR_ARG
+    # aliasing: outputs over inputs or over each other
+    assert rms(lib, q=X + 100) == NQ_ERR_ALIAS
+    assert rms(lib, ro=R + 2) == NQ_ERR_ALIAS     # partial overlap of the in-place pair
+    assert rms(lib, ro=X) == NQ_ERR_ALIAS         # residual_out over x
+    assert rms(lib, sc=Q + 8) == NQ_ERR_ALIAS
+    assert rms(lib, n=Q, ld_n=256) == NQ_ERR_ALIAS
+    assert rms(lib, q=G) == NQ_ERR_ALIAS
+
+
+def test_layernorm_fp8_validation(lib):
+    call = lambda **k: lib.nq_layernorm_quant_fp8(
+        k.get("x", X), k.get("ld_x", 512), k.get("g", G), k.get("b", B), k.get("eps", 1e-5),
+        k.get("s", S), k.get("q", Q), k.get("ld_q", 512), k.get("M", 2), k.get("d", 512), None)
+    assert call(M=0) == NQ_OK
+    assert call(s=None) == NQ_ERR_NULL
+    assert call(b=None) == NQ_ERR_NULL
+    assert call(ld_x=511) == NQ_ERR_STRIDE
+    assert call(q=X) == NQ_ERR_ALIAS
+    assert call(q=S) == NQ_ERR_ALIAS
+    assert call(d=-3) == NQ_ERR_SHAPE
+
+
+def test_group_fp8_validation(lib):
+    call = lambda **k: lib.nq_per_token_group_quant_fp8(
+        k.get("x", X), k.get("ld_x", 4096), k.get("M", 2), k.get("K", 4096), k.get("g", 128),
+        k.get("mode", 0), k.get("q", Q), k.get("ld_q", 4096), k.get("s", SC), None)
+    assert call(M=0) == NQ_OK
+    assert call(M=0, mode=1) == NQ_OK
+    assert call(g=64) == NQ_ERR_ARG
+    assert call(mode=2) == NQ_ERR_ARG
+    assert call(K=4000, ld_x=4000, ld_q=4000) == NQ_ERR_SHAPE
+    assert call(ld_q=4095) == NQ_ERR_STRIDE
+    assert call(s=None) == NQ_ERR_NULL
+    assert call(s=X + 64) == NQ_ERR_ALIAS
+
+
+def test_nvfp4_validation(lib):
+    call = lambda **k: lib.nq_rmsnorm_quant_nvfp4(
+        k.get("x", X), k.get("ld_x", 2112), k.get("r", None), k.get("ld_r", 0), k.get("ro", None),
+        k.get("ld_ro", 0), k.get("g", G), 1e-6, k.get("gs", S), k.get("q", Q), k.get("ld_q", 768),
+        k.get("sf", SC), k.get("ld_sf", 96), k.get("n", None), k.get("ld_n", 0), k.get("M", 2),
+        k.get("d", 1536), None)
+    assert call(M=0) == NQ_OK                      # residual-less column slice
+    assert call(d=1544, ld_q=772, ld_sf=97) == NQ_ERR_SHAPE   # d % 16
+    assert call(gs=None) == NQ_ERR_NULL
+    assert call(sf=None) == NQ_ERR_NULL
+    assert call(r=R, ld_r=1536, ld_ro=1536) == NQ_ERR_NULL   # residual_in without residual_out
+    assert call(r=R) == NQ_ERR_STRIDE
+    assert call(ld_q=700) == NQ_ERR_STRIDE
+    assert call(ld_sf=95) == NQ_ERR_STRIDE
+    assert call(sf=Q + 10) == NQ_ERR_ALIAS
+    # the output may not be placed in the unread columns of x's own rows:
+    # overlap is judged on address ranges
+    assert call(q=X + 2 * 1536) == NQ_ERR_ALIAS
+
+
+def test_diag_validation(lib):
+    assert lib.nq_diag_codec(7, X, Q, 16, None) == NQ_ERR_ARG
+    assert lib.nq_diag_codec(0, X, Q, 0, None) == NQ_OK
+    assert lib.nq_diag_codec(0, X, X + 4, 16, None) == NQ_ERR_ALIAS
+    assert lib.nq_diag_copy(X, Q, 15, None) == NQ_ERR_SHAPE
+    assert lib.nq_diag_copy(X + 4, Q, 16, None) == NQ_ERR_ARG
+    assert lib.nq_diag_copy(X, Q, 0, None) == NQ_OK
+
+
+def test_binding_imports_without_gpu():
+    import fp4_quantization_amd.nq as nq
+    assert "gfx950" in nq.nq_version()
+    assert nq.nq_status_string(-4).startswith("an output overlaps")
