@@ -14,9 +14,11 @@ that no step finds its data in the 256 MB last-level cache.
 
 Prints ONE JSON line.  `value` is whole-job throughput in GB/s of
 algorithmic bytes (inputs + residual write + fp8 output + scales, gamma
-once; see fp4_quantization_amd/traffic.py) over the K timed steps;
-`roofline.achieved` is the same bytes over the kernel's mean launch duration
-measured with HIP events on the launch stream.  `--suite` also prints one
+once; see fp4_quantization_amd/traffic.py) over the K timed back-to-back
+launches; `roofline.achieved` is the same bytes over the kernel's mean
+launch duration in a graph replay of the same launches, both measured with
+HIP events on the launch stream.  `m1_us_per_call` is the graph-amortized
+time of one M=1 call.  `--suite` also prints one
 line per workload (all five) to stderr.  `--profile-mode` runs a short fixed
 sequence meant to be wrapped by rocprofv3.  `--summarize` turns rocprofv3
 output into the text summaries kept under profiles/.
@@ -24,7 +26,6 @@ output into the text summaries kept under profiles/.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -59,143 +60,161 @@ def log(msg):
 
 # ------------------------------------------------------------- workloads --
 
-class RmsFp8Case:
-    """Rotating buffer sets of one fused add+RMSNorm+FP8 workload."""
+class Case:
+    """A workload bound to rotating buffer sets: `args[i]` is the complete
+    pre-marshalled argument tuple of libnq entry point `fn` (all but the
+    stream), so a timed step is one foreign call and one launch."""
+    fn = None
+    args: list = []
+    bytes = 0
+    label = ""
 
+    def step(self, i, stream):
+        st = self.fn(*self.args[i % len(self.args)], stream)
+        if st != 0:
+            raise RuntimeError(f"{self.label}: status {st}")
+
+
+def _sets_for(nbytes, cap=8):
+    """Buffer sets needed so consecutive steps never reuse data still held
+    in the 256 MB last-level cache (footprint >= 2 x LLC)."""
+    return max(1, min(cap, -(-2 * LLC_BYTES // max(nbytes, 1))))
+
+
+class RmsFp8Case(Case):
     def __init__(self, torch, nq, M, d, seed=0, static=False, sets=None):
         from fp4_quantization_amd import workloads as W, traffic
-        self.torch, self.nq, self.M, self.d = torch, nq, M, d
         w = W.rms_2816(M, seed) if d == 2816 else W.rms_small(seed, M)
         rd, wr = traffic.fused_add_rmsnorm_fp8(M, d, residual=True, static=static)
         self.bytes = rd + wr
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         r = torch.from_numpy(w["residual"]).view(torch.bfloat16).cuda()
         self.g = torch.from_numpy(w["gamma"]).cuda()
-        self.eps = w["eps"]
         self.ss = torch.tensor([0.05], dtype=torch.float32, device="cuda") if static else None
-        n = sets or max(1, min(8, -(-2 * LLC_BYTES // max(self.bytes, 1))))
-        self.sets = []
-        for _ in range(n):
-            self.sets.append(dict(x=x.clone(), r=r.clone(),
-                                  ro=torch.empty_like(r), q=torch.empty(M, d, dtype=torch.uint8, device="cuda"),
-                                  s=torch.empty(M, dtype=torch.float32, device="cuda")))
+        self.fn = nq.library().nq_fused_add_rmsnorm_quant_fp8
+        self.bufs, self.args = [], []
+        for _ in range(sets or _sets_for(self.bytes)):
+            b = dict(x=x.clone(), r=r.clone(), ro=torch.empty_like(r),
+                     q=torch.empty(M, d, dtype=torch.uint8, device="cuda"),
+                     s=torch.empty(M, dtype=torch.float32, device="cuda"))
+            self.bufs.append(b)
+            self.args.append((b["x"].data_ptr(), d, b["r"].data_ptr(), d, b["ro"].data_ptr(), d,
+                              self.g.data_ptr(), w["eps"], None if self.ss is None else self.ss.data_ptr(),
+                              b["q"].data_ptr(), d, None if static else b["s"].data_ptr(), None, 0, M, d))
         self.label = f"fused add+RMSNorm+per-token FP8 (e4m3), M={M}, d={d}" + (", static scale" if static else "")
 
-    def step(self, i, stream=None):
-        b = self.sets[i % len(self.sets)]
-        self.nq.nq_fused_add_rmsnorm_quant_fp8(b["x"], b["r"], b["ro"], self.g, self.eps, self.ss,
-                                               b["q"], None if self.ss is not None else b["s"], stream=stream)
 
-
-class GroupCase:
+class GroupCase(Case):
     def __init__(self, torch, nq, M, K=4096, ue8m0=False):
         from fp4_quantization_amd import workloads as W, traffic
-        self.torch, self.nq = torch, nq
         w = W.group_t3(M, K)
         self.bytes = traffic.total(traffic.group_fp8(M, K))
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
-        n = max(1, min(8, -(-2 * LLC_BYTES // self.bytes)))
-        self.sets = [dict(x=x.clone(), q=torch.empty(M, K, dtype=torch.uint8, device="cuda"),
-                          s=torch.empty(M * K // 128, dtype=torch.float32, device="cuda")) for _ in range(n)]
-        self.mode = nq.NQ_SCALE_UE8M0 if ue8m0 else nq.NQ_SCALE_FP32
+        self.fn = nq.library().nq_per_token_group_quant_fp8
+        mode = nq.NQ_SCALE_UE8M0 if ue8m0 else nq.NQ_SCALE_FP32
+        self.bufs, self.args = [], []
+        for _ in range(_sets_for(self.bytes)):
+            b = dict(x=x.clone(), q=torch.empty(M, K, dtype=torch.uint8, device="cuda"),
+                     s=torch.empty(M * K // 128, dtype=torch.float32, device="cuda"))
+            self.bufs.append(b)
+            self.args.append((b["x"].data_ptr(), K, M, K, 128, mode, b["q"].data_ptr(), K, b["s"].data_ptr()))
         self.label = f"per-token-group FP8, group 128, {'UE8M0' if ue8m0 else 'fp32'} scales, M={M}, K={K}"
 
-    def step(self, i, stream=None):
-        b = self.sets[i % len(self.sets)]
-        self.nq.nq_per_token_group_quant_fp8(b["x"], b["q"], b["s"], 128, self.mode, stream=stream)
 
-
-class LayerNormCase:
+class LayerNormCase(Case):
     def __init__(self, torch, nq, M=16384, d=4096):
         from fp4_quantization_amd import workloads as W, traffic
-        self.torch, self.nq = torch, nq
         w = W.layernorm_rows(M, d)
         self.bytes = traffic.total(traffic.layernorm_fp8(M, d))
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         self.g = torch.from_numpy(w["gamma"]).cuda()
         self.b = torch.from_numpy(w["beta"]).cuda()
         self.sc = torch.tensor([w["scale"]], dtype=torch.float32, device="cuda")
-        self.eps = w["eps"]
-        n = max(1, min(8, -(-2 * LLC_BYTES // self.bytes)))
-        self.sets = [dict(x=x.clone(), q=torch.empty(M, d, dtype=torch.uint8, device="cuda")) for _ in range(n)]
+        self.fn = nq.library().nq_layernorm_quant_fp8
+        self.bufs, self.args = [], []
+        for _ in range(_sets_for(self.bytes)):
+            b = dict(x=x.clone(), q=torch.empty(M, d, dtype=torch.uint8, device="cuda"))
+            self.bufs.append(b)
+            self.args.append((b["x"].data_ptr(), d, self.g.data_ptr(), self.b.data_ptr(), w["eps"],
+                              self.sc.data_ptr(), b["q"].data_ptr(), d, M, d))
         self.label = f"LayerNorm + static FP8 (scale tensor 0.05), M={M}, d={d}"
 
-    def step(self, i, stream=None):
-        b = self.sets[i % len(self.sets)]
-        self.nq.nq_layernorm_quant_fp8(b["x"], self.g, self.b, self.eps, self.sc, b["q"], stream=stream)
 
-
-class Nvfp4Case:
+class Nvfp4Case(Case):
     def __init__(self, torch, nq, M, sliced=False):
         from fp4_quantization_amd import workloads as W, traffic
-        self.torch, self.nq = torch, nq
         w = W.nvfp4_slice(M) if sliced else W.nvfp4_7168(M)
-        d = w["d"]
+        d, ld = w["d"], w["ld"]
         self.bytes = traffic.total(traffic.rmsnorm_nvfp4(M, d, residual=not sliced))
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         r = None if sliced else torch.from_numpy(w["residual"]).view(torch.bfloat16).cuda()
         self.g = torch.from_numpy(w["gamma"]).cuda()
         self.gs = torch.tensor([W.NVFP4_NOMINAL_GLOBAL_SCALE], dtype=torch.float32, device="cuda")
-        self.eps, self.d = w["eps"], d
-        n = max(1, min(8, -(-2 * LLC_BYTES // self.bytes)))
-        self.sets = []
-        for _ in range(n):
-            self.sets.append(dict(x=x.clone(), r=None if r is None else r.clone(),
-                                  ro=None if r is None else torch.empty_like(r),
-                                  q=torch.empty(M, d // 2, dtype=torch.uint8, device="cuda"),
-                                  sf=torch.empty(M, d // 16, dtype=torch.uint8, device="cuda")))
+        self.fn = nq.library().nq_rmsnorm_quant_nvfp4
+        self.bufs, self.args = [], []
+        for _ in range(_sets_for(self.bytes)):
+            b = dict(x=x.clone(), r=None if r is None else r.clone(), ro=None if r is None else torch.empty_like(r),
+                     q=torch.empty(M, d // 2, dtype=torch.uint8, device="cuda"),
+                     sf=torch.empty(M, d // 16, dtype=torch.uint8, device="cuda"))
+            self.bufs.append(b)
+            self.args.append((b["x"].data_ptr(), ld, None if r is None else b["r"].data_ptr(), d,
+                              None if r is None else b["ro"].data_ptr(), d, self.g.data_ptr(), w["eps"],
+                              self.gs.data_ptr(), b["q"].data_ptr(), d // 2, b["sf"].data_ptr(), d // 16,
+                              None, 0, M, d))
         self.label = (f"RMSNorm + NVFP4 on a 1536-of-2112 column slice, M={M}" if sliced
                       else f"residual-add + RMSNorm + NVFP4, M={M}, d=7168")
 
-    def step(self, i, stream=None):
-        b = self.sets[i % len(self.sets)]
-        self.nq.nq_rmsnorm_quant_nvfp4(b["x"][:, :self.d], b["r"], b["ro"], self.g, self.eps, self.gs,
-                                       b["q"], b["sf"], stream=stream)
 
-
-class CopyCase:
+class CopyCase(Case):
     """The 128-bit copy kernel over the same byte count: a same-box ceiling."""
 
     def __init__(self, torch, nq, nbytes):
-        self.torch, self.nq = torch, nq
         n = nbytes // 2 // 16 * 16
-        sets = max(1, min(8, -(-2 * LLC_BYTES // (2 * n))))
-        self.sets = [(torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255),
-                      torch.empty(n, dtype=torch.uint8, device="cuda")) for _ in range(sets)]
+        self.fn = nq.library().nq_diag_copy
+        self.bufs, self.args = [], []
+        for _ in range(_sets_for(2 * n)):
+            src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+            dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+            self.bufs.append((src, dst))
+            self.args.append((src.data_ptr(), dst.data_ptr(), n))
         self.bytes = 2 * n
         self.label = f"128-bit copy, {n} bytes read + {n} written"
-
-    def step(self, i, stream=None):
-        s, d = self.sets[i % len(self.sets)]
-        self.nq.nq_diag_copy(s, d, stream=stream)
 
 
 # ---------------------------------------------------------------- timing --
 
-def time_eager(torch, case, steps, warmup):
-    """Wall time of `steps` back-to-back calls, and each launch's own
-    duration from an event pair around it, all on the current stream."""
+def time_steps(torch, case, steps, warmup):
+    """`warmup` untimed launches, then exactly `steps` back-to-back launches
+    bracketed by synchronizations and by HIP events on the launch stream.
+    Returns (stream milliseconds, wall seconds)."""
     stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
     for i in range(warmup):
-        case.step(i)
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        case.step(i, h)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t0.record(stream)
     for i in range(steps):
-        starts[i].record(stream)
-        case.step(warmup + i)
-        ends[i].record(stream)
+        case.step(warmup + i, h)
     t1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    total_ms = t0.elapsed_time(t1)
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    return total_ms, per, wall
+    return t0.elapsed_time(t1), time.perf_counter() - w0
+
+
+def time_launch_events(torch, case, n=100):
+    """Mean of per-launch event pairs around single launches (includes the
+    event and launch overheads; a latency figure for small calls)."""
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        case.step(i, h)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
 def time_graph(torch, case, calls=20, replays=50):
@@ -205,13 +224,14 @@ def time_graph(torch, case, calls=20, replays=50):
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         for i in range(3):
-            case.step(i)
+            case.step(i, s.cuda_stream)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
         for i in range(calls):
-            case.step(i)
+            case.step(i, h)
     for _ in range(3):
         g.replay()
     torch.cuda.synchronize()
@@ -230,26 +250,27 @@ def time_graph(torch, case, calls=20, replays=50):
 
 # ----------------------------------------------------------- cpu baseline --
 
-def cpu_baseline(budget_s=12.0):
+def cpu_baseline(budget_s=10.0):
     """The oracle (plain single-threaded C) on a bounded sample of the same
-    workload: as many rows of M=8192, d=2816 as fit in about budget_s
-    seconds, scaled to GB/s of the same algorithmic bytes."""
+    workload: 512-row slices of the M=8192, d=2816 rows, taken in order and
+    wrapping around, until about budget_s seconds of CPU work; reported in
+    GB/s of the same algorithmic bytes."""
     import oracle
     from fp4_quantization_amd import workloads as W, traffic
     w = W.rms_2816(8192, 0)
     oracle.lib()
-    rows, elapsed, batch = 0, 0.0, 16
+    rows, elapsed, batch = 0, 0.0, 512
     t0 = time.perf_counter()
-    while elapsed < budget_s and rows < 8192:
-        lo, hi = rows, min(8192, rows + batch)
-        oracle.fused_add_rmsnorm_quant_fp8(w["x"][lo:hi], w["residual"][lo:hi], w["gamma"], w["eps"])
-        rows = hi
+    while elapsed < budget_s:
+        lo = rows % 8192
+        oracle.fused_add_rmsnorm_quant_fp8(w["x"][lo:lo + batch], w["residual"][lo:lo + batch],
+                                           w["gamma"], w["eps"])
+        rows += batch
         elapsed = time.perf_counter() - t0
-        batch = min(batch * 2, 512)
     rd, wr = traffic.fused_add_rmsnorm_fp8(rows, 2816)
     return {"value": round((rd + wr) / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} of 8192 rows of the M=8192, d=2816 workload (seed 0), {elapsed:.1f} s, "
-                      f"single-threaded, host {platform.processor() or platform.machine()}, "
+            "sample": f"{rows} rows ({rows / 8192:.2f} passes over the M=8192, d=2816 workload, seed 0) "
+                      f"in {elapsed:.1f} s, single-threaded, host {platform.processor() or platform.machine()}, "
                       f"{os.cpu_count()} cores visible"}
 
 
@@ -269,9 +290,82 @@ def read_traffic():
     return val if src == kernel_source_hash() else None
 
 
+# ------------------------------------------------------ profile summaries --
+
+MAIN_KERNEL_PREFIX = "void nq::k_add_rmsnorm_fp8<"
+COPY_KERNEL_PREFIX = "nq::k_diag_copy"
+PROFILE_COPY_BYTES = 64 << 20  # what --profile-mode's copies read and write each
+
+
+def _csv(path):
+    import csv
+    return list(csv.DictReader(open(path)))
+
+
+def summarize_trace(stats_csv, out_md, command):
+    """Text summary of a rocprofv3 --kernel-trace --stats run."""
+    rows = _csv(stats_csv)
+    lines = [f"# rocprofv3 kernel trace: fused add+RMSNorm+FP8, M=8192, d=2816", "",
+             f"Command (repository root): `{command}`", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    main = [r for r in rows if r["Name"].startswith(MAIN_KERNEL_PREFIX) and "128, 3" in r["Name"]]
+    if main:
+        avg_us = float(main[0]["AverageNs"]) / 1e3
+        from fp4_quantization_amd import traffic
+        b = traffic.total(traffic.fused_add_rmsnorm_fp8(8192, 2816))
+        lines += ["", f"main kernel average: {avg_us:.2f} us -> {b / avg_us / 1e3:.0f} GB/s of algorithmic "
+                  f"bytes ({b} per launch), {b / avg_us / 1e3 / HBM_PEAK_GBPS * 100:.1f}% of 8 TB/s", "",
+                  "The M=8192 calls are the bench's timed and graph-replayed launches; the many short "
+                  "calls of the other shape are its M=1 latency measurements."]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def summarize_counters(fetch_csv, write_csv, out_md, commands):
+    """HBM bytes per launch of the main kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for the
+    copy kernel moving exactly PROFILE_COPY_BYTES each way."""
+    from fp4_quantization_amd import traffic
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in _csv(path):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = "main" if name.startswith(MAIN_KERNEL_PREFIX) else "copy" if name.startswith(COPY_KERNEL_PREFIX) else None
+            if key:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in vals.items()}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    kib = PROFILE_COPY_BYTES / 1024
+    f_scale, w_scale = kib / f["copy"], kib / w["copy"]
+    rd = f["main"] * f_scale * 1024
+    wr = w["main"] * w_scale * 1024
+    a_rd, a_wr = traffic.fused_add_rmsnorm_fp8(8192, 2816)
+    lines = ["# rocprofv3 HBM counters: fused add+RMSNorm+FP8, M=8192, d=2816", "",
+             "Commands (repository root):", ""] + [f"- `{c}`" for c in commands] + [
+             "", "Counters are KiB per dispatch.  Each is scaled by what it reads for the 128-bit copy "
+             f"kernel of the same run, which reads and writes exactly {PROFILE_COPY_BYTES} bytes.", "",
+             "| counter | copy reference (KiB) | scale | main kernel (KiB) | scaled bytes | algorithmic bytes | ratio |",
+             "|---|---|---|---|---|---|---|",
+             f"| FETCH_SIZE | {f['copy']:.1f} | {f_scale:.4f} | {f['main']:.1f} | {rd:.0f} | {a_rd} | {rd / a_rd:.4f} |",
+             f"| WRITE_SIZE | {w['copy']:.1f} | {w_scale:.4f} | {w['main']:.1f} | {wr:.0f} | {a_wr} | {wr / a_wr:.4f} |",
+             "", f"hbm_bytes_per_launch: {rd + wr:.0f}",
+             f"algorithmic_bytes_per_launch: {a_rd + a_wr}",
+             f"kernel_source_hash: {kernel_source_hash()}",
+             "", "(bench.py reports `roofline.traffic` from these two lines while the kernel sources "
+             "still hash to the value above.)"]
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 # ------------------------------------------------------------------ main --
 
-def run_suite(torch, nq, steps, warmup):
+def run_suite(torch, nq):
     cases = [
         ("rms_small", lambda: RmsFp8Case(torch, nq, 64, 256)),
         ("rms_2816_m1", lambda: RmsFp8Case(torch, nq, 1, 2816, sets=64)),
@@ -293,11 +387,10 @@ def run_suite(torch, nq, steps, warmup):
     ]
     for name, make in cases:
         case = make()
-        total_ms, per, _ = time_eager(torch, case, steps, warmup)
         us_graph = time_graph(torch, case) * 1e3
         line = {"workload": name, "label": case.label, "bytes_per_call": case.bytes,
                 "us_per_call_graph": round(us_graph, 3),
-                "us_per_launch_events": round(float(per.mean()) * 1e3, 3),
+                "us_per_launch_events": round(time_launch_events(torch, case, 50) * 1e3, 3),
                 "GBps_graph": round(case.bytes / (us_graph * 1e-6) / 1e9, 1),
                 "pct_hbm_peak_graph": round(100 * case.bytes / (us_graph * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)}
         log(json.dumps(line))
@@ -314,7 +407,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-mode", action="store_true",
                     help="short fixed run for rocprofv3: copy reference + main kernel steps")
+    ap.add_argument("--summarize", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="write the profiles/ summaries from rocprofv3 output and exit")
     args = ap.parse_args()
+
+    if args.summarize:
+        stats, fetch, write = args.summarize
+        summarize_trace(stats, os.path.join(ROOT, "profiles", "rmsnorm_fp8_m8192_d2816_kernel_trace.md"),
+                        "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_kt -o kt --output-format csv -- "
+                        "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline")
+        summarize_counters(fetch, write, COUNTER_SUMMARY,
+                           ["rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o fetch --output-format csv "
+                            "-- python3 bench.py --profile-mode",
+                            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o write --output-format csv "
+                            "-- python3 bench.py --profile-mode"])
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -335,30 +442,33 @@ def main():
         for _ in range(10):
             nq.nq_diag_copy(src, dst)
         case = RmsFp8Case(torch, nq, 8192, 2816)
+        h = torch.cuda.current_stream().cuda_stream
         for i in range(20):
-            case.step(i)
+            case.step(i, h)
         torch.cuda.synchronize()
         log("profile-mode done")
         return
 
     case = RmsFp8Case(torch, nq, 8192, 2816)
-    total_ms, per, wall = time_eager(torch, case, args.steps, args.warmup)
+    total_ms, wall = time_steps(torch, case, args.steps, args.warmup)
     ms_per_step = total_ms / args.steps
     value = case.bytes / (ms_per_step * 1e-3) / 1e9
-    kernel_ms = float(per.mean())
+    # average launch duration of the same kernel over a graph of
+    # min(K, 50) launches (launch gaps removed), for the roofline
+    kernel_ms = time_graph(torch, case, calls=min(args.steps, 50), replays=10)
     achieved = case.bytes / (kernel_ms * 1e-3) / 1e9
     log(f"main: {args.steps} steps, {total_ms:.3f} ms on the stream ({wall * 1e3:.1f} ms wall), "
-        f"{ms_per_step * 1e3:.2f} us/step, kernel mean {kernel_ms * 1e3:.2f} us")
+        f"{ms_per_step * 1e3:.2f} us/step; graph-replayed kernel {kernel_ms * 1e3:.2f} us")
     del case
     torch.cuda.empty_cache()
 
     m1 = RmsFp8Case(torch, nq, 1, 2816, sets=64)
     m1_us = time_graph(torch, m1, calls=100) * 1e3
-    _, m1_per, _ = time_eager(torch, m1, 200, 20)
+    m1_ev_ms = time_launch_events(torch, m1, 200)
     del m1
 
     if args.suite:
-        run_suite(torch, nq, min(args.steps, 50), min(args.warmup, 5))
+        run_suite(torch, nq)
 
     traffic_bytes = read_traffic()
     out = {
@@ -372,7 +482,7 @@ def main():
                    "buffer_sets": 4, "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "m1_us_per_call": round(m1_us, 3),
-        "m1_us_per_launch_events": round(float(m1_per.mean()) * 1e3, 3),
+        "m1_us_per_launch_events": round(m1_ev_ms * 1e3, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_bytes},
     }

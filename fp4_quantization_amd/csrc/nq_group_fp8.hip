@@ -48,8 +48,10 @@ __global__ __launch_bounds__(kGroupBlock) void k_group_fp8(GroupArgs a)
     const int lane16 = threadIdx.x & 15;
     const uint32_t base = (uint32_t)blockIdx.x * (kGroupBlock / 16) * kGroupUnroll + threadIdx.x / 16;
 
+    // Idle lanes of the last block read group 0 (always in bounds) and
+    // store nothing, so every load is unconditional.
     uint4 w[kGroupUnroll];
-    int64_t xoff[kGroupUnroll], qoff[kGroupUnroll];
+    int64_t qoff[kGroupUnroll];
     bool ok[kGroupUnroll];
 #pragma unroll
     for (int u = 0; u < kGroupUnroll; ++u) {
@@ -58,10 +60,16 @@ __global__ __launch_bounds__(kGroupBlock) void k_group_fp8(GroupArgs a)
         const uint32_t g = ok[u] ? gi : 0u;
         const uint32_t m = g / a.groups_per_row, c = g - m * a.groups_per_row;
         const int col = (int)c * kGroup + lane16 * 8;
-        xoff[u] = (int64_t)m * a.ld_x + col;
+        const uint16_t* px = a.x + (int64_t)m * a.ld_x + col;
         qoff[u] = (int64_t)m * a.ld_q + col;
-        // K % 128 == 0, so a chunk is always whole.
-        w[u] = load_bf16x8<VEC>(a.x + xoff[u], 0, 8, ok[u]);
+        if constexpr (VEC) {
+            w[u] = ld_global_stream16(px);
+        } else {
+            uint32_t h[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) h[k] = px[k];
+            w[u] = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+        }
     }
 
 #pragma unroll
@@ -77,8 +85,16 @@ __global__ __launch_bounds__(kGroupBlock) void k_group_fp8(GroupArgs a)
         const float inv = s > 0.0f ? 1.0f / s : 0.0f;
         const uint2 q = make_uint2(e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv),
                                    e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv));
-        store_u8x8<VEC>(a.q + qoff[u], 0, 8, ok[u], q);
-        if (lane16 == 0 && ok[u]) a.scale_out[base + (uint32_t)u * (kGroupBlock / 16)] = s;
+        if (ok[u]) {
+            uint8_t* pq = a.q + qoff[u];
+            if constexpr (VEC) {
+                st_global_stream8(pq, q);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) pq[k] = (uint8_t)((k < 4 ? q.x : q.y) >> (8 * (k & 3)));
+            }
+            if (lane16 == 0) a.scale_out[base + (uint32_t)u * (kGroupBlock / 16)] = s;
+        }
     }
 }
 

@@ -37,20 +37,22 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_layernorm_fp8(LnFp8
     __shared__ double lds_var[S::kWaves];
 
     const int t = threadIdx.x % TEAM;
-    const int64_t row = (int64_t)blockIdx.x * S::kRows + threadIdx.x / TEAM;
-    const bool row_ok = row < a.M;
-    const int64_t rr = row_ok ? row : 0;
+    const RowMap m = row_map<TEAM>(a.M);
     const int d = a.d;
-    const uint16_t* xr = a.x + rr * a.ld_x;
+    const RowIO<VEC, kLoadStream, uint16_t> xio(a.x, a.ld_x, m, d);
+    const RowIO<VEC, kKeep, float> gio(a.gamma, d, vector_map(), d);
+    const RowIO<VEC, kKeep, float> bio(a.beta, d, vector_map(), d);
+    const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d);
 
     uint4 xw[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t) * 8;
-        xw[j] = load_bf16x8<VEC>(xr, e, d, row_ok && e < d);
+        xw[j] = xio.load16(e, e < d);
     }
 
-    // mean = sum(x) / d; every bf16 x is exact in binary64.
+    // mean = sum(x) / d; every bf16 x is exact in binary64 (masked = 0).
+    // The unpacked row is what c replaces below, so it stays unpacked.
     float c[CPL][8];
     double acc = 0.0;
 #pragma unroll
@@ -61,33 +63,39 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_layernorm_fp8(LnFp8
     }
     acc = team_sum<TEAM>(acc, lds_mean);
     const float mu = (float)(acc / (double)d);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // c = x - mean (binary32); var = sum(c^2) / d over the d real elements.
+    // c = x - mean (binary32), held in registers (at most 32 per lane);
+    // var = sum(c^2) / d over the d real elements (c^2 is exact in
+    // binary64).  A chunk past the row end contributes nothing.
     double acc2 = 0.0;
+    const int t1 = opaque(t);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const int e = (j * TEAM + t) * 8;
+        const int e = (j * TEAM + t1) * 8;
+        double part = 0.0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const bool live = row_ok && e + k < d;
-            c[j][k] = live ? c[j][k] - mu : 0.0f;
-            const double cd = (double)c[j][k];
-            acc2 = fma(cd, cd, acc2);
+            c[j][k] = c[j][k] - mu;
+            const bool live = VEC || e + k < d;  // whole chunks on the 128-bit path
+            const double cd = live ? (double)c[j][k] : 0.0;
+            part = fma(cd, cd, part);
         }
+        acc2 += e < d ? part : 0.0;
     }
     acc2 = team_sum<TEAM>(acc2, lds_var);
     const float var = (float)(acc2 / (double)d);
     const float rstd = 1.0f / sqrtf(var + a.eps);
     const float inv = 1.0f / a.scale[0];
+    __builtin_amdgcn_sched_barrier(0);
 
-    uint8_t* qr = a.q + rr * a.ld_q;
+    // y = ((c * rstd) * gamma) + beta; q = e4m3(y * (1 / scale)).
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const int e = (j * TEAM + t) * 8;
-        const bool ok = row_ok && e < d;
+        const int e = (j * TEAM + t1) * 8;
         float g[8], b[8], v[8];
-        load_f32x8<VEC>(a.gamma, e, d, ok, g);
-        load_f32x8<VEC>(a.beta, e, d, ok, b);
+        load_f32x8(gio, e, e < d, g);
+        load_f32x8(bio, e, e < d, b);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float n = c[j][k] * rstd;
@@ -95,8 +103,7 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_layernorm_fp8(LnFp8
             const float y = gn + b[k];
             v[k] = y * inv;
         }
-        const uint2 w = make_uint2(e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7]));
-        store_u8x8<VEC>(qr, e, d, ok, w);
+        qio.store8(e, e < d, make_uint2(e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])));
     }
 }
 

@@ -14,7 +14,10 @@
 // binary32 once regardless of the reduction tree), y = (z * rstd) * gamma
 // stays in fp32 registers, its absolute maximum is reduced a second time,
 // and the codes are produced straight from those registers: one rounding
-// (fp32 -> e4m3) instead of the unfused pipeline's two.
+// (fp32 -> e4m3) instead of the unfused pipeline's two.  Teams hold at most
+// 32 elements per lane, so x, the residual, z (as packed bf16: it is exactly
+// a bf16 value) and y all fit at full occupancy; every masked access goes
+// through buffer-resource range checks instead of branches.
 #include "nq_device.hpp"
 #include "nq_host.hpp"
 #include "nq_rows.hpp"
@@ -44,107 +47,112 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_fp8(Rms
     __shared__ float lds_max[S::kWaves];
 
     const int t = threadIdx.x % TEAM;
-    const int64_t row = (int64_t)blockIdx.x * S::kRows + threadIdx.x / TEAM;
-    const bool row_ok = row < a.M;
-    const int64_t rr = row_ok ? row : 0;  // keeps addresses formed below in range
+    const RowMap m = row_map<TEAM>(a.M);
     const int d = a.d;
     const bool has_r = a.r != nullptr;
 
-    const uint16_t* xr = a.x + rr * a.ld_x;
-    const uint16_t* rrow = has_r ? a.r + rr * a.ld_r : nullptr;
+    const RowIO<VEC, kLoadStream, uint16_t> xio(a.x, a.ld_x, m, d);
+    const RowIO<VEC, kLoadStream, uint16_t> rio(a.r, a.ld_r, m, d);
+    const RowIO<VEC, kStoreRows, uint16_t> roio(a.ro, a.ld_ro, m, d);
+    const RowIO<VEC, kKeep, float> gio(a.gamma, d, vector_map(), d);
 
-    // Issue every load of the row before the first use.
+    // Issue every load of the row before the first use.  A residual-less
+    // row adds -0.0, which leaves x unchanged bit for bit.
+    const uint32_t rfill = has_r ? 0u : kNegZeroBf16x2;
     uint4 xw[CPL], rw[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t) * 8;
-        const bool ok = row_ok && e < d;
-        xw[j] = load_bf16x8<VEC>(xr, e, d, ok);
-        rw[j] = has_r ? load_bf16x8<VEC>(rrow, e, d, ok) : make_uint4(0u, 0u, 0u, 0u);
+        xw[j] = xio.load16(e, e < d);
+        rw[j] = rio.load16(e, e < d);
     }
 
-    // z = bf16(x + r); residual write-back; sum of z^2.
-    float z[CPL][8];
+    // z = bf16(x + r), kept packed; residual write-back; sum of z^2.
+    uint4 zw[CPL];
     double acc = 0.0;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t) * 8;
-        const bool ok = row_ok && e < d;
-        float xv[8];
+        float xv[8], rv[8], z[8];
         unpack_bf16x8(xw[j], xv);
-        if (has_r) {
-            float rv[8];
-            unpack_bf16x8(rw[j], rv);
-            uint32_t p[4];
+        unpack_bf16x8(make_uint4(rw[j].x | rfill, rw[j].y | rfill, rw[j].z | rfill, rw[j].w | rfill), rv);
+        uint32_t p[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) p[k] = pack_bf16x2(xv[2 * k] + rv[2 * k], xv[2 * k + 1] + rv[2 * k + 1]);
-            const uint4 zw = make_uint4(p[0], p[1], p[2], p[3]);
-            store_bf16x8<VEC>(a.ro + rr * a.ld_ro, e, d, ok, zw);
-            unpack_bf16x8(zw, z[j]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) z[j][k] = xv[k];
-        }
+        for (int k = 0; k < 4; ++k) p[k] = pack_bf16x2(xv[2 * k] + rv[2 * k], xv[2 * k + 1] + rv[2 * k + 1]);
+        zw[j] = make_uint4(p[0], p[1], p[2], p[3]);
+        roio.store16(e, e < d, zw[j]);  // dropped when residual-less
+        unpack_bf16x8(zw[j], z);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const double zd = (double)z[j][k];
+            const double zd = (double)z[k];
             acc = fma(zd, zd, acc);  // z^2 is exact in binary64
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     // Reduction 1: rstd = 1 / sqrt(mean(z^2) + eps).
     acc = team_sum<TEAM>(acc, lds_sum);
     const float ms = (float)(acc / (double)d);
     const float rstd = 1.0f / sqrtf(ms + a.eps);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // y = (z * rstd) * gamma, kept in registers.
+    // y = (z * rstd) * gamma, held in fp32 registers (at most 32 per lane),
+    // its absolute maximum, and the optional bf16 copy of y.  The packed z
+    // is laundered first so its unpacked copy from the sum above is not kept
+    // alive across the reduction.
+    float y[CPL][8];
     float amax = 0.0f;
+    const RowIO<VEC, kStoreRows, uint16_t> nio(a.norm_out, a.ld_n, m, d);
+    const int t1 = opaque(t);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) opaque(zw[j]);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const int e = (j * TEAM + t) * 8;
-        const bool ok = row_ok && e < d;
-        float g[8];
-        load_f32x8<VEC>(a.gamma, e, d, ok, g);
+        const int e = (j * TEAM + t1) * 8;
+        float g[8], z[8];
+        load_f32x8(gio, e, e < d, g);
+        unpack_bf16x8(zw[j], z);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const float n = z[j][k] * rstd;
-            z[j][k] = n * g[k];
-            amax = fmaxf(amax, fabsf(z[j][k]));
+            const float n = z[k] * rstd;
+            y[j][k] = n * g[k];
+            amax = fmaxf(amax, fabsf(y[j][k]));
         }
+        amax = opaque(amax);  // fold each chunk as it is produced
         if (a.norm_out) {
-            const uint4 nw = make_uint4(pack_bf16x2(z[j][0], z[j][1]), pack_bf16x2(z[j][2], z[j][3]),
-                                        pack_bf16x2(z[j][4], z[j][5]), pack_bf16x2(z[j][6], z[j][7]));
-            store_bf16x8<VEC>(a.norm_out + rr * a.ld_n, e, d, ok, nw);
+            const uint4 nw = make_uint4(pack_bf16x2(y[j][0], y[j][1]), pack_bf16x2(y[j][2], y[j][3]),
+                                        pack_bf16x2(y[j][4], y[j][5]), pack_bf16x2(y[j][6], y[j][7]));
+            nio.store16(e, e < d, nw);
         }
     }
 
-    uint8_t* qr = a.q + rr * a.ld_q;
-    if (a.static_scale) {
-        // out = y / scale, applied as y * (1 / scale[0]); the scale is read
-        // on the device so a graph replay sees its current value.
+    // Static: out = y / scale, applied as y * (1 / scale[0]); the scale is
+    // read on the device so a graph replay sees its current value.
+    // Dynamic (reduction 2): s = amax / 448 and q = e4m3(y / s), one
+    // correctly rounded quotient per element (div_by).
+    const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d);
+    if (a.static_scale == nullptr) {
+        amax = team_max<TEAM>(amax, lds_max);
+        const float s = amax / kE4M3Max;
+        if (t == 0 && m.ok) a.scale_out[m.row] = s;
+        const float inv = s > 0.0f ? 1.0f / s : 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int e = (j * TEAM + t1) * 8;
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = div_by(y[j][k], s, inv);
+            qio.store8(e, e < d, make_uint2(e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])));
+        }
+    } else {
         const float inv = 1.0f / a.static_scale[0];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-            const int e = (j * TEAM + t) * 8;
-            const float* y = z[j];
-            const uint2 w = make_uint2(e4m3x4(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv),
-                                       e4m3x4(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv));
-            store_u8x8<VEC>(qr, e, d, row_ok && e < d, w);
-        }
-    } else {
-        // Reduction 2: per-token scale s = amax / 448; q = e4m3(y / s).
-        amax = team_max<TEAM>(amax, lds_max);
-        const float s = amax / kE4M3Max;
-        if (t == 0 && row_ok) a.scale_out[row] = s;
+            const int e = (j * TEAM + t1) * 8;
+            float v[8];
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int e = (j * TEAM + t) * 8;
-            const float* y = z[j];
-            uint2 w = make_uint2(0u, 0u);
-            if (s > 0.0f)
-                w = make_uint2(e4m3x4(y[0] / s, y[1] / s, y[2] / s, y[3] / s),
-                               e4m3x4(y[4] / s, y[5] / s, y[6] / s, y[7] / s));
-            store_u8x8<VEC>(qr, e, d, row_ok && e < d, w);
+            for (int k = 0; k < 8; ++k) v[k] = y[j][k] * inv;
+            qio.store8(e, e < d, make_uint2(e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])));
         }
     }
 }

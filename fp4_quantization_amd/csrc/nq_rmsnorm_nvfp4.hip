@@ -42,47 +42,41 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_nvfp4(R
     __shared__ double lds_sum[S::kWaves];
 
     const int t = threadIdx.x % TEAM;
-    const int64_t row = (int64_t)blockIdx.x * S::kRows + threadIdx.x / TEAM;
-    const bool row_ok = row < a.M;
-    const int64_t rr = row_ok ? row : 0;
+    const RowMap m = row_map<TEAM>(a.M);
     const int d = a.d;
     const bool has_r = a.r != nullptr;
-    const uint16_t* xr = a.x + rr * a.ld_x;
-    const uint16_t* rrow = has_r ? a.r + rr * a.ld_r : nullptr;
+    const RowIO<VEC, kLoadStream, uint16_t> xio(a.x, a.ld_x, m, d);
+    const RowIO<VEC, kLoadStream, uint16_t> rio(a.r, a.ld_r, m, d);
+    const RowIO<VEC, kStoreRows, uint16_t> roio(a.ro, a.ld_ro, m, d);
+    const RowIO<VEC, kKeep, float> gio(a.gamma, d, vector_map(), d);
 
+    // A residual-less row adds -0.0, which leaves x unchanged bit for bit.
+    const uint32_t rfill = has_r ? 0u : kNegZeroBf16x2;
     uint4 xw[CPL], rw[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t) * 8;
-        const bool ok = row_ok && e < d;
-        xw[j] = load_bf16x8<VEC>(xr, e, d, ok);
-        rw[j] = has_r ? load_bf16x8<VEC>(rrow, e, d, ok) : make_uint4(0u, 0u, 0u, 0u);
+        xw[j] = xio.load16(e, e < d);
+        rw[j] = rio.load16(e, e < d);
     }
 
-    float z[CPL][8];
+    uint4 zw[CPL];
     double acc = 0.0;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t) * 8;
-        const bool ok = row_ok && e < d;
-        float xv[8];
+        float xv[8], rv[8], z[8];
         unpack_bf16x8(xw[j], xv);
-        if (has_r) {
-            float rv[8];
-            unpack_bf16x8(rw[j], rv);
-            uint32_t p[4];
+        unpack_bf16x8(make_uint4(rw[j].x | rfill, rw[j].y | rfill, rw[j].z | rfill, rw[j].w | rfill), rv);
+        uint32_t p[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) p[k] = pack_bf16x2(xv[2 * k] + rv[2 * k], xv[2 * k + 1] + rv[2 * k + 1]);
-            const uint4 zw = make_uint4(p[0], p[1], p[2], p[3]);
-            store_bf16x8<VEC>(a.ro + rr * a.ld_ro, e, d, ok, zw);
-            unpack_bf16x8(zw, z[j]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) z[j][k] = xv[k];
-        }
+        for (int k = 0; k < 4; ++k) p[k] = pack_bf16x2(xv[2 * k] + rv[2 * k], xv[2 * k + 1] + rv[2 * k + 1]);
+        zw[j] = make_uint4(p[0], p[1], p[2], p[3]);
+        roio.store16(e, e < d, zw[j]);  // dropped when residual-less
+        unpack_bf16x8(zw[j], z);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const double zd = (double)z[j][k];
+            const double zd = (double)z[k];
             acc = fma(zd, zd, acc);
         }
     }
@@ -90,28 +84,32 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_nvfp4(R
     const float ms = (float)(acc / (double)d);
     const float rstd = 1.0f / sqrtf(ms + a.eps);
     const float G = 1.0f / a.global_scale[0];  // encode scale
+    __builtin_amdgcn_sched_barrier(0);
 
-    uint8_t* qr = a.q + rr * a.ld_q;
-    uint8_t* sfr = a.sf + rr * a.ld_sf;
+    const RowIO<VEC, kStoreRows, uint16_t> nio(a.norm_out, a.ld_n, m, d);
+    const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d / 2);
+    const RowIO<VEC, kStoreCodes, uint8_t> sfio(a.sf, a.ld_sf, m, d / 16);
+    const int t1 = opaque(t);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) opaque(zw[j]);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const int e = (j * TEAM + t) * 8;
-        const bool ok = row_ok && e < d;
-        float g[8];
-        load_f32x8<VEC>(a.gamma, e, d, ok, g);
+        const int e = (j * TEAM + t1) * 8;
+        float g[8], z[8], y[8];
+        load_f32x8(gio, e, e < d, g);
+        unpack_bf16x8(zw[j], z);
         float amax = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const float n = z[j][k] * rstd;
-            z[j][k] = n * g[k];
-            amax = fmaxf(amax, fabsf(z[j][k]));
+            const float n = z[k] * rstd;
+            y[k] = n * g[k];
+            amax = fmaxf(amax, fabsf(y[k]));
         }
-        if (a.norm_out) {
-            const uint4 nw = make_uint4(pack_bf16x2(z[j][0], z[j][1]), pack_bf16x2(z[j][2], z[j][3]),
-                                        pack_bf16x2(z[j][4], z[j][5]), pack_bf16x2(z[j][6], z[j][7]));
-            store_bf16x8<VEC>(a.norm_out + rr * a.ld_n, e, d, ok, nw);
-        }
-        // Block of 16 = this chunk and the partner lane's.
+        if (a.norm_out)
+            nio.store16(e, e < d, make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                             pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])));
+        // Block of 16 = this chunk and the partner lane's (same load
+        // instruction, lanes t and t^1).
         amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
         const float per = amax / kE2M1Max;
         const uint32_t sf = e4m3x4(per * G, 0.0f, 0.0f, 0.0f) & 0xFFu;
@@ -119,17 +117,9 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_nvfp4(R
         const float mult = sfd > 0.0f ? G / sfd : 0.0f;
         float v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = z[j][k] * mult;
-        const uint32_t codes = e2m1x8(v);
-        if (ok) {
-            if constexpr (VEC) {
-                *reinterpret_cast<uint32_t*>(qr + e / 2) = codes;
-            } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) qr[e / 2 + k] = (uint8_t)(codes >> (8 * k));
-            }
-            if ((t & 1) == 0) sfr[e / 16] = (uint8_t)sf;
-        }
+        for (int k = 0; k < 8; ++k) v[k] = y[k] * mult;
+        qio.store4(e / 2, e < d, e2m1x8(v));
+        sfio.store1(e / 16, e < d && (t1 & 1) == 0, sf);
     }
 }
 
