@@ -14,11 +14,12 @@ that no step finds its data in the 256 MB last-level cache.
 
 Prints ONE JSON line.  `value` is whole-job throughput in GB/s of
 algorithmic bytes (inputs + residual write + fp8 output + scales, gamma
-once; see fp4_quantization_amd/traffic.py) over the K timed back-to-back
-launches; `roofline.achieved` is the same bytes over the kernel's mean
-launch duration in a graph replay of the same launches, both measured with
-HIP events on the launch stream.  `m1_us_per_call` is the graph-amortized
-time of one M=1 call.  `--suite` also prints one
+once; see fp4_quantization_amd/traffic.py): the K timed steps are captured
+in one hipGraph and replayed once, timed with HIP events on the replay
+stream; each step is one launch, so `roofline.achieved` (bytes over the
+kernel's average launch duration) is the same figure.  `eager_ms_per_step`
+times the same K steps as plain launches, `m1_us_per_call` is the
+graph-amortized time of one M=1 call.  `--suite` also prints one
 line per workload (all five) to stderr.  `--profile-mode` runs a short fixed
 sequence meant to be wrapped by rocprofv3.  `--summarize` turns rocprofv3
 output into the text summaries kept under profiles/.
@@ -201,6 +202,31 @@ def time_steps(torch, case, steps, warmup):
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1), time.perf_counter() - w0
+
+
+def time_steps_graph(torch, case, steps, warmup):
+    """`warmup` untimed eager launches, then exactly `steps` launches captured
+    in one graph and replayed once, bracketed by synchronizations and by HIP
+    events on the replay stream (the first replay, so its one-time upload is
+    inside the timed region).  Returns stream milliseconds."""
+    h = torch.cuda.current_stream().cuda_stream
+    for i in range(warmup):
+        case.step(i, h)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        hh = torch.cuda.current_stream().cuda_stream
+        for i in range(steps):
+            case.step(warmup + i, hh)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    del g
+    return t0.elapsed_time(t1)
 
 
 def time_launch_events(torch, case, n=100):
@@ -450,15 +476,15 @@ def main():
         return
 
     case = RmsFp8Case(torch, nq, 8192, 2816)
-    total_ms, wall = time_steps(torch, case, args.steps, args.warmup)
+    total_ms = time_steps_graph(torch, case, args.steps, args.warmup)
     ms_per_step = total_ms / args.steps
     value = case.bytes / (ms_per_step * 1e-3) / 1e9
-    # average launch duration of the same kernel over a graph of
-    # min(K, 50) launches (launch gaps removed), for the roofline
-    kernel_ms = time_graph(torch, case, calls=min(args.steps, 50), replays=10)
-    achieved = case.bytes / (kernel_ms * 1e-3) / 1e9
-    log(f"main: {args.steps} steps, {total_ms:.3f} ms on the stream ({wall * 1e3:.1f} ms wall), "
-        f"{ms_per_step * 1e3:.2f} us/step; graph-replayed kernel {kernel_ms * 1e3:.2f} us")
+    # the same kernel's average launch duration in that timed replay
+    achieved = value
+    # for reference: the same K steps as plain back-to-back launches
+    eager_ms, _ = time_steps(torch, case, args.steps, 0)
+    log(f"main: {args.steps} steps in one graph replay: {total_ms:.3f} ms, {ms_per_step * 1e3:.2f} us/step; "
+        f"as plain launches {eager_ms / args.steps * 1e3:.2f} us/step")
     del case
     torch.cuda.empty_cache()
 
@@ -481,6 +507,7 @@ def main():
                    "M": 8192, "d": 2816, "bytes_per_step": case_bytes_8192(),
                    "buffer_sets": 4, "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "eager_ms_per_step": round(eager_ms / args.steps, 6),
         "m1_us_per_call": round(m1_us, 3),
         "m1_us_per_launch_events": round(m1_ev_ms * 1e3, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -117,35 +117,73 @@ __device__ __forceinline__ uint32_t e2m1x8(const float v[8])
 #endif
 
 // ------------------------------------------------------- reductions -------
-// Butterfly over aligned groups of W lanes (W a power of two <= 64): every
-// lane ends with the same value, because each step adds the same two
-// operands (a + b == b + a exactly).
+// Within a 16-lane DPP row: xor 1 and xor 2 inside each quad, then the
+// half-row mirror (lane i <-> 7-i) and the row mirror (i <-> 15-i).  Each
+// step combines the same two operands on both partner lanes (a + b == b + a
+// exactly), so every lane of the row ends with bitwise the same value.
+// Across the four rows of a wavefront the row results are read into scalar
+// registers and combined in a fixed order; across 32 lanes one cross-lane
+// exchange finishes the pair of rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm 1,0,3,2
+constexpr int kDppXor2 = 0x4E;        // quad_perm 2,3,0,1
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
 template <int W>
 __device__ __forceinline__ double group_sum(double v)
 {
-#pragma unroll
-    for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    static_assert(W == 16 || W == 32 || W == 64, "group of 16, 32 or 64 lanes");
+    v += dpp_f64<kDppXor1>(v);
+    v += dpp_f64<kDppXor2>(v);
+    v += dpp_f64<kDppHalfMirror>(v);
+    v += dpp_f64<kDppMirror>(v);
+    if constexpr (W == 32) v += __shfl_xor(v, 16, kWave);
+    if constexpr (W == 64)
+        v = (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
     return v;
 }
 
 template <int W>
 __device__ __forceinline__ float group_max(float v)
 {
-#pragma unroll
-    for (int off = W / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    static_assert(W == 16 || W == 32 || W == 64, "group of 16, 32 or 64 lanes");
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppMirror>(v));
+    if constexpr (W == 32) v = fmaxf(v, __shfl_xor(v, 16, kWave));
+    if constexpr (W == 64)
+        v = fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
     return v;
 }
 
-// Max over each aligned group of 16 lanes (one DPP row) with four DPP
-// moves: xor 1, xor 2 inside each quad, then the half-row and row mirrors.
-__device__ __forceinline__ float max16_dpp(float v)
-{
-    v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
-    v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
-    v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, false)); // row_half_mirror
-    v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xF, 0xF, false)); // row_mirror
-    return v;
-}
+// Max over each aligned group of 16 lanes (one DPP row).
+__device__ __forceinline__ float max16_dpp(float v) { return group_max<16>(v); }
 
 // Team reductions.  A team of TEAM lanes owns one row; TEAM <= 64 stays
 // inside a wavefront, TEAM > 64 spans TEAM/64 wavefronts of the block and
