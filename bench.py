@@ -19,7 +19,10 @@ in one hipGraph and replayed once, timed with HIP events on the replay
 stream; each step is one launch, so `roofline.achieved` (bytes over the
 kernel's average launch duration) is the same figure.  `eager_ms_per_step`
 times the same K steps as plain launches, `m1_us_per_call` is the
-graph-amortized time of one M=1 call.  `--suite` also prints one
+graph-amortized time of one M=1 call.  The default warmup (1000 untimed
+launches, ~27 ms of sustained load) brings the GPU to its steady clocks
+before the timed steps: measured on MI355X, after only 20 warmup launches
+the first two replays of the graph ran ~5% slower than later ones.  `--suite` also prints one
 line per workload (all five) to stderr.  `--profile-mode` runs a short fixed
 sequence meant to be wrapped by rocprofv3.  `--summarize` turns rocprofv3
 output into the text summaries kept under profiles/.
@@ -205,19 +208,24 @@ def time_steps(torch, case, steps, warmup):
 
 
 def time_steps_graph(torch, case, steps, warmup):
-    """`warmup` untimed eager launches, then exactly `steps` launches captured
-    in one graph and replayed once, bracketed by synchronizations and by HIP
-    events on the replay stream (the first replay, so its one-time upload is
-    inside the timed region).  Returns stream milliseconds."""
-    h = torch.cuda.current_stream().cuda_stream
-    for i in range(warmup):
-        case.step(i, h)
-    torch.cuda.synchronize()
+    """Exactly `steps` launches captured in one graph, then `warmup` untimed
+    eager launches, then the graph replayed once, bracketed by
+    synchronizations and by HIP events on the replay stream (the first
+    replay, so its one-time upload is inside the timed region).  Capturing
+    first keeps the GPU busy from the warmup straight into the timed steps:
+    measured on MI355X, after an idle gap the first ~100 launches of this
+    kernel run at ~27 us, the next ~100 at ~31 us, and it settles back near
+    27 us over a few hundred more, so a gap before the timed region (such as
+    a capture) lands the timed steps on that transient.  Returns stream
+    milliseconds."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         hh = torch.cuda.current_stream().cuda_stream
         for i in range(steps):
             case.step(warmup + i, hh)
+    h = torch.cuda.current_stream().cuda_stream
+    for i in range(warmup):
+        case.step(i, h)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -243,9 +251,12 @@ def time_launch_events(torch, case, n=100):
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
-def time_graph(torch, case, calls=20, replays=50):
+def time_graph(torch, case, calls=20, replays=50, warm_ms=25.0):
     """Per-call time of `calls` launches captured in one graph (launch gaps
-    removed), median over replays."""
+    removed), median over `replays` replays.  The replays are enqueued back
+    to back after about `warm_ms` of untimed replays, with events between
+    them and no synchronization, so the GPU stays busy at its steady clocks
+    throughout (see time_steps_graph)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -258,23 +269,27 @@ def time_graph(torch, case, calls=20, replays=50):
         h = torch.cuda.current_stream().cuda_stream
         for i in range(calls):
             case.step(i, h)
-    for _ in range(3):
-        g.replay()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    g.replay()
     torch.cuda.synchronize()
-    times = []
-    for _ in range(replays):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
+    a.record()
+    g.replay()
+    b.record()
+    b.synchronize()
+    n_warm = int(min(2000, max(1, warm_ms / max(a.elapsed_time(b), 1e-3))))
+    for _ in range(n_warm):
         g.replay()
-        b.record()
-        b.synchronize()
-        times.append(a.elapsed_time(b))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+    for e0, e1 in ev:
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    times = [e0.elapsed_time(e1) for e0, e1 in ev]
     del g
     return float(np.median(times)) / calls
 
-
-# ----------------------------------------------------------- cpu baseline --
 
 def cpu_baseline(budget_s=10.0):
     """The oracle (plain single-threaded C) on a bounded sample of the same
@@ -319,6 +334,8 @@ def read_traffic():
 # ------------------------------------------------------ profile summaries --
 
 MAIN_KERNEL_PREFIX = "void nq::k_add_rmsnorm_fp8<"
+DEFAULT_STEPS = 200
+DEFAULT_WARMUP = 1000
 COPY_KERNEL_PREFIX = "nq::k_diag_copy"
 PROFILE_COPY_BYTES = 64 << 20  # what --profile-mode's copies read and write each
 
@@ -329,7 +346,11 @@ def _csv(path):
 
 
 def summarize_trace(stats_csv, out_md, command):
-    """Text summary of a rocprofv3 --kernel-trace --stats run."""
+    """Text summary of a rocprofv3 --kernel-trace --stats run of the default
+    bench command: the per-kernel statistics, and the main kernel's average
+    over the timed window alone (its dispatches in start order: the warmup
+    launches, then the timed graph replay, then the eager reference run),
+    taken from the per-dispatch trace written next to the statistics."""
     rows = _csv(stats_csv)
     lines = [f"# rocprofv3 kernel trace: fused add+RMSNorm+FP8, M=8192, d=2816", "",
              f"Command (repository root): `{command}`", "",
@@ -339,13 +360,27 @@ def summarize_trace(stats_csv, out_md, command):
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     main = [r for r in rows if r["Name"].startswith(MAIN_KERNEL_PREFIX) and "128, 3" in r["Name"]]
     if main:
-        avg_us = float(main[0]["AverageNs"]) / 1e3
         from fp4_quantization_amd import traffic
         b = traffic.total(traffic.fused_add_rmsnorm_fp8(8192, 2816))
-        lines += ["", f"main kernel average: {avg_us:.2f} us -> {b / avg_us / 1e3:.0f} GB/s of algorithmic "
-                  f"bytes ({b} per launch), {b / avg_us / 1e3 / HBM_PEAK_GBPS * 100:.1f}% of 8 TB/s", "",
-                  "The M=8192 calls are the bench's timed and graph-replayed launches; the many short "
-                  "calls of the other shape are its M=1 latency measurements."]
+        name = main[0]["Name"]
+
+        def rate(us):
+            return f"{us:.2f} us -> {b / us / 1e3:.0f} GB/s, {b / us / 1e3 / HBM_PEAK_GBPS * 100:.1f}% of 8 TB/s"
+        lines += ["", f"Algorithmic bytes per launch: {b}.", "",
+                  f"- main kernel, all {main[0]['Calls']} dispatches: {rate(float(main[0]['AverageNs']) / 1e3)}"]
+        trace = os.path.join(os.path.dirname(stats_csv), os.path.basename(stats_csv).replace(
+            "kernel_stats", "kernel_trace"))
+        if os.path.exists(trace):
+            disp = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+                          for r in _csv(trace) if r["Kernel_Name"] == name)
+            w, k = DEFAULT_WARMUP, DEFAULT_STEPS
+            if len(disp) >= w + 2 * k:
+                dur = [(e - s0) / 1e3 for s0, e in disp]
+                timed = sum(dur[w:w + k]) / k
+                lines += [f"- timed window (dispatches {w}..{w + k - 1}, the graph replay): {rate(timed)}",
+                          f"- warmup dispatches 0..{w - 1}: {rate(sum(dur[:w]) / w)}",
+                          f"- eager reference run ({w + k}..{w + 2 * k - 1}): {rate(sum(dur[w + k:w + 2 * k]) / k)}"]
+        lines += ["", "The many short calls of the other shape are the M=1 latency measurements."]
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -427,8 +462,8 @@ def run_suite(torch, nq):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=DEFAULT_STEPS)
+    ap.add_argument("--warmup", type=int, default=DEFAULT_WARMUP)
     ap.add_argument("--suite", action="store_true", help="also time all five workloads (stderr)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-mode", action="store_true",
@@ -441,7 +476,7 @@ def main():
         stats, fetch, write = args.summarize
         summarize_trace(stats, os.path.join(ROOT, "profiles", "rmsnorm_fp8_m8192_d2816_kernel_trace.md"),
                         "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_kt -o kt --output-format csv -- "
-                        "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline")
+                        "python3 bench.py --no-cpu-baseline")
         summarize_counters(fetch, write, COUNTER_SUMMARY,
                            ["rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o fetch --output-format csv "
                             "-- python3 bench.py --profile-mode",

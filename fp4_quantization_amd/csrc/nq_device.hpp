@@ -287,6 +287,7 @@ struct RowIO<true, POLICY, T> {
     uint32_t lane_base;  // byte offset of this lane's row from the resource base
     int cols;
 
+    RowIO() = default;
     __device__ __forceinline__ RowIO(const T* base, int64_t ld, const RowMap& m, int ncols)
     {
         // A NULL tensor (absent residual or norm_out) gets an empty range:
@@ -334,6 +335,7 @@ struct RowIO<false, POLICY, T> {
     bool ok;
     int cols;
 
+    RowIO() = default;
     __device__ __forceinline__ RowIO(const T* base, int64_t ld, const RowMap& m, int ncols)
         : row(const_cast<T*>(base) + (m.ok ? m.row : 0) * ld), ok(m.ok && base != nullptr), cols(ncols) {}
 

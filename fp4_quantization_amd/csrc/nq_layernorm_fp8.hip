@@ -29,19 +29,20 @@ struct LnFp8Args {
     float eps;
 };
 
-template <int TEAM, int CPL, bool VEC>
-__global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_layernorm_fp8(LnFp8Args a)
+template <int TEAM, int CPL, bool VEC, bool STAGE, int BLOCK = row_block<TEAM, CPL, 2, VEC, STAGE>()>
+__global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
 {
-    using S = TeamShape<TEAM>;
+    using S = TeamShape<TEAM, BLOCK>;
     __shared__ double lds_mean[S::kWaves];
     __shared__ double lds_var[S::kWaves];
 
     const int t = threadIdx.x % TEAM;
-    const RowMap m = row_map<TEAM>(a.M);
+    const RowMap m = row_map<TEAM, BLOCK>(a.M);
     const int d = a.d;
     const RowIO<VEC, kLoadStream, uint16_t> xio(a.x, a.ld_x, m, d);
-    const RowIO<VEC, kKeep, float> gio(a.gamma, d, vector_map(), d);
-    const RowIO<VEC, kKeep, float> bio(a.beta, d, vector_map(), d);
+    using SV = SharedVectors<TEAM, CPL, VEC, 2, BLOCK, STAGE>;
+    __shared__ typename SV::Lds lds_gb;
+    SV gb({a.gamma, a.beta}, d);
     const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d);
 
     uint4 xw[CPL];
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_layernorm_fp8(LnFp8
         const int e = (j * TEAM + t) * 8;
         xw[j] = xio.load16(e, e < d);
     }
+    gb.issue();
 
     // mean = sum(x) / d; every bf16 x is exact in binary64 (masked = 0).
     // The unpacked row is what c replaces below, so it stays unpacked.
@@ -61,6 +63,7 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_layernorm_fp8(LnFp8
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc += (double)c[j][k];
     }
+    gb.publish(lds_gb);
     acc = team_sum<TEAM>(acc, lds_mean);
     const float mu = (float)(acc / (double)d);
     __builtin_amdgcn_sched_barrier(0);
@@ -94,8 +97,8 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_layernorm_fp8(LnFp8
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t1) * 8;
         float g[8], b[8], v[8];
-        load_f32x8(gio, e, e < d, g);
-        load_f32x8(bio, e, e < d, b);
+        gb.chunk(lds_gb, 0, e, g);
+        gb.chunk(lds_gb, 1, e, b);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float n = c[j][k] * rstd;
@@ -109,9 +112,12 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_layernorm_fp8(LnFp8
 
 template <int TEAM, int CPL, bool VEC>
 struct LnFp8Kernel {
+    template <bool STAGE>
+    static constexpr int block() { return row_block<TEAM, CPL, 2, VEC, STAGE>(); }
+    template <bool STAGE>
     static void launch(const LnFp8Args& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE>), grid, block, 0, s, a);
     }
 };
 

@@ -39,22 +39,24 @@ struct RmsFp8Args {
     float eps;
 };
 
-template <int TEAM, int CPL, bool VEC>
-__global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_fp8(RmsFp8Args a)
+template <int TEAM, int CPL, bool VEC, bool STAGE, int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
+__global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
 {
-    using S = TeamShape<TEAM>;
+    using S = TeamShape<TEAM, BLOCK>;
     __shared__ double lds_sum[S::kWaves];
     __shared__ float lds_max[S::kWaves];
 
     const int t = threadIdx.x % TEAM;
-    const RowMap m = row_map<TEAM>(a.M);
+    const RowMap m = row_map<TEAM, BLOCK>(a.M);
     const int d = a.d;
     const bool has_r = a.r != nullptr;
 
     const RowIO<VEC, kLoadStream, uint16_t> xio(a.x, a.ld_x, m, d);
     const RowIO<VEC, kLoadStream, uint16_t> rio(a.r, a.ld_r, m, d);
     const RowIO<VEC, kStoreRows, uint16_t> roio(a.ro, a.ld_ro, m, d);
-    const RowIO<VEC, kKeep, float> gio(a.gamma, d, vector_map(), d);
+    using SV = SharedVectors<TEAM, CPL, VEC, 1, BLOCK, STAGE>;
+    __shared__ typename SV::Lds lds_gamma;
+    SV gamma({a.gamma}, d);
 
     // Issue every load of the row before the first use.  A residual-less
     // row adds -0.0, which leaves x unchanged bit for bit.
@@ -66,6 +68,7 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_fp8(Rms
         xw[j] = xio.load16(e, e < d);
         rw[j] = rio.load16(e, e < d);
     }
+    gamma.issue();
 
     // z = bf16(x + r), kept packed; residual write-back; sum of z^2.
     uint4 zw[CPL];
@@ -91,6 +94,7 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_fp8(Rms
     __builtin_amdgcn_sched_barrier(0);
 
     // Reduction 1: rstd = 1 / sqrt(mean(z^2) + eps).
+    gamma.publish(lds_gamma);
     acc = team_sum<TEAM>(acc, lds_sum);
     const float ms = (float)(acc / (double)d);
     const float rstd = 1.0f / sqrtf(ms + a.eps);
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_fp8(Rms
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t1) * 8;
         float g[8], z[8];
-        load_f32x8(gio, e, e < d, g);
+        gamma.chunk(lds_gamma, 0, e, g);
         unpack_bf16x8(zw[j], z);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -159,9 +163,12 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_fp8(Rms
 
 template <int TEAM, int CPL, bool VEC>
 struct RmsFp8Kernel {
+    template <bool STAGE>
+    static constexpr int block() { return row_block<TEAM, CPL, 1, VEC, STAGE>(); }
+    template <bool STAGE>
     static void launch(const RmsFp8Args& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE>), grid, block, 0, s, a);
     }
 };
 

@@ -35,20 +35,22 @@ struct RmsFp4Args {
 };
 
 // VEC additionally needs 4-byte aligned packed-code rows (one dword per chunk).
-template <int TEAM, int CPL, bool VEC>
-__global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
+template <int TEAM, int CPL, bool VEC, bool STAGE, int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
+__global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
 {
-    using S = TeamShape<TEAM>;
+    using S = TeamShape<TEAM, BLOCK>;
     __shared__ double lds_sum[S::kWaves];
 
     const int t = threadIdx.x % TEAM;
-    const RowMap m = row_map<TEAM>(a.M);
+    const RowMap m = row_map<TEAM, BLOCK>(a.M);
     const int d = a.d;
     const bool has_r = a.r != nullptr;
     const RowIO<VEC, kLoadStream, uint16_t> xio(a.x, a.ld_x, m, d);
     const RowIO<VEC, kLoadStream, uint16_t> rio(a.r, a.ld_r, m, d);
     const RowIO<VEC, kStoreRows, uint16_t> roio(a.ro, a.ld_ro, m, d);
-    const RowIO<VEC, kKeep, float> gio(a.gamma, d, vector_map(), d);
+    using SV = SharedVectors<TEAM, CPL, VEC, 1, BLOCK, STAGE>;
+    __shared__ typename SV::Lds lds_gamma;
+    SV gamma({a.gamma}, d);
 
     // A residual-less row adds -0.0, which leaves x unchanged bit for bit.
     const uint32_t rfill = has_r ? 0u : kNegZeroBf16x2;
@@ -59,6 +61,7 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_nvfp4(R
         xw[j] = xio.load16(e, e < d);
         rw[j] = rio.load16(e, e < d);
     }
+    gamma.issue();
 
     uint4 zw[CPL];
     double acc = 0.0;
@@ -80,6 +83,7 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_nvfp4(R
             acc = fma(zd, zd, acc);
         }
     }
+    gamma.publish(lds_gamma);
     acc = team_sum<TEAM>(acc, lds_sum);
     const float ms = (float)(acc / (double)d);
     const float rstd = 1.0f / sqrtf(ms + a.eps);
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_nvfp4(R
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t1) * 8;
         float g[8], z[8], y[8];
-        load_f32x8(gio, e, e < d, g);
+        gamma.chunk(lds_gamma, 0, e, g);
         unpack_bf16x8(zw[j], z);
         float amax = 0.0f;
 #pragma unroll
@@ -125,9 +129,12 @@ __global__ __launch_bounds__(TeamShape<TEAM>::kBlock) void k_add_rmsnorm_nvfp4(R
 
 template <int TEAM, int CPL, bool VEC>
 struct RmsFp4Kernel {
+    template <bool STAGE>
+    static constexpr int block() { return row_block<TEAM, CPL, 1, VEC, STAGE>(); }
+    template <bool STAGE>
     static void launch(const RmsFp4Args& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        hipLaunchKernelGGL((k_add_rmsnorm_nvfp4<TEAM, CPL, VEC>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_add_rmsnorm_nvfp4<TEAM, CPL, VEC, STAGE>), grid, block, 0, s, a);
     }
 };
 

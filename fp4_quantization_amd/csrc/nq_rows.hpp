@@ -8,9 +8,10 @@
 // The row stays in registers between the two reductions ([FUSE] "FAQ": the
 // vector is held in registers through both phases, with the residual
 // written in place).  Blocks are 256 lanes (several rows per block) or
-// TEAM lanes when a team is larger; consecutive blocks are dealt round-robin
-// over the 8 XCDs, which measured faster than keeping neighbouring rows on
-// one XCD.
+// TEAM lanes when a team is larger, and grow to 512 or 1024 lanes where that
+// lets the vectors every row shares (gamma, beta) be staged in LDS (see
+// SharedVectors); consecutive blocks are dealt round-robin over the 8 XCDs,
+// which measured faster than keeping neighbouring rows on one XCD.
 //
 // Shape choice (pages: [NVFP4] commit notes gate schedules on problem size;
 // here the gate keys on M and d): see pick_row_shape.
@@ -84,6 +85,99 @@ __device__ __forceinline__ RowMap vector_map()
     return m;
 }
 
+// Vectors shared by every row (gamma, beta).  Loading them per row doubles
+// the load traffic that reaches the caches (measured on MI355X at d = 2816:
+// ~1.3 us of a 28 us call).  Where a block holds several rows, the block
+// loads each vector once, cooperatively, right after the first row loads,
+// writes it to LDS before the first reduction (whose barrier, or one of its
+// own for teams within a wavefront, orders the writes before every read),
+// and the lanes read their chunks from LDS.  Staged only while the LDS of
+// the blocks that fill a compute unit (32 wavefronts) stays within its
+// 160 KB; otherwise, and on the element-wise path, each lane loads its
+// chunks from memory.
+constexpr int kLanesPerCU = 2048;        // 8 wavefronts per SIMD x 4 SIMDs x 64
+constexpr int kLdsPerCU = 160 * 1024;
+
+constexpr bool stages_vectors(int team, int cpl, int nv, int block)
+{
+    return block / team >= 2 && team * cpl * 2 * 16 * nv * (kLanesPerCU / block) <= kLdsPerCU;
+}
+
+// Block size of a row kernel with NV shared vectors: with STAGE, the
+// default or the smallest larger block (up to 1024 lanes) that lets the
+// vectors be staged.  Measured at d = 2816: 2 rows per block beat 4 and 8.
+template <int TEAM, int CPL, int NV, bool VEC, bool STAGE>
+constexpr int row_block()
+{
+    if (STAGE && VEC && NV > 0)
+        for (int b = default_block<TEAM>(); b <= 1024; b *= 2)
+            if (stages_vectors(TEAM, CPL, NV, b)) return b;
+    return default_block<TEAM>();
+}
+
+template <int TEAM, int CPL, bool VEC, int NV, int BLOCK, bool STAGE>
+class SharedVectors {
+  public:
+    using S = TeamShape<TEAM, BLOCK>;
+    static constexpr int kSlots = TEAM * CPL * 2;  // 16-byte slots covering one row's chunks
+    static constexpr bool kStaged = STAGE && VEC && stages_vectors(TEAM, CPL, NV, BLOCK);
+    static constexpr int kPer = kStaged ? (kSlots + S::kBlock - 1) / S::kBlock : 1;
+    typedef uint4 Lds[kStaged ? NV : 1][kStaged ? kSlots : 1];
+    static_assert(!kStaged || kSlots * 16 * NV <= 64 * 1024, "staged vectors fit one block's LDS");
+
+    __device__ __forceinline__ SharedVectors(const float* const (&p)[NV], int d) : d_(d)
+    {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) io_[v] = RowIO<VEC, kKeep, float>(p[v], d, vector_map(), d);
+    }
+    // Issue the cooperative loads (staged only).
+    __device__ __forceinline__ void issue()
+    {
+        if constexpr (kStaged) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int u = 0; u < kPer; ++u) {
+                    const int i = u * S::kBlock + (int)threadIdx.x;
+                    held_[v][u] = io_[v].load16(i * 4, i * 4 < d_);
+                }
+        }
+    }
+    // Write the staged vectors to LDS (staged only; before the first
+    // reduction, which every lane of the block reaches).
+    __device__ __forceinline__ void publish(Lds& lds)
+    {
+        if constexpr (kStaged) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int u = 0; u < kPer; ++u) {
+                    const int i = u * S::kBlock + (int)threadIdx.x;
+                    if (i < kSlots) lds[v][i] = held_[v][u];
+                }
+            if constexpr (TEAM <= kWave) __syncthreads();
+        }
+    }
+    // 8 fp32 of vector v from element e (zeros past the end).
+    __device__ __forceinline__ void chunk(const Lds& lds, int v, int e, float g[8]) const
+    {
+        if constexpr (kStaged) {
+            const uint4 a = lds[v][e / 4], b = lds[v][e / 4 + 1];
+            g[0] = __uint_as_float(a.x); g[1] = __uint_as_float(a.y);
+            g[2] = __uint_as_float(a.z); g[3] = __uint_as_float(a.w);
+            g[4] = __uint_as_float(b.x); g[5] = __uint_as_float(b.y);
+            g[6] = __uint_as_float(b.z); g[7] = __uint_as_float(b.w);
+        } else {
+            load_f32x8(io_[v], e, e < d_, g);
+        }
+    }
+
+  private:
+    RowIO<VEC, kKeep, float> io_[NV];
+    uint4 held_[kStaged ? NV : 1][kPer];
+    int d_;
+};
+
 // Every (TEAM, CPL, VEC) shape that is compiled: teams of 16..1024 lanes
 // with at most 4 chunks (32 elements) per lane, so the fp32 row fits in
 // registers at full occupancy, plus the element-wise path (VEC = false) for
@@ -101,6 +195,7 @@ __device__ __forceinline__ RowMap vector_map()
 struct RowShape {
     int team = 0, cpl = 0;
     bool vec = false;
+    bool stage = true;  // stage shared vectors in LDS (many rows only)
 };
 
 // Rows below which the wide-team shape is used: the many-rows grid would
@@ -127,7 +222,9 @@ inline RowShape narrowest_team(int64_t d, int max_cpl)
 // lane (measured on MI355X at d = 2816: 128 lanes x 3 chunks beats 64 x 6
 // and 32 x 11 -- more, shorter wavefronts keep more rows in flight).  Few
 // rows: at most 2 chunks per lane, so one row is spread over many SIMDs and
-// its latency is close to one memory round trip.
+// its latency is close to one memory round trip, and no staging of the
+// shared vectors (its barrier and LDS round trip cost ~0.45 us at M <= 128,
+// with nothing to share across a block's rows).
 inline RowShape pick_row_shape(int64_t M, int64_t d, bool vec)
 {
     if (!vec) {
@@ -140,26 +237,44 @@ inline RowShape pick_row_shape(int64_t M, int64_t d, bool vec)
     if (s.team == 0) return s;
     const int64_t waves = M * ((s.team + 63) / 64);
     if (waves >= kFewRowsWaves) return s;
-    const RowShape wide = narrowest_team(d, 2);
-    return wide.team ? wide : s;
+    RowShape wide = narrowest_team(d, 2);
+    if (wide.team == 0) wide = s;
+    wide.stage = false;
+    return wide;
 }
 
 // Largest grid the launcher accepts.
 constexpr int64_t kMaxBlocks = 0x7FFFFFFF;
 
-// Launches K<TEAM, CPL, VEC>::launch(args, grid, block, stream) for the
-// chosen shape; false if the shape is not compiled or the grid would exceed
-// kMaxBlocks.
+// One launch of kernel shape KS with or without staging: KS::block<STAGE>()
+// lanes per block, KS::launch<STAGE>(args, grid, block, stream).
+template <class KS, int TEAM, bool STAGE, typename Args>
+inline bool launch_rows(const Args& a, int64_t M, hipStream_t stream)
+{
+    constexpr int block = KS::template block<STAGE>();
+    constexpr int rows = block / TEAM;
+    const int64_t blocks = (M + rows - 1) / rows;
+    if (blocks > kMaxBlocks) return false;
+    KS::template launch<STAGE>(a, dim3((unsigned)blocks), dim3(block), stream);
+    return true;
+}
+
+template <template <int, int, bool> class K, int T, int C, bool V, typename Args>
+inline bool launch_shape(bool stage, const Args& a, int64_t M, hipStream_t stream)
+{
+    if constexpr (V) {
+        if (stage) return launch_rows<K<T, C, V>, T, true>(a, M, stream);
+    }
+    return launch_rows<K<T, C, V>, T, false>(a, M, stream);
+}
+
+// Launches kernel K for the chosen shape; false if the shape is not
+// compiled or the grid would exceed kMaxBlocks.
 template <template <int, int, bool> class K, typename Args>
 inline bool launch_row_shape(const RowShape& s, const Args& a, int64_t M, hipStream_t stream)
 {
 #define NQ_X(T, C, V)                                                                       \
-    if (s.team == T && s.cpl == C && s.vec == V) {                                          \
-        const int64_t blocks = (M + TeamShape<T>::kRows - 1) / TeamShape<T>::kRows;         \
-        if (blocks > kMaxBlocks) return false;                                               \
-        K<T, C, V>::launch(a, dim3((unsigned)blocks), dim3(TeamShape<T>::kBlock), stream);   \
-        return true;                                                                         \
-    }
+    if (s.team == T && s.cpl == C && s.vec == V) return launch_shape<K, T, C, V>(s.stage, a, M, stream);
     NQ_ROW_SHAPES(NQ_X)
 #undef NQ_X
     return false;

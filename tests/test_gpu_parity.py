@@ -133,7 +133,7 @@ def test_rms_fp8_static_scale(nq, orc, scale):
 
 
 @pytest.mark.parametrize("d", [8, 16, 32, 111, 128, 136, 1000, 2048, 4104, 8208, 16384, 32768])
-@pytest.mark.parametrize("M", [3, 1100])
+@pytest.mark.parametrize("M", [3, 1101])
 def test_rms_fp8_ragged_d(nq, orc, d, M):
     note(f"rms fp8 ragged d={d} M={M}")
     w = W.rms_rows(M, d, 2 if d >= 16 else 0, 20.0, seed=d)
@@ -231,7 +231,7 @@ def test_layernorm_full_config_sampled(nq, orc):
 
 
 @pytest.mark.parametrize("d", [111, 256, 768, 4096, 16384])
-@pytest.mark.parametrize("M", [1, 7, 1500])
+@pytest.mark.parametrize("M", [1, 7, 1501])
 def test_layernorm_shapes(nq, orc, d, M):
     note(f"layernorm d={d} M={M}")
     w = W.layernorm_rows(M=M, d=d, seed=d + M)
@@ -239,6 +239,17 @@ def test_layernorm_shapes(nq, orc, d, M):
     rows = sample_rows(M, 24)
     o = orc.layernorm_quant_fp8(w["x"][rows], w["gamma"], w["beta"], w["eps"], w["scale"])
     assert_codes(q[rows], o["q"], "ln q")
+
+
+def test_layernorm_schedules_bitwise_equal(nq):
+    """Many rows (gamma and beta staged in LDS, several rows per block) and
+    few rows (wide team, per-lane loads) give identical codes."""
+    note("layernorm schedule equality")
+    w = W.layernorm_rows(M=2048, d=4096, seed=21)
+    big = run_ln(nq, w)
+    for lo, hi in ((0, 16), (1001, 1004), (2047, 2048)):
+        small = run_ln(nq, dict(w, x=w["x"][lo:hi], M=hi - lo))
+        assert_bits_equal(small, big[lo:hi], "ln q few-rows vs many-rows")
 
 
 def test_layernorm_graph_replay_reads_scale_on_device(nq, orc):
@@ -368,7 +379,7 @@ def compare_nvfp4(orc, w, got, rows, sg, norm_out=False):
         assert_bits_equal(got["norm_out"][rows], o["norm_out"], "norm_out")
 
 
-@pytest.mark.parametrize("M", [1, 64, 8192])
+@pytest.mark.parametrize("M", [1, 64, 1001, 8192])
 @pytest.mark.parametrize("sg_mult", [1.0, 0.25])
 def test_nvfp4_7168(nq, orc, M, sg_mult):
     note(f"nvfp4 d=7168 M={M} sg x{sg_mult}")
@@ -376,6 +387,19 @@ def test_nvfp4_7168(nq, orc, M, sg_mult):
     sg = calibrated_sg(orc, w) * sg_mult
     got = run_nvfp4(nq, w, sg, norm_out=(M == 64))
     compare_nvfp4(orc, w, got, sample_rows(M, 48), sg, norm_out=(M == 64))
+
+
+def test_nvfp4_schedules_bitwise_equal(nq, orc):
+    """Many rows (gamma staged in LDS) and few rows (wide team, per-lane
+    loads) give identical bits."""
+    note("nvfp4 schedule equality")
+    w = W.nvfp4_7168(1024)
+    sg = calibrated_sg(orc, w)
+    big = run_nvfp4(nq, w, sg)
+    for lo, hi in ((0, 16), (501, 504), (1023, 1024)):
+        small = run_nvfp4(nq, dict(w, x=w["x"][lo:hi], residual=w["residual"][lo:hi], M=hi - lo), sg)
+        for k in ("q", "sf", "residual_out"):
+            assert_bits_equal(small[k], big[k][lo:hi], f"nvfp4 {k} few-rows vs many-rows")
 
 
 @pytest.mark.parametrize("M", [1, 64, 8192])
