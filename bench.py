@@ -30,6 +30,7 @@ output into the text summaries kept under profiles/.
 from __future__ import annotations
 
 import argparse
+import re
 import hashlib
 import json
 import os
@@ -52,9 +53,14 @@ LLC_BYTES = 256 << 20
 
 
 def kernel_source_hash() -> str:
+    """Hash of the main kernel's sources with comments and blank space
+    removed, so the counter summary goes stale on a code change only."""
     h = hashlib.sha256()
     for p in MAIN_KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+        src = open(os.path.join(ROOT, p)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
