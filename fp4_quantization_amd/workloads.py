@@ -71,6 +71,12 @@ def rms_2816(M: int, seed: int = 0):
     return rms_rows(M, 2816, 28, 50.0, seed)
 
 
+def rms_group_7168(M: int, seed: int = 0):
+    """Block-FP8 consumer rows for the fused RMSNorm + group-128 quantizer:
+    d=7168, 1% = 72 outlier channels x50 (the d=2816 recipe), eps 1e-6."""
+    return rms_rows(M, 7168, 72, 50.0, seed)
+
+
 def group_t3(M: int, K: int = 4096, seed: int = 0):
     """Student-t (nu = 3) activations, bf16 [M, K]."""
     rng = np.random.default_rng(seed)

@@ -227,6 +227,31 @@ def per_token_group_quant_fp8(x, group=128, ue8m0=False, K=None):
     return dict(q=q, scale=s)
 
 
+def fused_add_rmsnorm_quant_fp8_group(x, residual, gamma, eps, group=128, ue8m0=False,
+                                      bf16_source=False, d=None, want_norm_out=False, want_y=False):
+    """O7.  Returns dict(q [M, d], scale [M, d/group], residual_out, norm_out, y)."""
+    x = _u16(x)
+    M, d, ld_x = _rows(x, d)
+    r = None if residual is None else _u16(residual)
+    ld_r = 0 if r is None else r.shape[1]
+    r_out = None if r is None else np.empty((M, d), np.uint16)
+    g = _f32(gamma)
+    assert g.size >= d
+    q = np.empty((M, d), np.uint8)
+    s = np.empty((M, d // group), np.float32)
+    n_out = np.empty((M, d), np.uint16) if want_norm_out else None
+    y = np.empty((M, d), np.float32) if want_y else None
+    zb = np.empty(d, np.float32)
+    yb = np.empty(d, np.float32)
+    _check(lib().or_fused_add_rmsnorm_quant_fp8_group(
+        _p(x, _c_u16p), _i64(ld_x), _p(r, _c_u16p), _i64(ld_r), _p(r_out, _c_u16p), _i64(d),
+        _p(g, _c_f32p), ctypes.c_float(eps), ctypes.c_int32(group), ctypes.c_int32(1 if ue8m0 else 0),
+        ctypes.c_int32(1 if bf16_source else 0), _p(q, _c_u8p), _i64(d), _p(s, _c_f32p), _i64(d // group),
+        _p(n_out, _c_u16p), _i64(d), _p(y, _c_f32p), _i64(d), _p(zb, _c_f32p), _p(yb, _c_f32p),
+        _i64(M), _i64(d)))
+    return dict(q=q, scale=s, residual_out=r_out, norm_out=n_out, y=y)
+
+
 def rmsnorm_quant_nvfp4(x, residual, gamma, eps, global_scale, d=None,
                         want_norm_out=False, want_y=False, mode_b=False):
     """O5.  Returns dict(q [M, d/2], sf [M, d/16], residual_out, norm_out, y)."""

@@ -394,6 +394,62 @@ int or_per_token_group_quant_fp8(
 }
 
 /* ------------------------------------------------------------------------ */
+/* O7: fused (residual-add +) RMSNorm + per-token-group FP8 with reciprocal  */
+/* multiply ([GRP] "Details": the fused RMSNorm + group-quant kernel, the    */
+/* fusion pass's target for block-FP8 models, uses the same reciprocal-     */
+/* multiply numerics as the standalone group quantizer).  z, residual_out,  */
+/* rstd and y as in O2; then per group of `group` contiguous elements of    */
+/* the row, exactly O4's steps on the group's values v_i:                   */
+/*   amax = max |v_i|; s = amax / 448 (UE8M0: next power of two, as O4);     */
+/*   inv = 1 / s (0 when s = 0); q_i = E4(v_i * inv); scale_out[m, g] = s.    */
+/* Source of v: y itself (fp32, the default), or with bf16_source the bf16  */
+/* rounding of y -- the unfused pipeline (norm output stored as bf16, then  */
+/* quantized), which the page's fused/unfused agreement implies.            */
+/* ------------------------------------------------------------------------ */
+int or_fused_add_rmsnorm_quant_fp8_group(
+    const uint16_t *x, int64_t ld_x,
+    const uint16_t *residual_in, int64_t ld_r,
+    uint16_t *residual_out, int64_t ld_ro,
+    const float *gamma, float eps,
+    int32_t group, int32_t ue8m0, int32_t bf16_source,
+    uint8_t *q_out, int64_t ld_q,
+    float *scale_out, int64_t ld_s,   /* [M, d / group], row stride ld_s */
+    uint16_t *norm_out, int64_t ld_n,
+    float *y_out, int64_t ld_y,
+    float *zbuf, float *ybuf, int64_t M, int64_t d)
+{
+    if (check_rows(M, d, ld_x) || group <= 0 || d % group || !gamma || !q_out || !scale_out ||
+        ld_s < d / group || !zbuf || !ybuf)
+        return OR_ERR_ARG;
+    int64_t G = d / group;
+    for (int64_t m = 0; m < M; ++m) {
+        add_rmsnorm_row(x + m * ld_x, residual_in ? residual_in + m * ld_r : NULL,
+                        residual_out ? residual_out + m * ld_ro : NULL,
+                        gamma, eps, d, zbuf, ybuf);
+        if (norm_out)
+            for (int64_t i = 0; i < d; ++i) norm_out[m * ld_n + i] = or_bf16_encode(ybuf[i]);
+        if (y_out) memcpy(y_out + m * ld_y, ybuf, (size_t)d * sizeof(float));
+        if (bf16_source)
+            for (int64_t i = 0; i < d; ++i) ybuf[i] = or_bf16_decode(or_bf16_encode(ybuf[i]));
+        for (int64_t g = 0; g < G; ++g) {
+            const float *v = ybuf + g * group;
+            float amax = 0.0f;
+            for (int32_t i = 0; i < group; ++i) {
+                float a = fabsf(v[i]);
+                if (a > amax) amax = a;
+            }
+            float s = amax / 448.0f;
+            if (ue8m0) s = pow2_ceil(s);
+            float inv = (s > 0.0f) ? 1.0f / s : 0.0f;
+            for (int32_t i = 0; i < group; ++i)
+                q_out[m * ld_q + g * group + i] = or_e4m3_encode(v[i] * inv);
+            scale_out[m * ld_s + g] = s;
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* O5: (residual-add +) RMSNorm + NVFP4 ([NVFP4] "Description", commit       */
 /* notes).  z, residual_out, rstd and y as in O2, x read with row stride     */
 /* ld_x (an in-place column slice).  With the global decode scale s_g > 0:   */

@@ -319,6 +319,129 @@ def test_group_zero_group_and_layout(orc):
     assert changed.sum() == 1 and changed[2, 2]
 
 
+# ------------------------------- O7 fused add+RMSNorm + group-128 FP8 ------
+
+def _groups(a, group=128):
+    return a.reshape(a.shape[0], -1, group)
+
+
+@pytest.mark.parametrize("wl", ["2816", "7168"])
+def test_fused_group_matches_binary64(orc, wl):
+    """Scales within 1e-6 of the binary64 group amax / 448 of the binary64 y,
+    and codes equal to e4m3 of the binary64 quotient wherever that quotient
+    is not within 2^-17 of a rounding boundary."""
+    w = W.rms_2816(M=64) if wl == "2816" else W.rms_group_7168(M=32)
+    d = w["d"]
+    o = orc.fused_add_rmsnorm_quant_fp8_group(w["x"], w["residual"], w["gamma"], w["eps"])
+    z, y64 = ref64_rms(w["x"], w["residual"], w["gamma"], w["eps"], d)
+    assert np.array_equal(o["residual_out"], z.view(torch.int16).numpy().view(np.uint16))
+    s64 = np.abs(_groups(y64)).max(axis=2) / 448.0
+    assert o["scale"].shape == (w["M"], d // 128)
+    assert np.max(np.abs(o["scale"] - s64) / s64) < 1e-6
+    codes, ok = robust_codes((_groups(y64) / s64[:, :, None]).reshape(y64.shape))
+    assert ok.mean() > 0.999
+    assert np.all(same_value(o["q"][ok], codes[ok]))
+
+
+def test_fused_group_scale_definition_and_absmax(orc):
+    """scale[m, g] = amax/448 of columns g*128 .. g*128+127 of the fp32 y (one
+    binary32 division), codes = E4(y * RN(1/s)) by PyTorch's e4m3 cast, and
+    every group's absmax element codes to +-448."""
+    w = W.rms_2816(M=48)
+    o = orc.fused_add_rmsnorm_quant_fp8_group(w["x"], w["residual"], w["gamma"], w["eps"], want_y=True)
+    g = _groups(o["y"])
+    amax = np.abs(g).max(axis=2).astype(np.float32)
+    assert np.array_equal(o["scale"], (amax / np.float32(448.0)).astype(np.float32))
+    inv = (np.float32(1) / o["scale"]).astype(np.float32)[:, :, None]
+    assert np.array_equal(_groups(o["q"]), torch_e4m3(g * inv).reshape(g.shape))
+    arg = np.abs(g).argmax(axis=2)
+    top = np.take_along_axis(_groups(o["q"]), arg[:, :, None], axis=2)
+    assert np.all((top & 0x7F) == 0x7E)
+    # reciprocal vs per-element division: one code apart on ~0.05% ([GRP])
+    div = torch_e4m3(g / o["scale"][:, :, None]).reshape(o["q"].shape)
+    differ = o["q"] != div
+    fig = GOLDEN["group_quant_divide_vs_reciprocal_flip_frac"]
+    assert differ.mean() <= fig["max"], differ.mean()
+    assert np.abs((o["q"].astype(int) & 0x7F) - (div.astype(int) & 0x7F)).max() <= 1
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_fused_group_bf16_source_is_the_unfused_pipeline(orc, ue8m0):
+    """With bf16_source the fused op equals the two-step pipeline it replaces:
+    RMSNorm with a bf16 output (O2's norm_out), then the standalone group
+    quantizer (O4) on that output -- codes and scales bit for bit ([GRP]
+    "Details": fused and unfused group-quant paths share numerics)."""
+    w = W.rms_group_7168(M=24)
+    o = orc.fused_add_rmsnorm_quant_fp8_group(w["x"], w["residual"], w["gamma"], w["eps"],
+                                              ue8m0=ue8m0, bf16_source=True, want_norm_out=True)
+    n = orc.fused_add_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], w["eps"],
+                                        want_norm_out=True)["norm_out"]
+    assert np.array_equal(o["norm_out"], n)
+    u = orc.per_token_group_quant_fp8(n, 128, ue8m0=ue8m0)
+    assert np.array_equal(o["q"], u["q"])
+    assert np.array_equal(o["scale"].view(np.uint32), u["scale"].view(np.uint32))
+    # the fp32-sourced codes differ from these only by the bf16 rounding of y
+    a = orc.fused_add_rmsnorm_quant_fp8_group(w["x"], w["residual"], w["gamma"], w["eps"], ue8m0=ue8m0)
+    assert 0.0 < (a["q"] != o["q"]).mean() < 0.05
+
+
+def test_fused_group_reduces_to_group_quant_when_norm_is_exact(orc):
+    """Rows whose mean square is exactly 1 (eps 0, so rstd = 1) and a gamma of
+    powers of two make y = z * gamma exactly: the fused op must then equal
+    O4 on those values, in both scale modes and both sources."""
+    rng = np.random.default_rng(3)
+    M, d = 6, 1024
+    z = np.empty((M, d), np.float32)
+    for m in range(M):
+        # 3k values of 0.5 and 4k of 1.25 average a square of 1 exactly; the rest are 1
+        k = 48 + 16 * m
+        v = np.concatenate([np.full(3 * k, 0.5), np.full(4 * k, 1.25), np.ones(d - 7 * k)])
+        z[m] = rng.permutation(v * rng.choice([-1.0, 1.0], d))
+    gamma = np.ldexp(1.0, rng.integers(-3, 4, d)).astype(np.float32)
+    bits = W.to_bf16_bits(z)
+    exact = W.to_bf16_bits(z * gamma)
+    for ue in (False, True):
+        ref = orc.per_token_group_quant_fp8(exact, 128, ue8m0=ue)
+        for src in (False, True):
+            o = orc.fused_add_rmsnorm_quant_fp8_group(bits, None, gamma, 0.0, ue8m0=ue,
+                                                      bf16_source=src, want_y=True)
+            assert np.array_equal(o["y"], z * gamma)
+            assert np.array_equal(o["q"], ref["q"])
+            assert np.array_equal(o["scale"], ref["scale"])
+
+
+def test_fused_group_ue8m0_and_zero_group(orc):
+    """UE8M0 scales are the smallest powers of two with amax/s <= 448, divide
+    equals reciprocal; an all-zero group gets scale 0 and zero codes, and a
+    change inside one group moves only that group's scale."""
+    w = W.rms_2816(M=16)
+    x = w["x"].copy()
+    r = w["residual"].copy()
+    x[3, 256:384] = 0
+    r[3, 256:384] = 0
+    o = orc.fused_add_rmsnorm_quant_fp8_group(x, r, w["gamma"], w["eps"], ue8m0=True, want_y=True)
+    s = o["scale"].astype(np.float64)
+    assert s[3, 2] == 0 and np.all(o["q"][3, 256:384] == 0)
+    nz = s > 0
+    assert np.all(np.frexp(s[nz])[0] == 0.5)
+    amax = np.abs(_groups(o["y"])).max(axis=2).astype(np.float64)
+    assert np.all(amax[nz] / s[nz] <= 448.0)
+    assert np.all(amax[nz] / (s[nz] / 2) > 448.0 * (1 - 2.0 ** -23))
+    div = torch_e4m3(_groups(o["y"]) / np.where(nz, o["scale"], 1)[:, :, None]).reshape(o["q"].shape)
+    assert np.array_equal(o["q"][3, :256], div[3, :256])
+    assert np.array_equal(o["q"][nz.repeat(128, axis=1)], div[nz.repeat(128, axis=1)])
+    # group locality: raising one element of group 5 of row 7 (rstd changes for
+    # the whole row, so compare with the row's other groups rescaled)
+    base = orc.fused_add_rmsnorm_quant_fp8_group(x, r, w["gamma"], w["eps"])
+    x2 = x.copy()
+    x2[7, 5 * 128 + 3] = W.to_bf16_bits(np.array([900.0], np.float32))[0]
+    o2 = orc.fused_add_rmsnorm_quant_fp8_group(x2, r, w["gamma"], w["eps"])
+    other = [m for m in range(16) if m != 7]
+    assert np.array_equal(o2["scale"][other], base["scale"][other])
+    ratio = o2["scale"][7] / base["scale"][7]
+    assert ratio[5] > 2 * np.median(ratio)
+
+
 # --------------------------------------------------- O5 NVFP4 --------------
 
 E2 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
