@@ -175,6 +175,32 @@ class Nvfp4Case(Case):
                       else f"residual-add + RMSNorm + NVFP4, M={M}, d=7168")
 
 
+class RmsGroupCase(Case):
+    """Fused add+RMSNorm + per-token-group (128) FP8 with one reciprocal per group."""
+
+    def __init__(self, torch, nq, M, d=7168, ue8m0=False):
+        from fp4_quantization_amd import workloads as W, traffic
+        w = W.rms_group_7168(M) if d == 7168 else W.rms_2816(M)
+        self.bytes = traffic.total(traffic.fused_add_rmsnorm_fp8_group(M, d))
+        x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
+        r = torch.from_numpy(w["residual"]).view(torch.bfloat16).cuda()
+        self.g = torch.from_numpy(w["gamma"]).cuda()
+        self.fn = nq.library().nq_fused_add_rmsnorm_quant_fp8_group
+        G = d // 128
+        mode = nq.NQ_SCALE_UE8M0 if ue8m0 else nq.NQ_SCALE_FP32
+        self.bufs, self.args = [], []
+        for _ in range(_sets_for(self.bytes)):
+            b = dict(x=x.clone(), r=r.clone(), ro=torch.empty_like(r),
+                     q=torch.empty(M, d, dtype=torch.uint8, device="cuda"),
+                     s=torch.empty(M, G, dtype=torch.float32, device="cuda"))
+            self.bufs.append(b)
+            self.args.append((b["x"].data_ptr(), d, b["r"].data_ptr(), d, b["ro"].data_ptr(), d,
+                              self.g.data_ptr(), w["eps"], 128, mode, 0, b["q"].data_ptr(), d,
+                              b["s"].data_ptr(), G, None, 0, M, d))
+        self.label = (f"fused add+RMSNorm + group-128 FP8 ({'UE8M0' if ue8m0 else 'fp32'} scales), "
+                      f"M={M}, d={d}")
+
+
 class CopyCase(Case):
     """The 128-bit copy kernel over the same byte count: a same-box ceiling."""
 
@@ -443,6 +469,10 @@ def run_suite(torch, nq):
         ("group_m32768_fp32", lambda: GroupCase(torch, nq, 32768)),
         ("group_m32768_ue8m0", lambda: GroupCase(torch, nq, 32768, ue8m0=True)),
         ("group_m1", lambda: GroupCase(torch, nq, 1)),
+        ("rms_group_7168_m1", lambda: RmsGroupCase(torch, nq, 1)),
+        ("rms_group_7168_m8192", lambda: RmsGroupCase(torch, nq, 8192)),
+        ("rms_group_7168_m8192_ue8m0", lambda: RmsGroupCase(torch, nq, 8192, ue8m0=True)),
+        ("rms_group_2816_m8192", lambda: RmsGroupCase(torch, nq, 8192, d=2816)),
         ("layernorm_m16384", lambda: LayerNormCase(torch, nq)),
         ("nvfp4_7168_m1", lambda: Nvfp4Case(torch, nq, 1)),
         ("nvfp4_7168_m64", lambda: Nvfp4Case(torch, nq, 64)),

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libnq.so")
 
 SOURCES = [
     "nq_rmsnorm_fp8.hip",
+    "nq_rmsnorm_fp8_group.hip",
     "nq_layernorm_fp8.hip",
     "nq_rmsnorm_nvfp4.hip",
     "nq_group_fp8.hip",

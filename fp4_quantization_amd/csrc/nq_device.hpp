@@ -227,6 +227,16 @@ __device__ __forceinline__ float team_max(float v, float* lds)
     return v;
 }
 
+// Smallest power of two >= t (t itself when it already is one; 0 stays 0):
+// with t = m * 2^e, 0.5 <= m < 1, that is t when m == 0.5, else 2^e.
+__device__ __forceinline__ float pow2_ceil(float t)
+{
+    if (t == 0.0f) return 0.0f;
+    const float m = __builtin_amdgcn_frexp_mantf(t);
+    const int e = __builtin_amdgcn_frexp_expf(t);
+    return m == 0.5f ? t : __builtin_amdgcn_ldexpf(1.0f, e);
+}
+
 // ------------------------------------------------------- division -------
 // Correctly rounded q = y / s from inv = 1 / s (itself correctly rounded):
 // q0 = y * inv is within one ulp of y / s, the remainder y - s * q0 is

@@ -32,16 +32,6 @@ constexpr int kGroup = 128;
 constexpr int kGroupBlock = 256;   // 16 groups per block per step
 constexpr int kGroupUnroll = 4;
 
-// Smallest power of two >= t (t itself when it already is one; 0 stays 0):
-// with t = m * 2^e, 0.5 <= m < 1, that is t when m == 0.5, else 2^e.
-__device__ __forceinline__ float pow2_ceil(float t)
-{
-    if (t == 0.0f) return 0.0f;
-    const float m = __builtin_amdgcn_frexp_mantf(t);
-    const int e = __builtin_amdgcn_frexp_expf(t);
-    return m == 0.5f ? t : __builtin_amdgcn_ldexpf(1.0f, e);
-}
-
 template <bool VEC, bool UE8M0>
 __global__ __launch_bounds__(kGroupBlock) void k_group_fp8(GroupArgs a)
 {

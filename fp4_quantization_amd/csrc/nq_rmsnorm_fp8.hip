@@ -20,6 +20,7 @@
 // through buffer-resource range checks instead of branches.
 #include "nq_device.hpp"
 #include "nq_host.hpp"
+#include "nq_rms_front.hpp"
 #include "nq_rows.hpp"
 
 namespace nq {
@@ -49,61 +50,16 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
     const int t = threadIdx.x % TEAM;
     const RowMap m = row_map<TEAM, BLOCK>(a.M);
     const int d = a.d;
-    const bool has_r = a.r != nullptr;
-
-    const RowIO<VEC, kLoadStream, uint16_t> xio(a.x, a.ld_x, m, d);
-    const RowIO<VEC, kLoadStream, uint16_t> rio(a.r, a.ld_r, m, d);
-    const RowIO<VEC, kStoreRows, uint16_t> roio(a.ro, a.ld_ro, m, d);
     using SV = SharedVectors<TEAM, CPL, VEC, 1, BLOCK, STAGE>;
     __shared__ typename SV::Lds lds_gamma;
     SV gamma({a.gamma}, d);
 
-    // Issue every load of the row before the first use.  A residual-less
-    // row adds -0.0, which leaves x unchanged bit for bit.
-    const uint32_t rfill = has_r ? 0u : kNegZeroBf16x2;
-    uint4 xw[CPL], rw[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int e = (j * TEAM + t) * 8;
-        xw[j] = xio.load16(e, e < d);
-        rw[j] = rio.load16(e, e < d);
-    }
-    gamma.issue();
-
-    // z = bf16(x + r), kept packed; residual write-back; sum of z^2.
     uint4 zw[CPL];
-    double acc = 0.0;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int e = (j * TEAM + t) * 8;
-        float xv[8], rv[8], z[8];
-        unpack_bf16x8(xw[j], xv);
-        unpack_bf16x8(make_uint4(rw[j].x | rfill, rw[j].y | rfill, rw[j].z | rfill, rw[j].w | rfill), rv);
-        uint32_t p[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) p[k] = pack_bf16x2(xv[2 * k] + rv[2 * k], xv[2 * k + 1] + rv[2 * k + 1]);
-        zw[j] = make_uint4(p[0], p[1], p[2], p[3]);
-        roio.store16(e, e < d, zw[j]);  // dropped when residual-less
-        unpack_bf16x8(zw[j], z);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const double zd = (double)z[k];
-            acc = fma(zd, zd, acc);  // z^2 is exact in binary64
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // Reduction 1: rstd = 1 / sqrt(mean(z^2) + eps).
-    gamma.publish(lds_gamma);
-    acc = team_sum<TEAM>(acc, lds_sum);
-    const float ms = (float)(acc / (double)d);
-    const float rstd = 1.0f / sqrtf(ms + a.eps);
-    __builtin_amdgcn_sched_barrier(0);
+    const float rstd = rms_front<TEAM, CPL, VEC>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
+                                                 lds_gamma, lds_sum, zw);
 
     // y = (z * rstd) * gamma, held in fp32 registers (at most 32 per lane),
-    // its absolute maximum, and the optional bf16 copy of y.  The packed z
-    // is laundered first so its unpacked copy from the sum above is not kept
-    // alive across the reduction.
+    // its absolute maximum, and the optional bf16 copy of y.
     float y[CPL][8];
     float amax = 0.0f;
     const RowIO<VEC, kStoreRows, uint16_t> nio(a.norm_out, a.ld_n, m, d);

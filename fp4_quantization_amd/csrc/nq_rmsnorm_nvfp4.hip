@@ -15,6 +15,7 @@
 // (d % 16 == 0 keeps both halves of a block on the same side of the end).
 #include "nq_device.hpp"
 #include "nq_host.hpp"
+#include "nq_rms_front.hpp"
 #include "nq_rows.hpp"
 
 namespace nq {
@@ -44,51 +45,16 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
     const int t = threadIdx.x % TEAM;
     const RowMap m = row_map<TEAM, BLOCK>(a.M);
     const int d = a.d;
-    const bool has_r = a.r != nullptr;
-    const RowIO<VEC, kLoadStream, uint16_t> xio(a.x, a.ld_x, m, d);
-    const RowIO<VEC, kLoadStream, uint16_t> rio(a.r, a.ld_r, m, d);
-    const RowIO<VEC, kStoreRows, uint16_t> roio(a.ro, a.ld_ro, m, d);
     using SV = SharedVectors<TEAM, CPL, VEC, 1, BLOCK, STAGE>;
     __shared__ typename SV::Lds lds_gamma;
     SV gamma({a.gamma}, d);
 
-    // A residual-less row adds -0.0, which leaves x unchanged bit for bit.
-    const uint32_t rfill = has_r ? 0u : kNegZeroBf16x2;
-    uint4 xw[CPL], rw[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int e = (j * TEAM + t) * 8;
-        xw[j] = xio.load16(e, e < d);
-        rw[j] = rio.load16(e, e < d);
-    }
-    gamma.issue();
+    const float sg = a.global_scale[0];  // issued early: read on the device at run time
 
     uint4 zw[CPL];
-    double acc = 0.0;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int e = (j * TEAM + t) * 8;
-        float xv[8], rv[8], z[8];
-        unpack_bf16x8(xw[j], xv);
-        unpack_bf16x8(make_uint4(rw[j].x | rfill, rw[j].y | rfill, rw[j].z | rfill, rw[j].w | rfill), rv);
-        uint32_t p[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) p[k] = pack_bf16x2(xv[2 * k] + rv[2 * k], xv[2 * k + 1] + rv[2 * k + 1]);
-        zw[j] = make_uint4(p[0], p[1], p[2], p[3]);
-        roio.store16(e, e < d, zw[j]);  // dropped when residual-less
-        unpack_bf16x8(zw[j], z);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const double zd = (double)z[k];
-            acc = fma(zd, zd, acc);
-        }
-    }
-    gamma.publish(lds_gamma);
-    acc = team_sum<TEAM>(acc, lds_sum);
-    const float ms = (float)(acc / (double)d);
-    const float rstd = 1.0f / sqrtf(ms + a.eps);
-    const float G = 1.0f / a.global_scale[0];  // encode scale
-    __builtin_amdgcn_sched_barrier(0);
+    const float rstd = rms_front<TEAM, CPL, VEC>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
+                                                 lds_gamma, lds_sum, zw);
+    const float G = 1.0f / sg;  // encode scale
 
     const RowIO<VEC, kStoreRows, uint16_t> nio(a.norm_out, a.ld_n, m, d);
     const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d / 2);

@@ -30,11 +30,13 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-_vp, _i64, _i32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+_vp, _i64, _i32, _u32, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
 
 _SIGS = {
     "nq_fused_add_rmsnorm_quant_fp8": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _f32, _vp, _vp, _i64,
                                        _vp, _vp, _i64, _i64, _i64, _vp],
+    "nq_fused_add_rmsnorm_quant_fp8_group": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _f32, _i32, _i32, _u32,
+                                             _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp],
     "nq_layernorm_quant_fp8": [_vp, _i64, _vp, _vp, _f32, _vp, _vp, _i64, _i64, _i64, _vp],
     "nq_per_token_group_quant_fp8": [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _i64, _vp, _vp],
     "nq_rmsnorm_quant_nvfp4": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _f32, _vp, _vp, _i64, _vp, _i64,
@@ -55,6 +57,7 @@ _lib.nq_version.restype = ctypes.c_char_p
 NQ_OK = 0
 NQ_SCALE_FP32 = 0
 NQ_SCALE_UE8M0 = 1
+NQ_FLAG_BF16_SOURCE = 1
 NQ_CODEC_E4M3 = 0
 NQ_CODEC_E2M1 = 1
 NQ_CODEC_BF16 = 2
@@ -146,6 +149,30 @@ def nq_fused_add_rmsnorm_quant_fp8(x, residual_in, residual_out, gamma, eps, sta
         _vec(scale_out, torch.float32, "scale_out", M if static_scale is None else None),
         pn, ldn, M, d, _stream(stream))
     _check(st, "nq_fused_add_rmsnorm_quant_fp8")
+
+
+def nq_fused_add_rmsnorm_quant_fp8_group(x, residual_in, residual_out, gamma, eps, q_out, scale_out,
+                                         group_size=128, scale_mode=NQ_SCALE_FP32, flags=0,
+                                         norm_out=None, stream=None):
+    """Fused (residual-add +) RMSNorm + per-token-group FP8 e4m3 (include/nq.h).
+    scale_out is a 2-D fp32 matrix [M, d / group_size] (its row stride is
+    passed through)."""
+    M, d = x.shape
+    px, ldx = _mat(x, _BF16, "x")
+    pr, ldr = _mat(residual_in, _BF16, "residual_in", d)
+    pro, ldro = _mat(residual_out, _BF16, "residual_out", d)
+    pq, ldq = _mat(q_out, _CODES8, "q_out", d)
+    ngroups = d // group_size if group_size > 0 else 0
+    ps, lds = _mat(scale_out, (torch.float32,), "scale_out", ngroups)
+    pn, ldn = _mat(norm_out, _BF16, "norm_out", d)
+    for t, n in ((residual_in, "residual_in"), (residual_out, "residual_out"), (q_out, "q_out"),
+                 (scale_out, "scale_out"), (norm_out, "norm_out")):
+        if t is not None and t.size(0) != M:
+            raise ValueError(f"{n}: expected {M} rows")
+    st = _lib.nq_fused_add_rmsnorm_quant_fp8_group(
+        px, ldx, pr, ldr, pro, ldro, _vec(gamma, torch.float32, "gamma", d), float(eps),
+        int(group_size), int(scale_mode), int(flags), pq, ldq, ps, lds, pn, ldn, M, d, _stream(stream))
+    _check(st, "nq_fused_add_rmsnorm_quant_fp8_group")
 
 
 def nq_layernorm_quant_fp8(x, gamma, beta, eps, scale, q_out, stream=None):

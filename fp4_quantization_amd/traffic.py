@@ -22,6 +22,14 @@ def fused_add_rmsnorm_fp8(M: int, d: int, residual: bool = True, static: bool = 
     return rd, wr
 
 
+def fused_add_rmsnorm_fp8_group(M: int, d: int, residual: bool = True, group: int = 128):
+    """(bytes read, bytes written) for nq_fused_add_rmsnorm_quant_fp8_group:
+    the per-token op's traffic with one fp32 scale per group instead of per row."""
+    rd = M * (2 * d + (2 * d if residual else 0)) + 4 * d
+    wr = M * ((2 * d if residual else 0) + d + 4 * (d // group))
+    return rd, wr
+
+
 def layernorm_fp8(M: int, d: int):
     rd = M * 2 * d + 8 * d + 4
     wr = M * d

@@ -70,6 +70,9 @@ typedef int nq_status;
 #define NQ_SCALE_FP32 0         /* s = amax / 448 */
 #define NQ_SCALE_UE8M0 1        /* s = amax / 448 rounded up to a power of two */
 
+/* Option bits of the entry points that take `flags`. */
+#define NQ_FLAG_BF16_SOURCE 1u  /* quantize bf16(y) instead of the fp32 y */
+
 /*
  * Fused (residual-add +) RMSNorm + per-token FP8 e4m3.
  * Defined by [FUSE] "TL;DR", "Where norm+quant sits" and "FAQ"; the static
@@ -158,6 +161,49 @@ nq_status nq_per_token_group_quant_fp8(
     const uint16_t* x, int64_t ld_x, int64_t M, int64_t K,
     int32_t group_size, int32_t scale_mode,
     uint8_t* q_out, int64_t ld_q, float* scale_out, void* stream);
+
+/*
+ * Fused (residual-add +) RMSNorm + per-token-group FP8 e4m3, one reciprocal
+ * per group (block-FP8 consumers).
+ * Defined by [GRP] "Details": the fused RMSNorm + group-quant kernel (the
+ * fusion target for block-FP8 models) quantizes with the standalone group
+ * quantizer's reciprocal-multiply numerics; the steps per group are those of
+ * nq_per_token_group_quant_fp8.
+ *
+ * Per row m:
+ *   z_i, residual_out_i, rstd, y_i   exactly as nq_fused_add_rmsnorm_quant_fp8
+ *   v_i  = y_i, or bf16(y_i) with NQ_FLAG_BF16_SOURCE (then the codes equal
+ *          the unfused pipeline: a bf16 RMSNorm output fed to
+ *          nq_per_token_group_quant_fp8)
+ *   per group g of group_size contiguous elements (d / group_size groups):
+ *     amax = max |v_i|;  s = amax / 448 (NQ_SCALE_FP32) or that value
+ *     rounded up to a power of two (NQ_SCALE_UE8M0)
+ *     inv = 1 / s (0 when s == 0);  q_i = e4m3(v_i * inv)
+ *     scale_out[m * ld_s + g] = s
+ *   norm_out_i = bf16(y_i)        only when norm_out != NULL
+ *
+ *   x            [M, d] bf16, row stride ld_x
+ *   residual_in  [M, d] bf16, row stride ld_r, or NULL (residual-less)
+ *   residual_out [M, d] bf16, row stride ld_ro; NULL iff residual_in is NULL;
+ *                may equal residual_in (in place)
+ *   gamma        [d] fp32
+ *   group_size   128 (NQ_ERR_ARG otherwise); d % group_size == 0
+ *   scale_mode   NQ_SCALE_FP32 or NQ_SCALE_UE8M0 (NQ_ERR_ARG otherwise)
+ *   flags        0 or NQ_FLAG_BF16_SOURCE (NQ_ERR_ARG for other bits)
+ *   q_out        [M, d] e4m3 codes, row stride ld_q
+ *   scale_out    [M, d / group_size] fp32, row stride ld_s (>= d / group_size)
+ *   norm_out     [M, d] bf16, row stride ld_n, or NULL
+ */
+nq_status nq_fused_add_rmsnorm_quant_fp8_group(
+    const uint16_t* x, int64_t ld_x,
+    const uint16_t* residual_in, int64_t ld_r,
+    uint16_t* residual_out, int64_t ld_ro,
+    const float* gamma, float eps,
+    int32_t group_size, int32_t scale_mode, uint32_t flags,
+    uint8_t* q_out, int64_t ld_q,
+    float* scale_out, int64_t ld_s,
+    uint16_t* norm_out, int64_t ld_n,
+    int64_t M, int64_t d, void* stream);
 
 /*
  * (Residual-add +) RMSNorm + NVFP4: packed E2M1 elements with one e4m3 scale

@@ -27,6 +27,8 @@ def lib():
     L = ctypes.CDLL(LIB)
     v, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     L.nq_fused_add_rmsnorm_quant_fp8.argtypes = [v, i64, v, i64, v, i64, v, f32, v, v, i64, v, v, i64, i64, i64, v]
+    L.nq_fused_add_rmsnorm_quant_fp8_group.argtypes = [v, i64, v, i64, v, i64, v, f32, i32, i32,
+                                                       ctypes.c_uint32, v, i64, v, i64, v, i64, i64, i64, v]
     L.nq_layernorm_quant_fp8.argtypes = [v, i64, v, v, f32, v, v, i64, i64, i64, v]
     L.nq_per_token_group_quant_fp8.argtypes = [v, i64, i64, i64, i32, i32, v, i64, v, v]
     L.nq_rmsnorm_quant_nvfp4.argtypes = [v, i64, v, i64, v, i64, v, f32, v, v, i64, v, i64, v, i64, i64, i64, v]
@@ -39,7 +41,8 @@ def lib():
 
 def test_header_declares_the_four_entry_points():
     fns = declared_functions()
-    for name in ("nq_fused_add_rmsnorm_quant_fp8", "nq_layernorm_quant_fp8",
+    for name in ("nq_fused_add_rmsnorm_quant_fp8", "nq_fused_add_rmsnorm_quant_fp8_group",
+                 "nq_layernorm_quant_fp8",
                  "nq_per_token_group_quant_fp8", "nq_rmsnorm_quant_nvfp4", "nq_status_string"):
         assert name in fns
 
@@ -95,6 +98,30 @@ def test_rmsnorm_fp8_validation(lib):
     assert rms(lib, sc=Q + 8) == NQ_ERR_ALIAS
     assert rms(lib, n=Q, ld_n=256) == NQ_ERR_ALIAS
     assert rms(lib, q=G) == NQ_ERR_ALIAS
+
+
+def test_rmsnorm_fp8_group_validation(lib):
+    def call(**kw):
+        a = dict(x=X, ld_x=2816, r=R, ld_r=2816, ro=RO, ld_ro=2816, g=G, eps=1e-6, gs=128, mode=0,
+                 flags=0, q=Q, ld_q=2816, s=SC, ld_s=22, n=None, ld_n=0, M=4, d=2816)
+        a.update(kw)
+        return lib.nq_fused_add_rmsnorm_quant_fp8_group(
+            a["x"], a["ld_x"], a["r"], a["ld_r"], a["ro"], a["ld_ro"], a["g"], a["eps"], a["gs"], a["mode"],
+            a["flags"], a["q"], a["ld_q"], a["s"], a["ld_s"], a["n"], a["ld_n"], a["M"], a["d"], None)
+    assert call(M=0) == NQ_OK
+    assert call(M=0, ro=R, mode=1, flags=1) == NQ_OK
+    assert call(gs=64) == NQ_ERR_ARG
+    assert call(mode=2) == NQ_ERR_ARG
+    assert call(flags=2) == NQ_ERR_ARG
+    assert call(eps=-1.0) == NQ_ERR_ARG
+    assert call(d=2800, ld_x=2800, ld_r=2800, ld_ro=2800, ld_q=2800) == NQ_ERR_SHAPE  # d % 128
+    assert call(ld_s=21) == NQ_ERR_STRIDE
+    assert call(ld_q=2815) == NQ_ERR_STRIDE
+    assert call(s=None) == NQ_ERR_NULL
+    assert call(ro=None) == NQ_ERR_NULL
+    assert call(s=Q + 64) == NQ_ERR_ALIAS
+    assert call(s=G + 64) == NQ_ERR_ALIAS
+    assert call(ro=R + 2) == NQ_ERR_ALIAS
 
 
 def test_layernorm_fp8_validation(lib):

@@ -208,6 +208,156 @@ def test_rms_fp8_schedules_bitwise_equal(nq):
         assert_bits_equal(small["scale"].view(np.uint32), big["scale"][lo:hi].view(np.uint32), "scale")
 
 
+# ------------------------------- RMSNorm + per-token-group (128) FP8 ------
+
+def run_rms_group(nq, w, ue8m0=False, bf16_source=False, norm_out=False, in_place=False, ld_s=None):
+    M, d = w["M"], w["d"]
+    G = d // 128
+    x = to_dev_bf16(w["x"])
+    r = to_dev_bf16(w["residual"]) if w["residual"] is not None else None
+    if r is not None and in_place:
+        ro = r
+    elif r is not None:
+        ro_buf, ro = guarded_bf16(M, d)
+    else:
+        ro = None
+    q_buf, q = guarded_u8(M, d)
+    ld_s = G if ld_s is None else ld_s
+    s_buf = torch.full((M * ld_s + GUARD // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    s = s_buf[: M * ld_s].view(M, ld_s)[:, :G]
+    n_buf, n = guarded_bf16(M, d) if norm_out else (None, None)
+    nq.nq_fused_add_rmsnorm_quant_fp8_group(
+        x[:, :d] if x.shape[1] != d else x, r, ro, to_dev_f32(w["gamma"]), w["eps"], q, s,
+        scale_mode=nq.NQ_SCALE_UE8M0 if ue8m0 else nq.NQ_SCALE_FP32,
+        flags=nq.NQ_FLAG_BF16_SOURCE if bf16_source else 0, norm_out=n)
+    torch.cuda.synchronize()
+    check_guard_u8(q_buf, M * d)
+    sh = s_buf.cpu().numpy()
+    assert np.all(np.isnan(sh[M * ld_s:])), "write past the end of scale_out"
+    if ld_s > G:  # the padding columns of every scale row are untouched
+        assert np.all(np.isnan(sh[: M * ld_s].reshape(M, ld_s)[:, G:]))
+    return dict(q=host_u8(q), scale=s.cpu().numpy(), residual_out=host_u16(ro) if ro is not None else None,
+                norm_out=host_u16(n) if n is not None else None)
+
+
+def compare_rms_group(orc, w, got, rows, ue8m0=False, bf16_source=False, norm_out=False):
+    rs = w["residual"][rows] if w["residual"] is not None else None
+    o = orc.fused_add_rmsnorm_quant_fp8_group(w["x"][rows], rs, w["gamma"], w["eps"], ue8m0=ue8m0,
+                                              bf16_source=bf16_source, d=w["d"], want_norm_out=norm_out)
+    if rs is not None:
+        assert_bits_equal(got["residual_out"][rows], o["residual_out"], "residual_out")
+    if ue8m0:  # powers of two: equal or a factor 2 apart would be a wrong rounding
+        assert_bits_equal(got["scale"][rows].view(np.uint32), o["scale"].view(np.uint32), "ue8m0 scale")
+    else:
+        assert_scales(got["scale"][rows], o["scale"], "group scale")
+    flips = assert_codes(got["q"][rows], o["q"], "q")
+    if norm_out:
+        assert_bits_equal(got["norm_out"][rows], o["norm_out"], "norm_out")
+    return flips
+
+
+@pytest.mark.parametrize("M", [1, 64, 1001, 8192])
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_rms_group_7168(nq, orc, M, ue8m0):
+    note(f"rms group fp8 d=7168 M={M} ue8m0={ue8m0}")
+    w = W.rms_group_7168(M)
+    got = run_rms_group(nq, w, ue8m0=ue8m0)
+    compare_rms_group(orc, w, got, sample_rows(M, 40), ue8m0=ue8m0)
+
+
+@pytest.mark.parametrize("M", [1, 16, 1101, 8192])
+def test_rms_group_2816(nq, orc, M):
+    note(f"rms group fp8 d=2816 M={M}")
+    w = W.rms_2816(M, seed=7)
+    got = run_rms_group(nq, w, norm_out=(M == 16))
+    compare_rms_group(orc, w, got, sample_rows(M, 64), norm_out=(M == 16))
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_rms_group_bf16_source(nq, orc, ue8m0):
+    """The bf16-sourced mode equals the oracle's (the unfused pipeline) and
+    the standalone group quantizer run on the kernel's own bf16 norm_out."""
+    note(f"rms group fp8 bf16 source ue8m0={ue8m0}")
+    w = W.rms_group_7168(96, seed=2)
+    got = run_rms_group(nq, w, ue8m0=ue8m0, bf16_source=True, norm_out=True)
+    compare_rms_group(orc, w, got, np.arange(96), ue8m0=ue8m0, bf16_source=True, norm_out=True)
+    n = to_dev_bf16(got["norm_out"])
+    q = torch.empty(96, 7168, dtype=torch.uint8, device="cuda")
+    s = torch.empty(96 * 56, dtype=torch.float32, device="cuda")
+    nq.nq_per_token_group_quant_fp8(n, q, s, scale_mode=nq.NQ_SCALE_UE8M0 if ue8m0 else nq.NQ_SCALE_FP32)
+    torch.cuda.synchronize()
+    assert_bits_equal(got["q"], host_u8(q), "fused bf16-sourced vs norm_out -> group quant")
+    assert_bits_equal(got["scale"].ravel().view(np.uint32), s.cpu().numpy().view(np.uint32), "scales")
+
+
+@pytest.mark.parametrize("d", [128, 384, 1152, 2048, 8320, 16384, 32768])
+@pytest.mark.parametrize("M", [3, 1101])
+def test_rms_group_ragged_d(nq, orc, d, M):
+    note(f"rms group fp8 d={d} M={M}")
+    w = W.rms_rows(M, d, 2, 20.0, seed=d + 1)
+    got = run_rms_group(nq, w, norm_out=True)
+    compare_rms_group(orc, w, got, sample_rows(M, 24), norm_out=True)
+
+
+def test_rms_group_in_place_residual_less_strided_scales(nq, orc):
+    note("rms group fp8 in-place / residual-less / scale row stride")
+    w = W.rms_2816(64, seed=8)
+    got = run_rms_group(nq, w, in_place=True, ld_s=29)
+    compare_rms_group(orc, w, got, np.arange(64))
+    w2 = dict(w, residual=None)
+    got2 = run_rms_group(nq, w2, ue8m0=True)
+    compare_rms_group(orc, w2, got2, np.arange(64), ue8m0=True)
+
+
+def test_rms_group_zero_groups_and_element_path(nq, orc):
+    """All-zero groups give scale 0 and zero codes; a row stride of d+1
+    forces the element-wise path, which must match the 128-bit path."""
+    note("rms group fp8 zero groups / element-wise path")
+    M, d = 33, 2816
+    w = W.rms_2816(M, seed=9)
+    x, r = w["x"].copy(), w["residual"].copy()
+    x[4, 128:512] = 0; r[4, 128:512] = 0
+    x[9] = 0; r[9] = 0
+    w = dict(w, x=x, residual=r)
+    base = run_rms_group(nq, w)
+    compare_rms_group(orc, w, base, np.arange(M))
+    assert np.all(base["scale"][4, 1:4] == 0) and np.all(base["q"][4, 128:512] == 0)
+    assert np.all(base["scale"][9] == 0) and np.all(base["q"][9] == 0)
+    xs = np.zeros((M, d + 1), np.uint16); xs[:, :d] = x
+    rs = np.zeros((M, d + 1), np.uint16); rs[:, :d] = r
+    xd, rd = to_dev_bf16(xs), to_dev_bf16(rs)
+    ro = torch.empty(M, d, dtype=torch.bfloat16, device="cuda")
+    q = torch.empty(M, d, dtype=torch.uint8, device="cuda")
+    s = torch.empty(M, d // 128, dtype=torch.float32, device="cuda")
+    nq.nq_fused_add_rmsnorm_quant_fp8_group(xd[:, :d], rd[:, :d], ro, to_dev_f32(w["gamma"]), w["eps"], q, s)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_u8(q), base["q"], "q element-wise vs vector path")
+    assert_bits_equal(s.cpu().numpy().view(np.uint32), base["scale"].view(np.uint32), "scale")
+    assert_bits_equal(host_u16(ro), base["residual_out"], "residual_out")
+
+
+def test_rms_group_schedules_bitwise_equal(nq):
+    """Many rows (gamma staged in LDS) and few rows (wide team) give
+    identical bits."""
+    note("rms group fp8 schedule equality")
+    w = W.rms_group_7168(1024, seed=4)
+    big = run_rms_group(nq, w)
+    for lo, hi in ((0, 16), (501, 504), (1023, 1024)):
+        small = run_rms_group(nq, dict(w, x=w["x"][lo:hi], residual=w["residual"][lo:hi], M=hi - lo))
+        for k in ("q", "residual_out"):
+            assert_bits_equal(small[k], big[k][lo:hi], f"{k} few-rows vs many-rows")
+        assert_bits_equal(small["scale"].view(np.uint32), big["scale"][lo:hi].view(np.uint32), "scale")
+
+
+def test_rms_group_empty(nq):
+    note("rms group fp8 M=0")
+    x = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
+    q = torch.empty(0, 256, dtype=torch.uint8, device="cuda")
+    s = torch.empty(0, 2, dtype=torch.float32, device="cuda")
+    nq.nq_fused_add_rmsnorm_quant_fp8_group(x, None, None, torch.ones(256, device="cuda"), 1e-6, q, s)
+    torch.cuda.synchronize()
+
+
 # --------------------------------------------------- LayerNorm + FP8 ------
 
 def run_ln(nq, w, scale_t=None):
