@@ -60,7 +60,12 @@ def lib() -> ctypes.CDLL:
         L.or_e2m1_encode.argtypes = [ctypes.c_float]
         L.or_e2m1_decode.restype = ctypes.c_float
         L.or_e2m1_decode.argtypes = [ctypes.c_uint8]
-        for name in ("or_bf16_encode_n", "or_e4m3_encode_n", "or_e4m3_decode_n", "or_e2m1_encode_n"):
+        L.or_e5m2_encode.restype = ctypes.c_uint8
+        L.or_e5m2_encode.argtypes = [ctypes.c_float]
+        L.or_e5m2_decode.restype = ctypes.c_float
+        L.or_e5m2_decode.argtypes = [ctypes.c_uint8]
+        for name in ("or_bf16_encode_n", "or_e4m3_encode_n", "or_e4m3_decode_n", "or_e2m1_encode_n",
+                     "or_e5m2_encode_n", "or_e5m2_decode_n"):
             getattr(L, name).restype = None
         L.or_name.restype = ctypes.c_char_p
         _lib = L
@@ -114,6 +119,29 @@ def e4m3_decode(c) -> np.ndarray:
     return out.reshape(c.shape)
 
 
+def e5m2_encode(v) -> np.ndarray:
+    v = _f32(v)
+    flat = v.ravel()
+    out = np.empty(flat.shape, np.uint8)
+    lib().or_e5m2_encode_n(_p(flat, _c_f32p), _p(out, _c_u8p), _i64(flat.size))
+    return out.reshape(v.shape)
+
+
+def e5m2_decode(c) -> np.ndarray:
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    flat = c.ravel()
+    out = np.empty(flat.shape, np.float32)
+    lib().or_e5m2_decode_n(_p(flat, _c_u8p), _p(out, _c_f32p), _i64(flat.size))
+    return out.reshape(c.shape)
+
+
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
+def _fmt(fmt: str) -> ctypes.c_int32:
+    return ctypes.c_int32(FP8_FORMATS[fmt])
+
+
 def e2m1_encode(v) -> np.ndarray:
     v = _f32(v)
     flat = v.ravel()
@@ -142,9 +170,10 @@ def _check(rc):
 # ------------------------------------------------------------------- ops ---
 
 def fused_add_rmsnorm_quant_fp8(x, residual, gamma, eps, static_scale=None, d=None,
-                                want_norm_out=False, want_y=False):
+                                want_norm_out=False, want_y=False, fmt="e4m3"):
     """O2.  x, residual: uint16 [M, ld] (residual may be None); reads the
-    first d columns.  Returns dict(q, scale, residual_out, norm_out, y)."""
+    first d columns; fmt "e4m3" or "e5m2".  Returns dict(q, scale,
+    residual_out, norm_out, y)."""
     x = _u16(x)
     M, d, ld_x = _rows(x, d)
     r = None if residual is None else _u16(residual)
@@ -164,11 +193,11 @@ def fused_add_rmsnorm_quant_fp8(x, residual, gamma, eps, static_scale=None, d=No
         _p(r_out, _c_u16p), _i64(d), _p(g, _c_f32p), ctypes.c_float(eps),
         _p(ss, _c_f32p), _p(q, _c_u8p), _i64(d), _p(scale, _c_f32p),
         _p(n_out, _c_u16p), _i64(d), _p(y, _c_f32p), _i64(d),
-        _p(zb, _c_f32p), _p(yb, _c_f32p), _i64(M), _i64(d)))
+        _p(zb, _c_f32p), _p(yb, _c_f32p), _fmt(fmt), _i64(M), _i64(d)))
     return dict(q=q, scale=scale, residual_out=r_out, norm_out=n_out, y=y)
 
 
-def quant_fp8_rows(y, static_scale=None):
+def quant_fp8_rows(y, static_scale=None, fmt="e4m3"):
     """The quantization step of O2 alone, on fp32 rows y [M, d]."""
     y = _f32(y)
     M, d = y.shape
@@ -176,7 +205,7 @@ def quant_fp8_rows(y, static_scale=None):
     scale = None if static_scale is not None else np.empty(M, np.float32)
     ss = None if static_scale is None else np.array([static_scale], np.float32)
     _check(lib().or_quant_fp8_rows(_p(y, _c_f32p), _i64(M), _i64(d), _p(ss, _c_f32p),
-                                   _p(q, _c_u8p), _p(scale, _c_f32p)))
+                                   _p(q, _c_u8p), _p(scale, _c_f32p), _fmt(fmt)))
     return dict(q=q, scale=scale)
 
 
@@ -199,23 +228,26 @@ def unfused_rmsnorm_quant_fp8(x, residual, gamma, eps, static_scale=None, d=None
     return dict(q=q, scale=scale)
 
 
-def layernorm_quant_fp8(x, gamma, beta, eps, scale, d=None, want_y=False):
-    """O3.  Returns dict(q, y)."""
+def layernorm_quant_fp8(x, gamma, beta, eps, scale=None, d=None, want_y=False, fmt="e4m3"):
+    """O3 (static: `scale` given) or O8 (dynamic per-token: scale None).
+    Returns dict(q, scale (dynamic only), y)."""
     x = _u16(x)
     M, d, ld_x = _rows(x, d)
     g, b = _f32(gamma), _f32(beta)
     q = np.empty((M, d), np.uint8)
     y = np.empty((M, d), np.float32) if want_y else None
-    ss = np.array([scale], np.float32)
+    ss = None if scale is None else np.array([scale], np.float32)
+    so = np.empty(M, np.float32) if scale is None else None
     cb = np.empty(d, np.float32)
+    yb = np.empty(d, np.float32)
     _check(lib().or_layernorm_quant_fp8(
         _p(x, _c_u16p), _i64(ld_x), _p(g, _c_f32p), _p(b, _c_f32p), ctypes.c_float(eps),
-        _p(ss, _c_f32p), _p(q, _c_u8p), _i64(d), _p(y, _c_f32p), _i64(d),
-        _p(cb, _c_f32p), _i64(M), _i64(d)))
-    return dict(q=q, y=y)
+        _p(ss, _c_f32p), _p(q, _c_u8p), _i64(d), _p(so, _c_f32p), _p(y, _c_f32p), _i64(d),
+        _p(cb, _c_f32p), _p(yb, _c_f32p), _fmt(fmt), _i64(M), _i64(d)))
+    return dict(q=q, scale=so, y=y)
 
 
-def per_token_group_quant_fp8(x, group=128, ue8m0=False, K=None):
+def per_token_group_quant_fp8(x, group=128, ue8m0=False, K=None, fmt="e4m3"):
     """O4.  Returns dict(q [M, K], scale [M, K/group])."""
     x = _u16(x)
     M, K, ld_x = _rows(x, K)
@@ -223,12 +255,13 @@ def per_token_group_quant_fp8(x, group=128, ue8m0=False, K=None):
     s = np.empty((M, K // group), np.float32)
     _check(lib().or_per_token_group_quant_fp8(
         _p(x, _c_u16p), _i64(ld_x), _i64(M), _i64(K), ctypes.c_int32(group),
-        ctypes.c_int32(1 if ue8m0 else 0), _p(q, _c_u8p), _i64(K), _p(s, _c_f32p)))
+        ctypes.c_int32(1 if ue8m0 else 0), _p(q, _c_u8p), _i64(K), _p(s, _c_f32p), _fmt(fmt)))
     return dict(q=q, scale=s)
 
 
 def fused_add_rmsnorm_quant_fp8_group(x, residual, gamma, eps, group=128, ue8m0=False,
-                                      bf16_source=False, d=None, want_norm_out=False, want_y=False):
+                                      bf16_source=False, d=None, want_norm_out=False, want_y=False,
+                                      fmt="e4m3"):
     """O7.  Returns dict(q [M, d], scale [M, d/group], residual_out, norm_out, y)."""
     x = _u16(x)
     M, d, ld_x = _rows(x, d)
@@ -248,7 +281,7 @@ def fused_add_rmsnorm_quant_fp8_group(x, residual, gamma, eps, group=128, ue8m0=
         _p(g, _c_f32p), ctypes.c_float(eps), ctypes.c_int32(group), ctypes.c_int32(1 if ue8m0 else 0),
         ctypes.c_int32(1 if bf16_source else 0), _p(q, _c_u8p), _i64(d), _p(s, _c_f32p), _i64(d // group),
         _p(n_out, _c_u16p), _i64(d), _p(y, _c_f32p), _i64(d), _p(zb, _c_f32p), _p(yb, _c_f32p),
-        _i64(M), _i64(d)))
+        _fmt(fmt), _i64(M), _i64(d)))
     return dict(q=q, scale=s, residual_out=r_out, norm_out=n_out, y=y)
 
 

@@ -28,9 +28,13 @@
  * operation order; the readings taken here are listed in the repository's
  * design notes and repeated at each function.
  *
+ * FP8 outputs are e4m3 (largest finite 448) or e5m2 (largest finite 57344),
+ * chosen per call; dynamic scales divide by the chosen format's largest
+ * finite value.
+ *
  * Pinning.  Every function here is checked by the CPU tests against things
  * other than itself: closed forms of the formats, library conversions
- * (PyTorch's bf16 and float8_e4m3fn casts), brute force on small inputs, an
+ * (PyTorch's bf16, float8_e4m3fn and float8_e5m2 casts), brute force on small inputs, an
  * independent binary64 recomputation, and invariants and statistics the pages
  * state.  One part is "parity unpinned": the NVFP4 block-scale operation order
  * and the meaning of the global scale (or_rmsnorm_quant_nvfp4) are fixed by no
@@ -127,6 +131,47 @@ uint8_t or_e4m3_encode(float v)
     return (uint8_t)(code | (signbit(v) ? 0x80u : 0u));
 }
 
+/* ------------------------------------------------------------------------ */
+/* OCP FP8 E5M2: 1 sign, 5 exponent bits (bias 15), 2 mantissa bits;         */
+/* exponent 31 holds infinities (mantissa 0) and NaNs; largest finite 57344. */
+/* [LNQ] "Description" and "Tests": the FP8 output may be e4m3 or e5m2.      */
+/* The encoder saturates like the e4m3 one (clamp to +-57344, then nearest,  */
+/* ties to even): a scaled value never becomes infinite.                     */
+/* ------------------------------------------------------------------------ */
+
+float or_e5m2_decode(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 2) & 0x1F, m = c & 0x3;
+    float mag;
+    if (e == 0x1F) mag = m ? NAN : INFINITY;
+    else if (e == 0) mag = ldexpf((float)m / 4.0f, -14);          /* subnormal */
+    else             mag = ldexpf(1.0f + (float)m / 4.0f, e - 15); /* normal */
+    return sign ? -mag : mag;
+}
+
+static double e5m2_mags[124];
+static int e5m2_ready = 0;
+
+uint8_t or_e5m2_encode(float v)
+{
+    if (!e5m2_ready) {
+        for (unsigned c = 0; c < 124; ++c) e5m2_mags[c] = (double)or_e5m2_decode((uint8_t)c);
+        e5m2_ready = 1;
+    }
+    unsigned code = nearest_code(fabsf(v), e5m2_mags, 124);
+    return (uint8_t)(code | (signbit(v) ? 0x80u : 0u));
+}
+
+/* The FP8 format an op writes: 0 = e4m3 (largest finite 448), 1 = e5m2
+ * (largest finite 57344).  Dynamic scales divide the absolute maximum by
+ * the format's largest finite value. */
+#define OR_FP8_E4M3 0
+#define OR_FP8_E5M2 1
+
+static float fp8_max(int32_t fmt) { return fmt == OR_FP8_E5M2 ? 57344.0f : 448.0f; }
+static uint8_t fp8_encode(float v, int32_t fmt)
+{ return fmt == OR_FP8_E5M2 ? or_e5m2_encode(v) : or_e4m3_encode(v); }
+
 /* E2M1 (the 4-bit element of NVFP4 [NVFP4] "Description"): magnitudes
  * 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7 and bit 3 the sign. */
 float or_e2m1_decode(uint8_t c)
@@ -153,6 +198,10 @@ void or_e4m3_decode_n(const uint8_t *c, float *out, int64_t n)
 { for (int64_t i = 0; i < n; ++i) out[i] = or_e4m3_decode(c[i]); }
 void or_e2m1_encode_n(const float *v, uint8_t *out, int64_t n)
 { for (int64_t i = 0; i < n; ++i) out[i] = or_e2m1_encode(v[i]); }
+void or_e5m2_encode_n(const float *v, uint8_t *out, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) out[i] = or_e5m2_encode(v[i]); }
+void or_e5m2_decode_n(const uint8_t *c, float *out, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) out[i] = or_e5m2_decode(c[i]); }
 
 /* ------------------------------------------------------------------------ */
 /* Shared row steps, written out once in the order the pages describe.       */
@@ -207,38 +256,39 @@ static void add_rmsnorm_row(const uint16_t *x, const uint16_t *r, uint16_t *r_ou
  * the formula itself is not printed there, so this follows the plain
  * reading: scale = amax / 448, code = E4(y / scale), one division per
  * element ([GRP] "Details": per-token FP8 keeps exact per-element
- * division).  An all-zero row stores scale 0 and codes 0. */
-static float quant_fp8_dynamic_row(const float *y, int64_t d, uint8_t *q)
+ * division); for e5m2 the divisor is 57344.  An all-zero row stores scale
+ * 0 and codes 0. */
+static float quant_fp8_dynamic_row(const float *y, int64_t d, uint8_t *q, int32_t fmt)
 {
     float amax = 0.0f;
     for (int64_t i = 0; i < d; ++i) {
         float a = fabsf(y[i]);
         if (a > amax) amax = a;
     }
-    float s = amax / 448.0f;
+    float s = amax / fp8_max(fmt);
     for (int64_t i = 0; i < d; ++i)
-        q[i] = (s > 0.0f) ? or_e4m3_encode(y[i] / s) : 0u;
+        q[i] = (s > 0.0f) ? fp8_encode(y[i] / s, fmt) : 0u;
     return s;
 }
 
 /* Static FP8 of one fp32 row: out = y / scale, applied as y * (1 / scale)
  * ([LNQ] "Description": the scale divides; [GRAPH] "Changes": the kernel
  * forms scale_inv = 1 / scale[0] from the one-element tensor). */
-static void quant_fp8_static_row(const float *y, int64_t d, float inv, uint8_t *q)
+static void quant_fp8_static_row(const float *y, int64_t d, float inv, uint8_t *q, int32_t fmt)
 {
-    for (int64_t i = 0; i < d; ++i) q[i] = or_e4m3_encode(y[i] * inv);
+    for (int64_t i = 0; i < d; ++i) q[i] = fp8_encode(y[i] * inv, fmt);
 }
 
 /* The quantization step of O2 on its own, for rows of fp32 values the test
  * chooses (dynamic when static_scale is NULL).  Same code as above. */
 int or_quant_fp8_rows(const float *y, int64_t M, int64_t d, const float *static_scale,
-                      uint8_t *q, float *scale_out)
+                      uint8_t *q, float *scale_out, int32_t fmt)
 {
     if (M < 0 || d <= 0 || !y || !q || (!static_scale && !scale_out)) return OR_ERR_ARG;
     float inv = static_scale ? 1.0f / static_scale[0] : 0.0f;
     for (int64_t m = 0; m < M; ++m) {
-        if (static_scale) quant_fp8_static_row(y + m * d, d, inv, q + m * d);
-        else scale_out[m] = quant_fp8_dynamic_row(y + m * d, d, q + m * d);
+        if (static_scale) quant_fp8_static_row(y + m * d, d, inv, q + m * d, fmt);
+        else scale_out[m] = quant_fp8_dynamic_row(y + m * d, d, q + m * d, fmt);
     }
     return OR_OK;
 }
@@ -262,6 +312,7 @@ int or_fused_add_rmsnorm_quant_fp8(
     uint16_t *norm_out, int64_t ld_n,/* optional bf16(y) */
     float *y_out, int64_t ld_y,      /* optional fp32 y, for the tests */
     float *zbuf, float *ybuf,        /* caller scratch, d floats each */
+    int32_t fmt,                     /* OR_FP8_E4M3 or OR_FP8_E5M2 */
     int64_t M, int64_t d)
 {
     if (check_rows(M, d, ld_x) || !gamma || !q_out || !zbuf || !ybuf) return OR_ERR_ARG;
@@ -271,8 +322,8 @@ int or_fused_add_rmsnorm_quant_fp8(
         add_rmsnorm_row(x + m * ld_x, residual_in ? residual_in + m * ld_r : NULL,
                         residual_out ? residual_out + m * ld_ro : NULL,
                         gamma, eps, d, zbuf, ybuf);
-        if (static_scale) quant_fp8_static_row(ybuf, d, inv, q_out + m * ld_q);
-        else scale_out[m] = quant_fp8_dynamic_row(ybuf, d, q_out + m * ld_q);
+        if (static_scale) quant_fp8_static_row(ybuf, d, inv, q_out + m * ld_q, fmt);
+        else scale_out[m] = quant_fp8_dynamic_row(ybuf, d, q_out + m * ld_q, fmt);
         if (norm_out)
             for (int64_t i = 0; i < d; ++i) norm_out[m * ld_n + i] = or_bf16_encode(ybuf[i]);
         if (y_out) memcpy(y_out + m * ld_y, ybuf, (size_t)d * sizeof(float));
@@ -301,8 +352,8 @@ int or_unfused_rmsnorm_quant_fp8(
         add_rmsnorm_row(x + m * ld_x, residual_in ? residual_in + m * ld_r : NULL,
                         NULL, gamma, eps, d, zbuf, ybuf);
         for (int64_t i = 0; i < d; ++i) ybuf[i] = or_bf16_decode(or_bf16_encode(ybuf[i]));
-        if (static_scale) quant_fp8_static_row(ybuf, d, inv, q_out + m * ld_q);
-        else scale_out[m] = quant_fp8_dynamic_row(ybuf, d, q_out + m * ld_q);
+        if (static_scale) quant_fp8_static_row(ybuf, d, inv, q_out + m * ld_q, OR_FP8_E4M3);
+        else scale_out[m] = quant_fp8_dynamic_row(ybuf, d, q_out + m * ld_q, OR_FP8_E4M3);
     }
     return OR_OK;
 }
@@ -314,18 +365,25 @@ int or_unfused_rmsnorm_quant_fp8(
 /*   var = mean(c^2)                   (population variance, two passes)     */
 /*   rstd = 1 / sqrt(var + eps)                                              */
 /*   y_i = ((c_i * rstd) * gamma_i) + beta_i                                 */
-/*   q_i = E4(y_i * (1 / scale[0]))                                          */
+/*   q_i = E(y_i * (1 / scale[0]))                                           */
+/* O8: the same y with a dynamic per-token scale instead ([LNQ]             */
+/* "Description": the library's LayerNorm also has a per-token path, left   */
+/* unconnected there): s = amax(y) / fmax -> scale_out[m], q_i = E(y_i / s), */
+/* one division per element like the RMSNorm per-token op ([GRP] "Details"). */
+/* E is e4m3 or e5m2 (fmt; [LNQ] "Tests" cover both).                       */
 /* ------------------------------------------------------------------------ */
 int or_layernorm_quant_fp8(
     const uint16_t *x, int64_t ld_x,
     const float *gamma, const float *beta, float eps,
-    const float *scale,               /* host pointer to the one element */
+    const float *scale,               /* host pointer to the one element; NULL = dynamic */
     uint8_t *q_out, int64_t ld_q,
+    float *scale_out,                 /* [M], dynamic only */
     float *y_out, int64_t ld_y,       /* optional */
-    float *cbuf, int64_t M, int64_t d)
+    float *cbuf, float *ybuf, int32_t fmt, int64_t M, int64_t d)
 {
-    if (check_rows(M, d, ld_x) || !gamma || !beta || !scale || !q_out || !cbuf) return OR_ERR_ARG;
-    float inv = 1.0f / scale[0];
+    if (check_rows(M, d, ld_x) || !gamma || !beta || !q_out || !cbuf || !ybuf) return OR_ERR_ARG;
+    if (!scale && !scale_out) return OR_ERR_ARG;
+    float inv = scale ? 1.0f / scale[0] : 0.0f;
     for (int64_t m = 0; m < M; ++m) {
         const uint16_t *xr = x + m * ld_x;
         double s = 0.0;
@@ -340,10 +398,11 @@ int or_layernorm_quant_fp8(
         for (int64_t i = 0; i < d; ++i) {
             float n = cbuf[i] * rstd;
             float g = n * gamma[i];
-            float y = g + beta[i];
-            q_out[m * ld_q + i] = or_e4m3_encode(y * inv);
-            if (y_out) y_out[m * ld_y + i] = y;
+            ybuf[i] = g + beta[i];
         }
+        if (scale) quant_fp8_static_row(ybuf, d, inv, q_out + m * ld_q, fmt);
+        else scale_out[m] = quant_fp8_dynamic_row(ybuf, d, q_out + m * ld_q, fmt);
+        if (y_out) memcpy(y_out + m * ld_y, ybuf, (size_t)d * sizeof(float));
     }
     return OR_OK;
 }
@@ -357,6 +416,7 @@ int or_layernorm_quant_fp8(
 /*               the next power of two above t (so |x| / s <= 448)           */
 /*   inv = 1 / s (one correctly rounded division per group; 0 when s = 0)    */
 /*   q_i = E4(x_i * inv);  scales stored row-major [M, K / group]            */
+/* For e5m2 output (fmt) 448 becomes 57344 and E4 becomes E5.                */
 /* ------------------------------------------------------------------------ */
 static float pow2_ceil(float t)
 {
@@ -369,7 +429,7 @@ static float pow2_ceil(float t)
 
 int or_per_token_group_quant_fp8(
     const uint16_t *x, int64_t ld_x, int64_t M, int64_t K, int32_t group,
-    int32_t ue8m0, uint8_t *q_out, int64_t ld_q, float *scale_out)
+    int32_t ue8m0, uint8_t *q_out, int64_t ld_q, float *scale_out, int32_t fmt)
 {
     if (M < 0 || K <= 0 || group <= 0 || K % group || ld_x < K || !q_out || !scale_out)
         return OR_ERR_ARG;
@@ -382,11 +442,11 @@ int or_per_token_group_quant_fp8(
                 float a = fabsf(or_bf16_decode(xg[i]));
                 if (a > amax) amax = a;
             }
-            float s = amax / 448.0f;
+            float s = amax / fp8_max(fmt);
             if (ue8m0) s = pow2_ceil(s);
             float inv = (s > 0.0f) ? 1.0f / s : 0.0f;
             for (int32_t i = 0; i < group; ++i)
-                q_out[m * ld_q + g * group + i] = or_e4m3_encode(or_bf16_decode(xg[i]) * inv);
+                q_out[m * ld_q + g * group + i] = fp8_encode(or_bf16_decode(xg[i]) * inv, fmt);
             scale_out[m * G + g] = s;
         }
     }
@@ -402,6 +462,7 @@ int or_per_token_group_quant_fp8(
 /* the row, exactly O4's steps on the group's values v_i:                   */
 /*   amax = max |v_i|; s = amax / 448 (UE8M0: next power of two, as O4);     */
 /*   inv = 1 / s (0 when s = 0); q_i = E4(v_i * inv); scale_out[m, g] = s.    */
+/* (e5m2 output: 57344 and E5 in place of 448 and E4.)                      */
 /* Source of v: y itself (fp32, the default), or with bf16_source the bf16  */
 /* rounding of y -- the unfused pipeline (norm output stored as bf16, then  */
 /* quantized), which the page's fused/unfused agreement implies.            */
@@ -416,7 +477,7 @@ int or_fused_add_rmsnorm_quant_fp8_group(
     float *scale_out, int64_t ld_s,   /* [M, d / group], row stride ld_s */
     uint16_t *norm_out, int64_t ld_n,
     float *y_out, int64_t ld_y,
-    float *zbuf, float *ybuf, int64_t M, int64_t d)
+    float *zbuf, float *ybuf, int32_t fmt, int64_t M, int64_t d)
 {
     if (check_rows(M, d, ld_x) || group <= 0 || d % group || !gamma || !q_out || !scale_out ||
         ld_s < d / group || !zbuf || !ybuf)
@@ -438,11 +499,11 @@ int or_fused_add_rmsnorm_quant_fp8_group(
                 float a = fabsf(v[i]);
                 if (a > amax) amax = a;
             }
-            float s = amax / 448.0f;
+            float s = amax / fp8_max(fmt);
             if (ue8m0) s = pow2_ceil(s);
             float inv = (s > 0.0f) ? 1.0f / s : 0.0f;
             for (int32_t i = 0; i < group; ++i)
-                q_out[m * ld_q + g * group + i] = or_e4m3_encode(v[i] * inv);
+                q_out[m * ld_q + g * group + i] = fp8_encode(v[i] * inv, fmt);
             scale_out[m * ld_s + g] = s;
         }
     }

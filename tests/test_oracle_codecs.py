@@ -1,6 +1,6 @@
 """Pins of the oracle's number formats against things other than itself.
 
-e4m3 and bf16 are checked against PyTorch's own casts (library routines, a
+e4m3, e5m2 and bf16 are checked against PyTorch's own casts (library routines, a
 different implementation) and against a brute-force nearest-value search in
 binary64 written here; E2M1 against the brute-force search and the format's
 eight magnitudes.  Format sources: the FP8 formats paper that "Fusing RMSNorm
@@ -101,6 +101,68 @@ def test_e4m3_encode_nearest_by_search(orc):
 # ----------------------------------------------------------------- E2M1 ----
 
 E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+# ----------------------------------------------------------------- e5m2 ----
+# OCP FP8 e5m2 (the second FP8 output format of "feat: fused FP8 quantization
+# output for LayerNorm", "Description" and "Tests"): bias 15, 2 mantissa bits,
+# exponent 31 for infinities and NaNs, largest finite 57344.
+
+def _torch_e5m2(v: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.clip(v, -57344.0, 57344.0).astype(np.float32))
+    return t.to(torch.float8_e5m2).view(torch.uint8).numpy()
+
+
+def test_e5m2_decode_matches_torch_all_codes(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    ours = orc.e5m2_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float32).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert sorted(np.nonzero(nan)[0].tolist()) == [0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF]
+    assert ours[0x7C] == np.inf and ours[0xFC] == -np.inf
+
+
+def test_e5m2_landmarks(orc):
+    v = orc.e5m2_decode(np.arange(256, dtype=np.uint8))
+    assert float(v[0x7B]) == 57344.0                    # largest finite
+    assert float(v[0x01]) == 2.0 ** -16                 # smallest subnormal
+    assert float(v[0x04]) == 2.0 ** -14                 # smallest normal
+    pos = v[:0x7C]
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(v[0x80:0xFC], -v[0x00:0x7C])
+
+
+@pytest.mark.parametrize("exp_field", list(range(127 - 18, 127 + 17)))
+def test_e5m2_encode_matches_torch_exhaustive_binade(orc, exp_field):
+    """Every binary32 in the binades that reach e5m2 (2^-18 .. 2^16), both signs."""
+    for sign in (0, 1):
+        v = _fp32_patterns(exp_field, sign)
+        assert np.array_equal(orc.e5m2_encode(v), _torch_e5m2(v))
+
+
+def test_e5m2_encode_random_and_saturation(orc):
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 2**32, 2_000_000, dtype=np.uint64).astype(np.uint32)
+    v = bits.view(np.float32)
+    v = v[np.isfinite(v)]
+    assert np.array_equal(orc.e5m2_encode(v), _torch_e5m2(v))
+    big = np.array([57344.0, 61439.0, 61440.0, 1e30, -1e30, np.float32(3.4e38)], np.float32)
+    assert orc.e5m2_encode(big).tolist() == [0x7B, 0x7B, 0x7B, 0x7B, 0xFB, 0x7B]  # saturates, never inf
+    assert orc.e5m2_encode(np.array([0.0, -0.0, 2.0 ** -17, -(2.0 ** -17)], np.float32)).tolist() == \
+        [0x00, 0x80, 0x00, 0x80]  # the tie at half the smallest subnormal goes to even (zero)
+
+
+def test_e5m2_encode_nearest_by_search(orc):
+    """Against a brute-force nearest search on values straddling every
+    e5m2 midpoint."""
+    mags = orc.e5m2_decode(np.arange(0x7C, dtype=np.uint8)).astype(np.float64)
+    mids = (mags[:-1] + mags[1:]) / 2
+    v = np.concatenate([mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+                        np.nextafter(mids.astype(np.float32), np.float32(0)), mags]).astype(np.float32)
+    want = _nearest_by_search(v, mags)
+    assert np.array_equal(orc.e5m2_encode(v).astype(np.int64) & 0x7F, want)
 
 
 def test_e2m1_decode_table(orc):

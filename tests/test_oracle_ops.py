@@ -38,15 +38,25 @@ def torch_e4m3(v) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+def torch_e5m2(v) -> np.ndarray:
+    t = torch.from_numpy(np.clip(np.asarray(v, np.float32), -57344, 57344))
+    return t.to(torch.float8_e5m2).view(torch.uint8).numpy()
+
+
+FMAX = {"e4m3": 448.0, "e5m2": 57344.0}
+TOP = {"e4m3": 0x7E, "e5m2": 0x7B}
+CAST = {"e4m3": torch_e4m3, "e5m2": torch_e5m2}
+
+
 def e4m3_value(codes) -> np.ndarray:
     return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).float().numpy()
 
 
-def robust_codes(q64: np.ndarray):
-    """e4m3 code of a binary64 quotient, and whether it is unambiguous: the
+def robust_codes(q64: np.ndarray, fmt: str = "e4m3"):
+    """FP8 code of a binary64 quotient, and whether it is unambiguous: the
     code is the same at q*(1-DELTA) and q*(1+DELTA)."""
-    lo = torch_e4m3((q64 * (1 - DELTA)).astype(np.float32))
-    hi = torch_e4m3((q64 * (1 + DELTA)).astype(np.float32))
+    lo = CAST[fmt]((q64 * (1 - DELTA)).astype(np.float32))
+    hi = CAST[fmt]((q64 * (1 + DELTA)).astype(np.float32))
     return hi, lo == hi
 
 
@@ -144,30 +154,33 @@ def test_rmsnorm_fp8_constant_row_and_zero_row(orc):
     assert o["scale"][2] == 0.0 and np.all(o["q"][2] == 0)
 
 
-def test_per_token_quant_divides_per_element(orc):
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_per_token_quant_divides_per_element(orc, fmt):
     """Per-token FP8 keeps one division per element ([GRP] "Details": per-token
     FP8 keeps exact per-element division).  Rows are built from fp32 values
-    for which RN(y/s) and RN(y * RN(1/s)) fall on different sides of an e4m3
-    rounding boundary; the oracle must give the division's code."""
+    for which RN(y/s) and RN(y * RN(1/s)) fall on different sides of an FP8
+    rounding boundary; the oracle must give the division's code.  The same
+    row step serves the RMSNorm and the dynamic LayerNorm ops."""
     rng = np.random.default_rng(11)
+    fmax = np.float32(FMAX[fmt])
     found = []
     while len(found) < 8:
         amax = np.float32(rng.uniform(1.0, 2.0))
-        s = amax / np.float32(448.0)
+        s = amax / fmax
         inv = np.float32(1.0) / s
         y = rng.uniform(-amax, amax, 200_000).astype(np.float32)
-        qd = torch_e4m3(y / s)
-        qm = torch_e4m3(y * inv)
+        qd = CAST[fmt](y / s)
+        qm = CAST[fmt](y * inv)
         bad = np.nonzero(qd != qm)[0]
         if bad.size:
             found.append((amax, y[bad[:16]]))
     for amax, ys in found:
         row = np.concatenate([[amax], ys]).astype(np.float32)[None, :]
-        o = orc.quant_fp8_rows(row)
-        s = amax / np.float32(448.0)
+        o = orc.quant_fp8_rows(row, fmt=fmt)
+        s = amax / fmax
         assert o["scale"][0] == s
-        assert np.array_equal(o["q"][0], torch_e4m3(row[0] / s))
-        assert not np.array_equal(o["q"][0], torch_e4m3(row[0] * (np.float32(1.0) / s)))
+        assert np.array_equal(o["q"][0], CAST[fmt](row[0] / s))
+        assert not np.array_equal(o["q"][0], CAST[fmt](row[0] * (np.float32(1.0) / s)))
 
 
 def test_rmsnorm_fp8_norm_out_is_bf16_of_y(orc):
@@ -244,6 +257,118 @@ def test_layernorm_constant_row_gives_beta(orc):
     assert np.array_equal(o["y"][0], b)
     inv = np.float32(1) / np.float32(0.05)
     assert np.array_equal(o["q"][0], torch_e4m3(b * inv))
+
+
+# ------------------------------------------- e5m2 outputs, dynamic LN ------
+
+def ref64_ln(x_bits, gamma, beta, eps):
+    """Independent binary64 LayerNorm (population variance)."""
+    x = W.bf16_bits_to_f32(x_bits).astype(np.float64)
+    mu = x.mean(axis=1, keepdims=True)
+    c = x - mu
+    rstd = 1.0 / np.sqrt((c * c).mean(axis=1, keepdims=True) + eps)
+    return c * rstd * gamma.astype(np.float64) + beta.astype(np.float64)
+
+
+def test_rmsnorm_fp8_e5m2_matches_binary64_and_static(orc):
+    """e5m2 output ("feat: fused FP8 quantization output for LayerNorm",
+    "Description": the FP8 output may be e4m3 or e5m2): dynamic scale =
+    amax/57344, codes = E5(y/s); static codes = E5(y * RN(1/scale))."""
+    w = W.rms_2816(M=64)
+    o = orc.fused_add_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], w["eps"], want_y=True, fmt="e5m2")
+    _, y64 = ref64_rms(w["x"], w["residual"], w["gamma"], w["eps"], 2816)
+    s64 = np.abs(y64).max(axis=1) / 57344.0
+    assert np.max(np.abs(o["scale"] - s64) / s64) < 1e-6
+    amax = np.abs(o["y"]).max(axis=1).astype(np.float32)
+    assert np.array_equal(o["scale"], (amax / np.float32(57344.0)).astype(np.float32))
+    codes, ok = robust_codes(y64 / s64[:, None], "e5m2")
+    assert ok.mean() > 0.999 and np.all(same_value(o["q"][ok], codes[ok]))
+    top = o["q"][np.arange(64), np.abs(o["y"]).argmax(axis=1)]
+    assert np.all((top & 0x7F) == 0x7B)
+    # e5m2 is coarser than e4m3: more codes per row land on zero or saturate less
+    o4 = orc.fused_add_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], w["eps"])
+    assert not np.array_equal(o["q"], o4["q"])
+    st = orc.fused_add_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], w["eps"], static_scale=0.05,
+                                         want_y=True, fmt="e5m2")
+    inv = np.float32(1) / np.float32(0.05)
+    assert np.array_equal(st["q"], torch_e5m2(st["y"] * inv))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_layernorm_dynamic_matches_binary64(orc, fmt):
+    """LayerNorm with a per-token dynamic scale (the library path [LNQ]
+    "Description" says exists but is left unconnected): s = amax(y)/fmax,
+    codes = E(y/s) against a binary64 recomputation; the absmax element codes
+    to the format's largest finite value."""
+    w = W.layernorm_rows(M=96, d=1024, seed=4)
+    o = orc.layernorm_quant_fp8(w["x"], w["gamma"], w["beta"], w["eps"], None, want_y=True, fmt=fmt)
+    y64 = ref64_ln(w["x"], w["gamma"], w["beta"], w["eps"])  # y itself: pinned by the static op's test
+    s64 = np.abs(y64).max(axis=1) / FMAX[fmt]
+    assert np.max(np.abs(o["scale"] - s64) / s64) < 1e-6
+    amax = np.abs(o["y"]).max(axis=1).astype(np.float32)
+    assert np.array_equal(o["scale"], (amax / np.float32(FMAX[fmt])).astype(np.float32))
+    codes, ok = robust_codes(y64 / s64[:, None], fmt)
+    assert ok.mean() > 0.999 and np.all(same_value(o["q"][ok], codes[ok]))
+    top = o["q"][np.arange(96), np.abs(o["y"]).argmax(axis=1)]
+    assert np.all((top & 0x7F) == TOP[fmt])
+    # the per-element quotient is a division (not a reciprocal multiply)
+    assert np.array_equal(o["q"], CAST[fmt](o["y"] / o["scale"][:, None]))
+    # the y is the static op's y
+    st = orc.layernorm_quant_fp8(w["x"], w["gamma"], w["beta"], w["eps"], 0.05, want_y=True, fmt=fmt)
+    assert np.array_equal(st["y"], o["y"])
+    assert st["scale"] is None
+
+
+def test_layernorm_dynamic_constant_and_zero_rows(orc):
+    """A constant row has c = 0, so y = beta exactly and s = max|beta|/448;
+    with beta = 0 too the row is all zero: scale 0 and zero codes."""
+    d = 512
+    rng = np.random.default_rng(2)
+    x = W.to_bf16_bits(np.full((2, d), 3.25, np.float32))
+    gamma = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(d)).astype(np.float32)
+    o = orc.layernorm_quant_fp8(x, gamma, beta, 1e-5, None, want_y=True)
+    assert np.array_equal(o["y"][0], beta)
+    assert o["scale"][0] == np.float32(np.abs(beta).max()) / np.float32(448)
+    z = orc.layernorm_quant_fp8(x, gamma, np.zeros(d, np.float32), 1e-5, None)
+    assert np.all(z["scale"] == 0) and np.all(z["q"] == 0)
+
+
+def test_layernorm_static_e5m2(orc):
+    """[LNQ] "Tests": e5m2 at scales 0.01 / 1 / 10: codes = E5(y * RN(1/scale))."""
+    w = W.layernorm_rows(M=16, d=4096, seed=1)
+    for scale in (0.01, 1.0, 10.0):
+        o = orc.layernorm_quant_fp8(w["x"], w["gamma"], w["beta"], w["eps"], scale, want_y=True, fmt="e5m2")
+        inv = np.float32(1) / np.float32(scale)
+        assert np.array_equal(o["q"], torch_e5m2(o["y"] * inv))
+        y64 = ref64_ln(w["x"], w["gamma"], w["beta"], w["eps"])
+        codes, ok = robust_codes(y64 / scale, "e5m2")
+        assert ok.mean() > 0.999 and np.all(same_value(o["q"][ok], codes[ok]))
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_group_e5m2(orc, ue8m0):
+    """Group quant with e5m2 output: s = amax/57344 (UE8M0: the next power of
+    two), codes = E5(x * RN(1/s)); the fused RMSNorm + group op in
+    bf16-sourced mode equals norm_out fed to it."""
+    w = W.group_t3(M=256)
+    o = orc.per_token_group_quant_fp8(w["x"], 128, ue8m0=ue8m0, fmt="e5m2")
+    x = W.bf16_bits_to_f32(w["x"]).reshape(256, 32, 128)
+    amax = np.abs(x).max(axis=2).astype(np.float32)
+    t = (amax / np.float32(57344)).astype(np.float32)
+    if ue8m0:
+        s = o["scale"].astype(np.float64)
+        assert np.all(np.frexp(s)[0] == 0.5)
+        assert np.all(amax / s <= 57344.0) and np.all(amax / (s / 2) > 57344.0 * (1 - 2.0 ** -23))
+    else:
+        assert np.array_equal(o["scale"], t)
+    inv = (np.float32(1) / o["scale"]).astype(np.float32)[:, :, None]
+    assert np.array_equal(o["q"].reshape(x.shape), torch_e5m2(x * inv).reshape(x.shape))
+    wf = W.rms_group_7168(M=8)
+    f = orc.fused_add_rmsnorm_quant_fp8_group(wf["x"], wf["residual"], wf["gamma"], wf["eps"], ue8m0=ue8m0,
+                                              bf16_source=True, want_norm_out=True, fmt="e5m2")
+    u = orc.per_token_group_quant_fp8(f["norm_out"], 128, ue8m0=ue8m0, fmt="e5m2")
+    assert np.array_equal(f["q"], u["q"]) and np.array_equal(f["scale"], u["scale"])
 
 
 # --------------------------------------------------- O4 group quant --------
