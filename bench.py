@@ -92,7 +92,7 @@ def _sets_for(nbytes, cap=8):
 
 
 class RmsFp8Case(Case):
-    def __init__(self, torch, nq, M, d, seed=0, static=False, sets=None):
+    def __init__(self, torch, nq, M, d, seed=0, static=False, sets=None, e5m2=False):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.rms_2816(M, seed) if d == 2816 else W.rms_small(seed, M)
         rd, wr = traffic.fused_add_rmsnorm_fp8(M, d, residual=True, static=static)
@@ -101,17 +101,20 @@ class RmsFp8Case(Case):
         r = torch.from_numpy(w["residual"]).view(torch.bfloat16).cuda()
         self.g = torch.from_numpy(w["gamma"]).cuda()
         self.ss = torch.tensor([0.05], dtype=torch.float32, device="cuda") if static else None
-        self.fn = nq.library().nq_fused_add_rmsnorm_quant_fp8
+        lib = nq.library()
+        self.fn = lib.nq_fused_add_rmsnorm_quant_fp8_ex if e5m2 else lib.nq_fused_add_rmsnorm_quant_fp8
         self.bufs, self.args = [], []
         for _ in range(sets or _sets_for(self.bytes)):
             b = dict(x=x.clone(), r=r.clone(), ro=torch.empty_like(r),
                      q=torch.empty(M, d, dtype=torch.uint8, device="cuda"),
                      s=torch.empty(M, dtype=torch.float32, device="cuda"))
             self.bufs.append(b)
-            self.args.append((b["x"].data_ptr(), d, b["r"].data_ptr(), d, b["ro"].data_ptr(), d,
-                              self.g.data_ptr(), w["eps"], None if self.ss is None else self.ss.data_ptr(),
-                              b["q"].data_ptr(), d, None if static else b["s"].data_ptr(), None, 0, M, d))
-        self.label = f"fused add+RMSNorm+per-token FP8 (e4m3), M={M}, d={d}" + (", static scale" if static else "")
+            ss = None if self.ss is None else self.ss.data_ptr()
+            head = (b["x"].data_ptr(), d, b["r"].data_ptr(), d, b["ro"].data_ptr(), d, self.g.data_ptr(), w["eps"], ss)
+            tail = (b["q"].data_ptr(), d, None if static else b["s"].data_ptr(), None, 0, M, d)
+            self.args.append(head + ((nq.NQ_FLAG_E5M2,) if e5m2 else ()) + tail)
+        self.label = (f"fused add+RMSNorm+per-token FP8 ({'e5m2' if e5m2 else 'e4m3'}), M={M}, d={d}"
+                      + (", static scale" if static else ""))
 
 
 class GroupCase(Case):
@@ -132,22 +135,32 @@ class GroupCase(Case):
 
 
 class LayerNormCase(Case):
-    def __init__(self, torch, nq, M=16384, d=4096):
+    def __init__(self, torch, nq, M=16384, d=4096, dynamic=False, e5m2=False):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.layernorm_rows(M, d)
-        self.bytes = traffic.total(traffic.layernorm_fp8(M, d))
+        self.bytes = traffic.total(traffic.layernorm_fp8(M, d, dynamic=dynamic))
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         self.g = torch.from_numpy(w["gamma"]).cuda()
         self.b = torch.from_numpy(w["beta"]).cuda()
         self.sc = torch.tensor([w["scale"]], dtype=torch.float32, device="cuda")
-        self.fn = nq.library().nq_layernorm_quant_fp8
+        ex = dynamic or e5m2
+        self.fn = nq.library().nq_layernorm_quant_fp8_ex if ex else nq.library().nq_layernorm_quant_fp8
+        flags = nq.NQ_FLAG_E5M2 if e5m2 else 0
         self.bufs, self.args = [], []
         for _ in range(_sets_for(self.bytes)):
-            b = dict(x=x.clone(), q=torch.empty(M, d, dtype=torch.uint8, device="cuda"))
+            b = dict(x=x.clone(), q=torch.empty(M, d, dtype=torch.uint8, device="cuda"),
+                     s=torch.empty(M, dtype=torch.float32, device="cuda"))
             self.bufs.append(b)
-            self.args.append((b["x"].data_ptr(), d, self.g.data_ptr(), self.b.data_ptr(), w["eps"],
-                              self.sc.data_ptr(), b["q"].data_ptr(), d, M, d))
-        self.label = f"LayerNorm + static FP8 (scale tensor 0.05), M={M}, d={d}"
+            sc = None if dynamic else self.sc.data_ptr()
+            if ex:
+                self.args.append((b["x"].data_ptr(), d, self.g.data_ptr(), self.b.data_ptr(), w["eps"], sc, flags,
+                                  b["q"].data_ptr(), d, b["s"].data_ptr() if dynamic else None, M, d))
+            else:
+                self.args.append((b["x"].data_ptr(), d, self.g.data_ptr(), self.b.data_ptr(), w["eps"],
+                                  sc, b["q"].data_ptr(), d, M, d))
+        fmt = "e5m2" if e5m2 else "e4m3"
+        self.label = (f"LayerNorm + dynamic per-token FP8 ({fmt}), M={M}, d={d}" if dynamic
+                      else f"LayerNorm + static FP8 ({fmt}, scale tensor 0.05), M={M}, d={d}")
 
 
 class Nvfp4Case(Case):
@@ -466,6 +479,7 @@ def run_suite(torch, nq):
         ("rms_2816_m256", lambda: RmsFp8Case(torch, nq, 256, 2816)),
         ("rms_2816_m8192", lambda: RmsFp8Case(torch, nq, 8192, 2816)),
         ("rms_2816_m8192_static", lambda: RmsFp8Case(torch, nq, 8192, 2816, static=True)),
+        ("rms_2816_m8192_e5m2", lambda: RmsFp8Case(torch, nq, 8192, 2816, e5m2=True)),
         ("group_m32768_fp32", lambda: GroupCase(torch, nq, 32768)),
         ("group_m32768_ue8m0", lambda: GroupCase(torch, nq, 32768, ue8m0=True)),
         ("group_m1", lambda: GroupCase(torch, nq, 1)),
@@ -474,6 +488,9 @@ def run_suite(torch, nq):
         ("rms_group_7168_m8192_ue8m0", lambda: RmsGroupCase(torch, nq, 8192, ue8m0=True)),
         ("rms_group_2816_m8192", lambda: RmsGroupCase(torch, nq, 8192, d=2816)),
         ("layernorm_m16384", lambda: LayerNormCase(torch, nq)),
+        ("layernorm_m16384_e5m2", lambda: LayerNormCase(torch, nq, e5m2=True)),
+        ("layernorm_dynamic_m16384", lambda: LayerNormCase(torch, nq, dynamic=True)),
+        ("layernorm_dynamic_m1", lambda: LayerNormCase(torch, nq, M=1, dynamic=True)),
         ("nvfp4_7168_m1", lambda: Nvfp4Case(torch, nq, 1)),
         ("nvfp4_7168_m64", lambda: Nvfp4Case(torch, nq, 64)),
         ("nvfp4_7168_m8192", lambda: Nvfp4Case(torch, nq, 8192)),

@@ -57,6 +57,45 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
     return (uint32_t)w;
 }
 
+// ------------------------------------------------------------ e5m2 -------
+// e5m2(v): clamp to [-57344, 57344] (saturating like e4m3, so a scaled value
+// never becomes infinite), then the native round-to-nearest-even conversion
+// (v_cvt_pk_bf8_f32).  Four values -> one dword, value 0 in byte 0.
+constexpr float kE5M2Max = 57344.0f;  // largest finite OCP e5m2 value
+
+__device__ __forceinline__ float clamp_e5m2(float v)
+{
+    return __builtin_amdgcn_fmed3f(v, -kE5M2Max, kE5M2Max);
+}
+
+__device__ __forceinline__ uint32_t e5m2x4(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_bf8_f32(clamp_e5m2(a), clamp_e5m2(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(clamp_e5m2(c), clamp_e5m2(d), w, true);
+    return (uint32_t)w;
+}
+
+// The FP8 output format of a kernel instance, and its largest finite value
+// (the divisor of dynamic scales).
+enum class Fp8 { E4M3, E5M2 };
+
+template <Fp8 F>
+constexpr float fp8_max() { return F == Fp8::E5M2 ? kE5M2Max : kE4M3Max; }
+
+template <Fp8 F>
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d)
+{
+    if constexpr (F == Fp8::E5M2) return e5m2x4(a, b, c, d);
+    else return e4m3x4(a, b, c, d);
+}
+
+// 8 values -> two dwords
+template <Fp8 F>
+__device__ __forceinline__ uint2 fp8x8(const float v[8])
+{
+    return make_uint2(fp8x4<F>(v[0], v[1], v[2], v[3]), fp8x4<F>(v[4], v[5], v[6], v[7]));
+}
+
 // Decode of an e4m3 code (used for the NVFP4 block scale): sign, 4-bit
 // exponent with bias 7, 3-bit mantissa, subnormals at exponent 0.  Codes
 // reaching here come from e4m3x4 of a non-negative clamped value, so never

@@ -32,7 +32,7 @@ constexpr int kGroup = 128;
 constexpr int kGroupBlock = 256;   // 16 groups per block per step
 constexpr int kGroupUnroll = 4;
 
-template <bool VEC, bool UE8M0>
+template <bool VEC, bool UE8M0, Fp8 F>
 __global__ __launch_bounds__(kGroupBlock) void k_group_fp8(GroupArgs a)
 {
     const int lane16 = threadIdx.x & 15;
@@ -70,11 +70,12 @@ __global__ __launch_bounds__(kGroupBlock) void k_group_fp8(GroupArgs a)
 #pragma unroll
         for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[k]));
         amax = max16_dpp(amax);
-        float s = amax / kE4M3Max;
+        float s = amax / fp8_max<F>();
         if constexpr (UE8M0) s = pow2_ceil(s);
         const float inv = s > 0.0f ? 1.0f / s : 0.0f;
-        const uint2 q = make_uint2(e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv),
-                                   e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = v[k] * inv;
+        const uint2 q = fp8x8<F>(v);
         if (ok[u]) {
             uint8_t* pq = a.q + qoff[u];
             if constexpr (VEC) {
@@ -89,23 +90,25 @@ __global__ __launch_bounds__(kGroupBlock) void k_group_fp8(GroupArgs a)
 }
 
 template <bool VEC, bool UE8M0>
-static void launch_group(const GroupArgs& a, hipStream_t s)
+static void launch_group(const GroupArgs& a, bool e5m2, hipStream_t s)
 {
     const uint32_t per_block = (kGroupBlock / 16) * kGroupUnroll;
     const uint32_t blocks = (a.total + per_block - 1) / per_block;
-    hipLaunchKernelGGL((k_group_fp8<VEC, UE8M0>), dim3(blocks), dim3(kGroupBlock), 0, s, a);
+    if (e5m2) hipLaunchKernelGGL((k_group_fp8<VEC, UE8M0, Fp8::E5M2>), dim3(blocks), dim3(kGroupBlock), 0, s, a);
+    else hipLaunchKernelGGL((k_group_fp8<VEC, UE8M0, Fp8::E4M3>), dim3(blocks), dim3(kGroupBlock), 0, s, a);
 }
 
 } // namespace nq
 
 using namespace nq;
 
-extern "C" nq_status nq_per_token_group_quant_fp8(
+extern "C" nq_status nq_per_token_group_quant_fp8_ex(
     const uint16_t* x, int64_t ld_x, int64_t M, int64_t K,
-    int32_t group_size, int32_t scale_mode,
+    int32_t group_size, int32_t scale_mode, uint32_t flags,
     uint8_t* q_out, int64_t ld_q, float* scale_out, void* stream)
 {
     if (group_size != kGroup) return NQ_ERR_ARG;
+    if ((flags & ~(uint32_t)NQ_FLAG_E5M2) != 0) return NQ_ERR_ARG;
     if (scale_mode != NQ_SCALE_FP32 && scale_mode != NQ_SCALE_UE8M0) return NQ_ERR_ARG;
     if (M < 0 || K <= 0 || K % group_size != 0 || M > kMaxRows) return NQ_ERR_SHAPE;
     if (bad_ld(ld_x, K) || bad_ld(ld_q, K)) return NQ_ERR_STRIDE;
@@ -125,7 +128,17 @@ extern "C" nq_status nq_per_token_group_quant_fp8(
     a.total = (uint32_t)(M * G);
     hipStream_t s = (hipStream_t)stream;
     const bool ue = scale_mode == NQ_SCALE_UE8M0;
-    if (vec) ue ? launch_group<true, true>(a, s) : launch_group<true, false>(a, s);
-    else     ue ? launch_group<false, true>(a, s) : launch_group<false, false>(a, s);
+    const bool e5 = (flags & NQ_FLAG_E5M2) != 0;
+    if (vec) ue ? launch_group<true, true>(a, e5, s) : launch_group<true, false>(a, e5, s);
+    else     ue ? launch_group<false, true>(a, e5, s) : launch_group<false, false>(a, e5, s);
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
+}
+
+extern "C" nq_status nq_per_token_group_quant_fp8(
+    const uint16_t* x, int64_t ld_x, int64_t M, int64_t K,
+    int32_t group_size, int32_t scale_mode,
+    uint8_t* q_out, int64_t ld_q, float* scale_out, void* stream)
+{
+    return nq_per_token_group_quant_fp8_ex(x, ld_x, M, K, group_size, scale_mode, 0u, q_out, ld_q, scale_out,
+                                           stream);
 }

@@ -1,4 +1,5 @@
-// nq_layernorm_fp8.hip -- LayerNorm + static per-tensor FP8 e4m3 for gfx950.
+// nq_layernorm_fp8.hip -- LayerNorm + FP8 (e4m3 or e5m2) with a static
+// per-tensor or a dynamic per-token scale, for gfx950.
 //
 // Pages: [LNQ] "feat: fused FP8 quantization output for LayerNorm"
 // ("Description": the quantization scale divides, out = normed / scale; the
@@ -21,20 +22,24 @@ struct LnFp8Args {
     const uint16_t* x;
     const float* gamma;
     const float* beta;
-    const float* scale;
+    const float* scale;     // static per-tensor scale, or NULL: dynamic per-token
     uint8_t* q;
+    float* scale_out;       // [M] per-token scales (dynamic only)
     int64_t ld_x, ld_q;
     int64_t M;
     int d;
     float eps;
+    bool e5m2;              // output format (e4m3 otherwise)
 };
 
-template <int TEAM, int CPL, bool VEC, bool STAGE, int BLOCK = row_block<TEAM, CPL, 2, VEC, STAGE>()>
+template <int TEAM, int CPL, bool VEC, bool STAGE, Fp8 F = Fp8::E4M3, bool DYN = false,
+          int BLOCK = row_block<TEAM, CPL, 2, VEC, STAGE>()>
 __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
 {
     using S = TeamShape<TEAM, BLOCK>;
     __shared__ double lds_mean[S::kWaves];
     __shared__ double lds_var[S::kWaves];
+    __shared__ float lds_max[S::kWaves];
 
     const int t = threadIdx.x % TEAM;
     const RowMap m = row_map<TEAM, BLOCK>(a.M);
@@ -44,6 +49,8 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
     __shared__ typename SV::Lds lds_gb;
     SV gb({a.gamma, a.beta}, d);
     const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d);
+    float scale = 1.0f;
+    if constexpr (!DYN) scale = a.scale[0];  // issued early: read on the device at run time
 
     uint4 xw[CPL];
 #pragma unroll
@@ -89,24 +96,59 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
     acc2 = team_sum<TEAM>(acc2, lds_var);
     const float var = (float)(acc2 / (double)d);
     const float rstd = 1.0f / sqrtf(var + a.eps);
-    const float inv = 1.0f / a.scale[0];
     __builtin_amdgcn_sched_barrier(0);
 
-    // y = ((c * rstd) * gamma) + beta; q = e4m3(y * (1 / scale)).
+    if constexpr (!DYN) {
+        // Static: y = ((c * rstd) * gamma) + beta; q = fp8(y * (1 / scale)),
+        // each chunk stored as it is produced.
+        const float inv = 1.0f / scale;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int e = (j * TEAM + t1) * 8;
-        float g[8], b[8], v[8];
-        gb.chunk(lds_gb, 0, e, g);
-        gb.chunk(lds_gb, 1, e, b);
+        for (int j = 0; j < CPL; ++j) {
+            const int e = (j * TEAM + t1) * 8;
+            float g[8], b[8], v[8];
+            gb.chunk(lds_gb, 0, e, g);
+            gb.chunk(lds_gb, 1, e, b);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float n = c[j][k] * rstd;
-            const float gn = n * g[k];
-            const float y = gn + b[k];
-            v[k] = y * inv;
+            for (int k = 0; k < 8; ++k) {
+                const float n = c[j][k] * rstd;
+                const float gn = n * g[k];
+                const float y = gn + b[k];
+                v[k] = y * inv;
+            }
+            qio.store8(e, e < d, fp8x8<F>(v));
         }
-        qio.store8(e, e < d, make_uint2(e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])));
+    } else {
+        // Dynamic per-token: y replaces c in the registers, its absolute
+        // maximum is reduced over the team (past the row end gamma and beta
+        // are zero, so y is too), s = amax / fmax, q = fp8(y / s) with one
+        // correctly rounded quotient per element (div_by).
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int e = (j * TEAM + t1) * 8;
+            float g[8], b[8];
+            gb.chunk(lds_gb, 0, e, g);
+            gb.chunk(lds_gb, 1, e, b);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float n = c[j][k] * rstd;
+                const float gn = n * g[k];
+                c[j][k] = gn + b[k];
+                amax = fmaxf(amax, fabsf(c[j][k]));
+            }
+        }
+        amax = team_max<TEAM>(amax, lds_max);
+        const float s = amax / fp8_max<F>();
+        if (t == 0 && m.ok) a.scale_out[m.row] = s;
+        const float inv = s > 0.0f ? 1.0f / s : 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int e = (j * TEAM + t1) * 8;
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = div_by(c[j][k], s, inv);
+            qio.store8(e, e < d, fp8x8<F>(v));
+        }
     }
 }
 
@@ -117,7 +159,14 @@ struct LnFp8Kernel {
     template <bool STAGE>
     static void launch(const LnFp8Args& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE>), grid, block, 0, s, a);
+        const bool dyn = a.scale == nullptr;
+        if (a.e5m2) {
+            if (dyn) hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2, false>), grid, block, 0, s, a);
+        } else {
+            if (dyn) hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3, false>), grid, block, 0, s, a);
+        }
     }
 };
 
@@ -125,22 +174,25 @@ struct LnFp8Kernel {
 
 using namespace nq;
 
-extern "C" nq_status nq_layernorm_quant_fp8(
+extern "C" nq_status nq_layernorm_quant_fp8_ex(
     const uint16_t* x, int64_t ld_x,
     const float* gamma, const float* beta, float eps,
-    const float* scale,
+    const float* scale, uint32_t flags,
     uint8_t* q_out, int64_t ld_q,
+    float* scale_out,
     int64_t M, int64_t d, void* stream)
 {
+    if ((flags & ~(uint32_t)NQ_FLAG_E5M2) != 0) return NQ_ERR_ARG;
     if (M < 0 || d <= 0 || d > NQ_MAX_D || M > kMaxRows) return NQ_ERR_SHAPE;
     if (!(eps >= 0.0f) || eps > 1e30f) return NQ_ERR_ARG;
     if (bad_ld(ld_x, d) || bad_ld(ld_q, d)) return NQ_ERR_STRIDE;
     if (M == 0) return NQ_OK;  // empty tensors may carry NULL data pointers
-    if (!x || !gamma || !beta || !scale || !q_out) return NQ_ERR_NULL;
+    if (!x || !gamma || !beta || !q_out) return NQ_ERR_NULL;
+    if (!scale && !scale_out) return NQ_ERR_NULL;  // dynamic scales need somewhere to go
 
     const Region in[] = {region(x, M, ld_x, d, 2), region(gamma, 1, d, d, 4),
                          region(beta, 1, d, d, 4), region(scale, 1, 1, 1, 4)};
-    const Region out[] = {region(q_out, M, ld_q, d, 1)};
+    const Region out[] = {region(q_out, M, ld_q, d, 1), region(scale ? nullptr : scale_out, 1, M, M, 4)};
     if (any_alias(in, out)) return NQ_ERR_ALIAS;
 
     const bool vec = d % 8 == 0 && aligned(x, 16) && ld_x % 8 == 0 && aligned(gamma, 16) &&
@@ -150,7 +202,20 @@ extern "C" nq_status nq_layernorm_quant_fp8(
 
     LnFp8Args a;
     a.x = x; a.gamma = gamma; a.beta = beta; a.scale = scale; a.q = q_out;
+    a.scale_out = scale ? nullptr : scale_out;
     a.ld_x = ld_x; a.ld_q = ld_q; a.M = M; a.d = (int)d; a.eps = eps;
+    a.e5m2 = (flags & NQ_FLAG_E5M2) != 0;
     if (!launch_row_shape<LnFp8Kernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
+}
+
+extern "C" nq_status nq_layernorm_quant_fp8(
+    const uint16_t* x, int64_t ld_x,
+    const float* gamma, const float* beta, float eps,
+    const float* scale,
+    uint8_t* q_out, int64_t ld_q,
+    int64_t M, int64_t d, void* stream)
+{
+    if (M > 0 && !scale) return NQ_ERR_NULL;  // this form is static-scale only
+    return nq_layernorm_quant_fp8_ex(x, ld_x, gamma, beta, eps, scale, 0u, q_out, ld_q, nullptr, M, d, stream);
 }

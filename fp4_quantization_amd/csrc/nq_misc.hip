@@ -17,8 +17,9 @@ __global__ __launch_bounds__(256) void k_diag_codec(int kind, const float* in, v
     float v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = i0 + k < n ? in[i0 + k] : 0.0f;
-    if (kind == NQ_CODEC_E4M3) {
-        const uint32_t w[2] = {e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])};
+    if (kind == NQ_CODEC_E4M3 || kind == NQ_CODEC_E5M2) {
+        const uint2 w2 = kind == NQ_CODEC_E4M3 ? fp8x8<Fp8::E4M3>(v) : fp8x8<Fp8::E5M2>(v);
+        const uint32_t w[2] = {w2.x, w2.y};
         uint8_t* o = (uint8_t*)out;
 #pragma unroll
         for (int k = 0; k < 8; ++k)
@@ -69,7 +70,8 @@ extern "C" const char* nq_version(void) { return "nq 0.1.0 gfx950"; }
 
 extern "C" nq_status nq_diag_codec(int32_t kind, const float* in, void* out, int64_t n, void* stream)
 {
-    if (kind != NQ_CODEC_E4M3 && kind != NQ_CODEC_E2M1 && kind != NQ_CODEC_BF16) return NQ_ERR_ARG;
+    if (kind != NQ_CODEC_E4M3 && kind != NQ_CODEC_E2M1 && kind != NQ_CODEC_BF16 && kind != NQ_CODEC_E5M2)
+        return NQ_ERR_ARG;
     if (n < 0 || n > (int64_t(1) << 40)) return NQ_ERR_SHAPE;
     if (n == 0) return NQ_OK;
     if (!in || !out) return NQ_ERR_NULL;

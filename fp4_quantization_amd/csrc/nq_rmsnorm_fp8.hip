@@ -38,9 +38,11 @@ struct RmsFp8Args {
     int64_t M;
     int d;
     float eps;
+    bool e5m2;              // output format (e4m3 otherwise)
 };
 
-template <int TEAM, int CPL, bool VEC, bool STAGE, int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
+template <int TEAM, int CPL, bool VEC, bool STAGE, Fp8 F = Fp8::E4M3,
+          int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
 __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
 {
     using S = TeamShape<TEAM, BLOCK>;
@@ -88,12 +90,12 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
 
     // Static: out = y / scale, applied as y * (1 / scale[0]); the scale is
     // read on the device so a graph replay sees its current value.
-    // Dynamic (reduction 2): s = amax / 448 and q = e4m3(y / s), one
-    // correctly rounded quotient per element (div_by).
+    // Dynamic (reduction 2): s = amax / 448 (57344 for e5m2) and
+    // q = fp8(y / s), one correctly rounded quotient per element (div_by).
     const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d);
     if (a.static_scale == nullptr) {
         amax = team_max<TEAM>(amax, lds_max);
-        const float s = amax / kE4M3Max;
+        const float s = amax / fp8_max<F>();
         if (t == 0 && m.ok) a.scale_out[m.row] = s;
         const float inv = s > 0.0f ? 1.0f / s : 0.0f;
 #pragma unroll
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
             float v[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) v[k] = div_by(y[j][k], s, inv);
-            qio.store8(e, e < d, make_uint2(e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])));
+            qio.store8(e, e < d, fp8x8<F>(v));
         }
     } else {
         const float inv = 1.0f / a.static_scale[0];
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
             float v[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) v[k] = y[j][k] * inv;
-            qio.store8(e, e < d, make_uint2(e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])));
+            qio.store8(e, e < d, fp8x8<F>(v));
         }
     }
 }
@@ -124,7 +126,8 @@ struct RmsFp8Kernel {
     template <bool STAGE>
     static void launch(const RmsFp8Args& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE>), grid, block, 0, s, a);
+        if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3>), grid, block, 0, s, a);
     }
 };
 
@@ -132,17 +135,18 @@ struct RmsFp8Kernel {
 
 using namespace nq;
 
-extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8(
+extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_ex(
     const uint16_t* x, int64_t ld_x,
     const uint16_t* residual_in, int64_t ld_r,
     uint16_t* residual_out, int64_t ld_ro,
     const float* gamma, float eps,
-    const float* static_scale,
+    const float* static_scale, uint32_t flags,
     uint8_t* q_out, int64_t ld_q,
     float* scale_out,
     uint16_t* norm_out, int64_t ld_n,
     int64_t M, int64_t d, void* stream)
 {
+    if ((flags & ~(uint32_t)NQ_FLAG_E5M2) != 0) return NQ_ERR_ARG;
     if (M < 0 || d <= 0 || d > NQ_MAX_D || M > kMaxRows) return NQ_ERR_SHAPE;
     if (!(eps >= 0.0f) || eps > 1e30f) return NQ_ERR_ARG;
     if (bad_ld(ld_x, d) || bad_ld(ld_q, d)) return NQ_ERR_STRIDE;
@@ -176,6 +180,23 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8(
     a.static_scale = static_scale; a.q = q_out; a.scale_out = scale_out; a.norm_out = norm_out;
     a.ld_x = ld_x; a.ld_r = ld_r; a.ld_ro = ld_ro; a.ld_q = ld_q; a.ld_n = ld_n;
     a.M = M; a.d = (int)d; a.eps = eps;
+    a.e5m2 = (flags & NQ_FLAG_E5M2) != 0;
     if (!launch_row_shape<RmsFp8Kernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
+}
+
+extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8(
+    const uint16_t* x, int64_t ld_x,
+    const uint16_t* residual_in, int64_t ld_r,
+    uint16_t* residual_out, int64_t ld_ro,
+    const float* gamma, float eps,
+    const float* static_scale,
+    uint8_t* q_out, int64_t ld_q,
+    float* scale_out,
+    uint16_t* norm_out, int64_t ld_n,
+    int64_t M, int64_t d, void* stream)
+{
+    return nq_fused_add_rmsnorm_quant_fp8_ex(x, ld_x, residual_in, ld_r, residual_out, ld_ro, gamma, eps,
+                                             static_scale, 0u, q_out, ld_q, scale_out, norm_out, ld_n, M, d,
+                                             stream);
 }

@@ -38,9 +38,11 @@ struct RmsGroupArgs {
     float eps;
     int ue8m0;              // scales rounded up to powers of two
     int bf16_source;        // quantize bf16(y) (the unfused pipeline's values)
+    bool e5m2;              // output format (e4m3 otherwise)
 };
 
-template <int TEAM, int CPL, bool VEC, bool STAGE, int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
+template <int TEAM, int CPL, bool VEC, bool STAGE, Fp8 F = Fp8::E4M3,
+          int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
 __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8_group(RmsGroupArgs a)
 {
     static_assert(TEAM % 16 == 0, "a group is one 16-lane DPP row");
@@ -86,13 +88,13 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8_group(RmsGroupArgs a)
         for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(y[k]));
         // The group's 16 lanes: every lane of the DPP row gets its maximum.
         amax = max16_dpp(amax);
-        float s = amax / kE4M3Max;
+        float s = amax / fp8_max<F>();
         if (a.ue8m0) s = pow2_ceil(s);
         const float inv = s > 0.0f ? 1.0f / s : 0.0f;
         float v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = y[k] * inv;
-        qio.store8(e, e < d, make_uint2(e4m3x4(v[0], v[1], v[2], v[3]), e4m3x4(v[4], v[5], v[6], v[7])));
+        qio.store8(e, e < d, fp8x8<F>(v));
         sio.store4(e / kRowGroup, e < d && (t1 & 15) == 0, __float_as_uint(s));
     }
 }
@@ -104,7 +106,8 @@ struct RmsGroupKernel {
     template <bool STAGE>
     static void launch(const RmsGroupArgs& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE>), grid, block, 0, s, a);
+        if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E5M2>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E4M3>), grid, block, 0, s, a);
     }
 };
 
@@ -125,7 +128,7 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_group(
 {
     if (group_size != kRowGroup) return NQ_ERR_ARG;
     if (scale_mode != NQ_SCALE_FP32 && scale_mode != NQ_SCALE_UE8M0) return NQ_ERR_ARG;
-    if ((flags & ~(uint32_t)NQ_FLAG_BF16_SOURCE) != 0) return NQ_ERR_ARG;
+    if ((flags & ~(uint32_t)(NQ_FLAG_BF16_SOURCE | NQ_FLAG_E5M2)) != 0) return NQ_ERR_ARG;
     if (M < 0 || d <= 0 || d > NQ_MAX_D || d % group_size != 0 || M > kMaxRows) return NQ_ERR_SHAPE;
     if (!(eps >= 0.0f) || eps > 1e30f) return NQ_ERR_ARG;
     const int64_t G = d / group_size;
@@ -159,6 +162,7 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_group(
     a.M = M; a.d = (int)d; a.eps = eps;
     a.ue8m0 = scale_mode == NQ_SCALE_UE8M0;
     a.bf16_source = (flags & NQ_FLAG_BF16_SOURCE) != 0;
+    a.e5m2 = (flags & NQ_FLAG_E5M2) != 0;
     if (!launch_row_shape<RmsGroupKernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
 }

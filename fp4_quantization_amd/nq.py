@@ -37,7 +37,11 @@ _SIGS = {
                                        _vp, _vp, _i64, _i64, _i64, _vp],
     "nq_fused_add_rmsnorm_quant_fp8_group": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _f32, _i32, _i32, _u32,
                                              _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp],
+    "nq_fused_add_rmsnorm_quant_fp8_ex": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _f32, _vp, _u32, _vp, _i64,
+                                          _vp, _vp, _i64, _i64, _i64, _vp],
     "nq_layernorm_quant_fp8": [_vp, _i64, _vp, _vp, _f32, _vp, _vp, _i64, _i64, _i64, _vp],
+    "nq_layernorm_quant_fp8_ex": [_vp, _i64, _vp, _vp, _f32, _vp, _u32, _vp, _i64, _vp, _i64, _i64, _vp],
+    "nq_per_token_group_quant_fp8_ex": [_vp, _i64, _i64, _i64, _i32, _i32, _u32, _vp, _i64, _vp, _vp],
     "nq_per_token_group_quant_fp8": [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _i64, _vp, _vp],
     "nq_rmsnorm_quant_nvfp4": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _f32, _vp, _vp, _i64, _vp, _i64,
                                _vp, _i64, _i64, _i64, _vp],
@@ -58,9 +62,11 @@ NQ_OK = 0
 NQ_SCALE_FP32 = 0
 NQ_SCALE_UE8M0 = 1
 NQ_FLAG_BF16_SOURCE = 1
+NQ_FLAG_E5M2 = 2
 NQ_CODEC_E4M3 = 0
 NQ_CODEC_E2M1 = 1
 NQ_CODEC_BF16 = 2
+NQ_CODEC_E5M2 = 3
 
 
 class NQError(RuntimeError):
@@ -85,7 +91,7 @@ def library() -> ctypes.CDLL:
 # ------------------------------------------------------------ marshalling --
 
 _BF16 = (torch.bfloat16,)
-_CODES8 = (torch.uint8, torch.float8_e4m3fn)
+_CODES8 = (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2)
 
 
 def _stream(stream) -> int:
@@ -175,6 +181,42 @@ def nq_fused_add_rmsnorm_quant_fp8_group(x, residual_in, residual_out, gamma, ep
     _check(st, "nq_fused_add_rmsnorm_quant_fp8_group")
 
 
+def nq_fused_add_rmsnorm_quant_fp8_ex(x, residual_in, residual_out, gamma, eps, static_scale, flags,
+                                      q_out, scale_out, norm_out=None, stream=None):
+    """nq_fused_add_rmsnorm_quant_fp8 with an output-format flag (include/nq.h)."""
+    M, d = x.shape
+    px, ldx = _mat(x, _BF16, "x")
+    pr, ldr = _mat(residual_in, _BF16, "residual_in", d)
+    pro, ldro = _mat(residual_out, _BF16, "residual_out", d)
+    pq, ldq = _mat(q_out, _CODES8, "q_out", d)
+    pn, ldn = _mat(norm_out, _BF16, "norm_out", d)
+    for t, n in ((residual_in, "residual_in"), (residual_out, "residual_out"), (q_out, "q_out"),
+                 (norm_out, "norm_out")):
+        if t is not None and t.size(0) != M:
+            raise ValueError(f"{n}: expected {M} rows")
+    st = _lib.nq_fused_add_rmsnorm_quant_fp8_ex(
+        px, ldx, pr, ldr, pro, ldro, _vec(gamma, torch.float32, "gamma", d), float(eps),
+        _vec(static_scale, torch.float32, "static_scale", 1), int(flags), pq, ldq,
+        _vec(scale_out, torch.float32, "scale_out", M if static_scale is None else None),
+        pn, ldn, M, d, _stream(stream))
+    _check(st, "nq_fused_add_rmsnorm_quant_fp8_ex")
+
+
+def nq_layernorm_quant_fp8_ex(x, gamma, beta, eps, scale, flags, q_out, scale_out=None, stream=None):
+    """LayerNorm + FP8, static (scale given) or dynamic per-token (scale None,
+    scale_out [M] fp32), e4m3 or e5m2 (include/nq.h)."""
+    M, d = x.shape
+    px, ldx = _mat(x, _BF16, "x")
+    pq, ldq = _mat(q_out, _CODES8, "q_out", d)
+    if q_out.size(0) != M:
+        raise ValueError(f"q_out: expected {M} rows")
+    st = _lib.nq_layernorm_quant_fp8_ex(
+        px, ldx, _vec(gamma, torch.float32, "gamma", d), _vec(beta, torch.float32, "beta", d),
+        float(eps), _vec(scale, torch.float32, "scale", 1), int(flags), pq, ldq,
+        _vec(scale_out, torch.float32, "scale_out", M if scale is None else None), M, d, _stream(stream))
+    _check(st, "nq_layernorm_quant_fp8_ex")
+
+
 def nq_layernorm_quant_fp8(x, gamma, beta, eps, scale, q_out, stream=None):
     """LayerNorm + static per-tensor FP8 e4m3 (include/nq.h)."""
     M, d = x.shape
@@ -201,6 +243,21 @@ def nq_per_token_group_quant_fp8(x, q_out, scale_out, group_size=128, scale_mode
         px, ldx, M, K, int(group_size), int(scale_mode), pq, ldq,
         _vec(scale_out, torch.float32, "scale_out", ngroups), _stream(stream))
     _check(st, "nq_per_token_group_quant_fp8")
+
+
+def nq_per_token_group_quant_fp8_ex(x, q_out, scale_out, group_size=128, scale_mode=NQ_SCALE_FP32, flags=0,
+                                    stream=None):
+    """Per-token-group FP8 with an output-format flag (include/nq.h)."""
+    M, K = x.shape
+    px, ldx = _mat(x, _BF16, "x")
+    pq, ldq = _mat(q_out, _CODES8, "q_out", K)
+    if q_out.size(0) != M:
+        raise ValueError(f"q_out: expected {M} rows")
+    ngroups = M * (K // group_size) if group_size > 0 else 0
+    st = _lib.nq_per_token_group_quant_fp8_ex(
+        px, ldx, M, K, int(group_size), int(scale_mode), int(flags), pq, ldq,
+        _vec(scale_out, torch.float32, "scale_out", ngroups), _stream(stream))
+    _check(st, "nq_per_token_group_quant_fp8_ex")
 
 
 def nq_rmsnorm_quant_nvfp4(x, residual_in, residual_out, gamma, eps, global_scale,

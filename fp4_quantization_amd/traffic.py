@@ -30,9 +30,11 @@ def fused_add_rmsnorm_fp8_group(M: int, d: int, residual: bool = True, group: in
     return rd, wr
 
 
-def layernorm_fp8(M: int, d: int):
-    rd = M * 2 * d + 8 * d + 4
-    wr = M * d
+def layernorm_fp8(M: int, d: int, dynamic: bool = False):
+    """Static: the one-element scale is read once; dynamic: a scale per row
+    is written instead."""
+    rd = M * 2 * d + 8 * d + (0 if dynamic else 4)
+    wr = M * (d + (4 if dynamic else 0))
     return rd, wr
 
 

@@ -72,6 +72,8 @@ typedef int nq_status;
 
 /* Option bits of the entry points that take `flags`. */
 #define NQ_FLAG_BF16_SOURCE 1u  /* quantize bf16(y) instead of the fp32 y */
+#define NQ_FLAG_E5M2 2u         /* FP8 codes in OCP e5m2 (largest finite 57344) instead of e4m3:
+                                   dynamic scales divide by 57344, e5m2() clamps to +-57344 */
 
 /*
  * Fused (residual-add +) RMSNorm + per-token FP8 e4m3.
@@ -114,6 +116,23 @@ nq_status nq_fused_add_rmsnorm_quant_fp8(
     int64_t M, int64_t d, void* stream);
 
 /*
+ * The same op with an output-format choice ([LNQ] "Description" and "Tests":
+ * the FP8 output may be e4m3 or e5m2).  flags: 0 or NQ_FLAG_E5M2 (NQ_ERR_ARG
+ * for other bits); every other argument as above.  With NQ_FLAG_E5M2 the
+ * dynamic scale is max_i |y_i| / 57344 and codes are e5m2.
+ */
+nq_status nq_fused_add_rmsnorm_quant_fp8_ex(
+    const uint16_t* x, int64_t ld_x,
+    const uint16_t* residual_in, int64_t ld_r,
+    uint16_t* residual_out, int64_t ld_ro,
+    const float* gamma, float eps,
+    const float* static_scale, uint32_t flags,
+    uint8_t* q_out, int64_t ld_q,
+    float* scale_out,
+    uint16_t* norm_out, int64_t ld_n,
+    int64_t M, int64_t d, void* stream);
+
+/*
  * LayerNorm + static per-tensor FP8 e4m3.
  * Defined by [LNQ] "Description" (the scale divides: out = normed / scale)
  * and the review thread; the scale is a one-element device tensor read when
@@ -139,6 +158,29 @@ nq_status nq_layernorm_quant_fp8(
     int64_t M, int64_t d, void* stream);
 
 /*
+ * LayerNorm + FP8 with a static per-tensor or a dynamic per-token scale, and
+ * an output-format choice.  [LNQ] "Description": the library LayerNorm has a
+ * per-token quantization path besides the per-tensor one, and the FP8
+ * output may be e4m3 or e5m2 ("Tests" cover both).
+ *
+ *   y_i as nq_layernorm_quant_fp8
+ *   scale != NULL (static):  q_i = fp8(y_i * (1 / scale[0])); scale_out unused
+ *   scale == NULL (dynamic): s = max_i |y_i| / fmax -> scale_out[m];
+ *                            q_i = fp8(y_i / s)  (one correctly rounded
+ *                            quotient per element; 0 when s == 0)
+ *   fmax = 448 (e4m3) or 57344 (NQ_FLAG_E5M2)
+ *   flags      0 or NQ_FLAG_E5M2 (NQ_ERR_ARG for other bits)
+ *   scale_out  [M] fp32, required when scale is NULL
+ */
+nq_status nq_layernorm_quant_fp8_ex(
+    const uint16_t* x, int64_t ld_x,
+    const float* gamma, const float* beta, float eps,
+    const float* scale, uint32_t flags,
+    uint8_t* q_out, int64_t ld_q,
+    float* scale_out,
+    int64_t M, int64_t d, void* stream);
+
+/*
  * Per-token-group FP8 e4m3 with one reciprocal per group.
  * Defined by [GRP] "Overview", "Details" and the commit message: scales are
  * amax / 448 per group of `group_size` contiguous elements, and elements are
@@ -160,6 +202,16 @@ nq_status nq_layernorm_quant_fp8(
 nq_status nq_per_token_group_quant_fp8(
     const uint16_t* x, int64_t ld_x, int64_t M, int64_t K,
     int32_t group_size, int32_t scale_mode,
+    uint8_t* q_out, int64_t ld_q, float* scale_out, void* stream);
+
+/*
+ * The same op with an output-format choice: flags 0 or NQ_FLAG_E5M2 (then
+ * s = amax / 57344, rounded up to a power of two with NQ_SCALE_UE8M0, and
+ * e5m2 codes).  Other arguments as above.
+ */
+nq_status nq_per_token_group_quant_fp8_ex(
+    const uint16_t* x, int64_t ld_x, int64_t M, int64_t K,
+    int32_t group_size, int32_t scale_mode, uint32_t flags,
     uint8_t* q_out, int64_t ld_q, float* scale_out, void* stream);
 
 /*
@@ -189,7 +241,8 @@ nq_status nq_per_token_group_quant_fp8(
  *   gamma        [d] fp32
  *   group_size   128 (NQ_ERR_ARG otherwise); d % group_size == 0
  *   scale_mode   NQ_SCALE_FP32 or NQ_SCALE_UE8M0 (NQ_ERR_ARG otherwise)
- *   flags        0 or NQ_FLAG_BF16_SOURCE (NQ_ERR_ARG for other bits)
+ *   flags        any of NQ_FLAG_BF16_SOURCE, NQ_FLAG_E5M2 (then 448 above is
+ *                57344 and the codes are e5m2); NQ_ERR_ARG for other bits
  *   q_out        [M, d] e4m3 codes, row stride ld_q
  *   scale_out    [M, d / group_size] fp32, row stride ld_s (>= d / group_size)
  *   norm_out     [M, d] bf16, row stride ld_n, or NULL
@@ -257,6 +310,7 @@ const char* nq_version(void);
  *   NQ_CODEC_E4M3: out[i] = e4m3 code of in[i]   (clamp to +-448, nearest-even)
  *   NQ_CODEC_E2M1: out[i] = E2M1 code of in[i]   (clamp to +-6, nearest-even)
  *   NQ_CODEC_BF16: out16[i] = bf16 bits of in[i] (nearest-even)
+ *   NQ_CODEC_E5M2: out[i] = e5m2 code of in[i]   (clamp to +-57344, nearest-even)
  * `out` is uint8_t for the 8-bit formats and uint16_t for bf16.
  *
  * nq_diag_copy: copies `bytes` (a multiple of 16, both pointers 16-byte
@@ -266,6 +320,7 @@ const char* nq_version(void);
 #define NQ_CODEC_E4M3 0
 #define NQ_CODEC_E2M1 1
 #define NQ_CODEC_BF16 2
+#define NQ_CODEC_E5M2 3
 nq_status nq_diag_codec(int32_t kind, const float* in, void* out, int64_t n, void* stream);
 nq_status nq_diag_copy(const void* src, void* dst, int64_t bytes, void* stream);
 

@@ -65,9 +65,10 @@ def _code_steps(a: np.ndarray, b: np.ndarray, mag_mask: int, sign_bit: int):
 
 
 def assert_codes(got: np.ndarray, want: np.ndarray, what: str, fmt: str = "e4m3"):
-    """e4m3 codes (uint8 per element) or E2M1 codes (uint8, one per element)."""
+    """e4m3 / e5m2 codes (uint8 per element) or E2M1 codes (uint8, one per element)."""
     assert got.shape == want.shape, (what, got.shape, want.shape)
-    mag, sign = (0x7F, 0x80) if fmt == "e4m3" else (0x7, 0x8)
+    # e4m3 and e5m2 codes both order magnitudes by their low 7 bits
+    mag, sign = (0x7F, 0x80) if fmt in ("e4m3", "e5m2") else (0x7, 0x8)
     same, adjacent = _code_steps(got, want, mag, sign)
     diff = ~same
     n = diff.sum()

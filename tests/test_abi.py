@@ -14,6 +14,20 @@ LIB = os.path.join(ROOT, "fp4_quantization_amd", "libnq.so")
 NQ_OK, NQ_ERR_NULL, NQ_ERR_SHAPE, NQ_ERR_STRIDE, NQ_ERR_ALIAS, NQ_ERR_ARG = 0, -1, -2, -3, -4, -6
 
 
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# The validation calls below pass fake device addresses and expect every one
+# to be rejected on the host; where a GPU is visible a validation regression
+# would launch a kernel on them, so these run only where none is.
+pytestmark = pytest.mark.skipif(_gpu_visible(), reason="host-validation tests pass fake device addresses")
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -30,6 +44,11 @@ def lib():
     L.nq_fused_add_rmsnorm_quant_fp8_group.argtypes = [v, i64, v, i64, v, i64, v, f32, i32, i32,
                                                        ctypes.c_uint32, v, i64, v, i64, v, i64, i64, i64, v]
     L.nq_layernorm_quant_fp8.argtypes = [v, i64, v, v, f32, v, v, i64, i64, i64, v]
+    u32 = ctypes.c_uint32
+    L.nq_fused_add_rmsnorm_quant_fp8_ex.argtypes = [v, i64, v, i64, v, i64, v, f32, v, u32, v, i64, v, v, i64,
+                                                    i64, i64, v]
+    L.nq_layernorm_quant_fp8_ex.argtypes = [v, i64, v, v, f32, v, u32, v, i64, v, i64, i64, v]
+    L.nq_per_token_group_quant_fp8_ex.argtypes = [v, i64, i64, i64, i32, i32, u32, v, i64, v, v]
     L.nq_per_token_group_quant_fp8.argtypes = [v, i64, i64, i64, i32, i32, v, i64, v, v]
     L.nq_rmsnorm_quant_nvfp4.argtypes = [v, i64, v, i64, v, i64, v, f32, v, v, i64, v, i64, v, i64, i64, i64, v]
     L.nq_diag_codec.argtypes = [i32, v, v, i64, v]
@@ -41,7 +60,9 @@ def lib():
 
 def test_header_declares_the_four_entry_points():
     fns = declared_functions()
-    for name in ("nq_fused_add_rmsnorm_quant_fp8", "nq_fused_add_rmsnorm_quant_fp8_group",
+    for name in ("nq_fused_add_rmsnorm_quant_fp8", "nq_fused_add_rmsnorm_quant_fp8_ex",
+                 "nq_fused_add_rmsnorm_quant_fp8_group", "nq_layernorm_quant_fp8_ex",
+                 "nq_per_token_group_quant_fp8_ex",
                  "nq_layernorm_quant_fp8",
                  "nq_per_token_group_quant_fp8", "nq_rmsnorm_quant_nvfp4", "nq_status_string"):
         assert name in fns
@@ -112,7 +133,7 @@ def test_rmsnorm_fp8_group_validation(lib):
     assert call(M=0, ro=R, mode=1, flags=1) == NQ_OK
     assert call(gs=64) == NQ_ERR_ARG
     assert call(mode=2) == NQ_ERR_ARG
-    assert call(flags=2) == NQ_ERR_ARG
+    assert call(flags=4) == NQ_ERR_ARG         # unknown bit
     assert call(eps=-1.0) == NQ_ERR_ARG
     assert call(d=2800, ld_x=2800, ld_r=2800, ld_ro=2800, ld_q=2800) == NQ_ERR_SHAPE  # d % 128
     assert call(ld_s=21) == NQ_ERR_STRIDE
@@ -149,6 +170,37 @@ def test_group_fp8_validation(lib):
     assert call(ld_q=4095) == NQ_ERR_STRIDE
     assert call(s=None) == NQ_ERR_NULL
     assert call(s=X + 64) == NQ_ERR_ALIAS
+
+
+def test_ex_entry_points_validation(lib):
+    """The format-flag forms: unknown bits are rejected, the dynamic LayerNorm
+    needs scale_out, and aliasing / NULL checks apply as in the base forms."""
+    rms = lambda **k: lib.nq_fused_add_rmsnorm_quant_fp8_ex(
+        X, 256, R, 256, RO, 256, G, 1e-6, k.get("ss", None), k.get("flags", 0), k.get("q", Q), 256,
+        k.get("sc", SC), None, 0, k.get("M", 4), 256, None)
+    assert rms(M=0, flags=2) == NQ_OK
+    assert rms(flags=1) == NQ_ERR_ARG          # the bf16-source bit is not an option here
+    assert rms(flags=6) == NQ_ERR_ARG
+    assert rms(flags=2, sc=None) == NQ_ERR_NULL
+    assert rms(flags=2, q=X) == NQ_ERR_ALIAS
+    ln = lambda **k: lib.nq_layernorm_quant_fp8_ex(
+        X, 512, G, B, 1e-5, k.get("s", None), k.get("flags", 0), k.get("q", Q), 512, k.get("so", SC),
+        k.get("M", 2), 512, None)
+    assert ln(M=0) == NQ_OK
+    assert ln(M=0, flags=2, s=S) == NQ_OK
+    assert ln(flags=8) == NQ_ERR_ARG
+    assert ln(so=None) == NQ_ERR_NULL          # dynamic without scale_out
+    assert ln(so=Q + 16) == NQ_ERR_ALIAS       # scale_out over the codes
+    assert ln(so=G + 4) == NQ_ERR_ALIAS        # scale_out over gamma
+    assert ln(s=S, so=None, q=X) == NQ_ERR_ALIAS
+    # the static base form still requires its scale
+    assert lib.nq_layernorm_quant_fp8(X, 512, G, B, 1e-5, None, Q, 512, 2, 512, None) == NQ_ERR_NULL
+    grp = lambda **k: lib.nq_per_token_group_quant_fp8_ex(
+        X, 4096, k.get("M", 2), 4096, 128, k.get("mode", 0), k.get("flags", 0), Q, 4096, k.get("s", SC), None)
+    assert grp(M=0, flags=2, mode=1) == NQ_OK
+    assert grp(flags=1) == NQ_ERR_ARG
+    assert grp(flags=2, s=None) == NQ_ERR_NULL
+    assert grp(flags=2, s=X + 64) == NQ_ERR_ALIAS
 
 
 def test_nvfp4_validation(lib):

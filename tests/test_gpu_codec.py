@@ -1,5 +1,5 @@
-"""GPU parity of the device conversion routines the kernels use (e4m3 with
-clamp, E2M1 with clamp, bf16) against the oracle's codecs, over every binary32
+"""GPU parity of the device conversion routines the kernels use (e4m3 and
+e5m2 with clamp, E2M1 with clamp, bf16) against the oracle's codecs, over every binary32
 in the binades that reach each format, both signs, plus midpoints and
 saturation edges.  Through nq_diag_codec, i.e. the C ABI."""
 import numpy as np
@@ -56,6 +56,30 @@ def test_e4m3_device_codec_edges(nq, orc):
     for n in (v.size, 1, 7, 9):  # ragged tails of the 8-per-thread packing
         got = _run(nq, nq.NQ_CODEC_E4M3, v[:n])
         assert np.array_equal(got, orc.e4m3_encode(v[:n]))
+
+
+@pytest.mark.parametrize("exp_lo", [109, 116, 123, 130, 137])
+def test_e5m2_device_codec_exhaustive(nq, orc, exp_lo):
+    """Binades 2^-18 .. 2^16 (every value that reaches e5m2, the clamp above)
+    split over five tests, both signs."""
+    for e in range(exp_lo, min(exp_lo + 7, 144)):
+        for sign in (0, 1):
+            v = _binade(e, sign)
+            got = _run(nq, nq.NQ_CODEC_E5M2, v)
+            want = orc.e5m2_encode(v)
+            bad = np.nonzero(got != want)[0]
+            assert bad.size == 0, (e, sign, bad.size, v[bad[:4]], got[bad[:4]], want[bad[:4]])
+
+
+def test_e5m2_device_codec_edges(nq, orc):
+    mags = orc.e5m2_decode(np.arange(124, dtype=np.uint8)).astype(np.float64)
+    mids = ((mags[1:] + mags[:-1]) / 2).astype(np.float32)
+    v = np.concatenate([mids, -mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+                        np.array([0.0, -0.0, 57344.0, 61439.0, 61440.0, 1e6, 3e38, -3e38, 1e-40, -1e-40,
+                                  2.0 ** -17, -(2.0 ** -17)], np.float32)]).astype(np.float32)
+    for n in (v.size, 1, 7, 9):
+        got = _run(nq, nq.NQ_CODEC_E5M2, v[:n])
+        assert np.array_equal(got, orc.e5m2_encode(v[:n]))
 
 
 @pytest.mark.parametrize("exp_field", list(range(121, 130)))

@@ -570,3 +570,161 @@ def test_nvfp4_partial_wave_sizes(nq, orc, d):
     sg = calibrated_sg(orc, w)
     got = run_nvfp4(nq, w, sg, norm_out=True)
     compare_nvfp4(orc, w, got, np.arange(33), sg, norm_out=True)
+
+
+# ----------------------------------------- e5m2 outputs and dynamic LayerNorm ----
+# "feat: fused FP8 quantization output for LayerNorm" ("Description",
+# "Tests"): the FP8 output may be e4m3 or e5m2, and the library LayerNorm's
+# per-token (dynamic) path; every FP8 entry point takes NQ_FLAG_E5M2.
+
+def run_rms_fp8_ex(nq, w, flags, static_scale=None):
+    M, d = w["M"], w["d"]
+    x, r = to_dev_bf16(w["x"]), to_dev_bf16(w["residual"])
+    ro_buf, ro = guarded_bf16(M, d)
+    q_buf, q = guarded_u8(M, d)
+    s_buf, s = guarded_f32(M)
+    ss = to_dev_f32([static_scale]) if static_scale is not None else None
+    nq.nq_fused_add_rmsnorm_quant_fp8_ex(x, r, ro, to_dev_f32(w["gamma"]), w["eps"], ss, flags, q,
+                                         None if ss is not None else s)
+    torch.cuda.synchronize()
+    check_guard_u8(q_buf, M * d)
+    if ss is None:
+        assert np.all(np.isnan(s_buf[M:].cpu().numpy()))
+    return dict(q=host_u8(q), scale=s.cpu().numpy(), residual_out=host_u16(ro))
+
+
+@pytest.mark.parametrize("M", [1, 64, 8192])
+@pytest.mark.parametrize("static", [False, True])
+def test_rms_fp8_e5m2(nq, orc, M, static):
+    note(f"rms fp8 e5m2 M={M} static={static}")
+    w = W.rms_2816(M, seed=12)
+    sc = 0.02 if static else None
+    got = run_rms_fp8_ex(nq, w, nq.NQ_FLAG_E5M2, sc)
+    rows = sample_rows(M, 64)
+    o = orc.fused_add_rmsnorm_quant_fp8(w["x"][rows], w["residual"][rows], w["gamma"], w["eps"],
+                                        static_scale=sc, fmt="e5m2")
+    assert_bits_equal(got["residual_out"][rows], o["residual_out"], "residual_out")
+    if not static:
+        assert_scales(got["scale"][rows], o["scale"], "e5m2 scale")
+    assert_codes(got["q"][rows], o["q"], "e5m2 q", fmt="e5m2")
+    # the e4m3 form of the same call is unchanged by the flag's existence
+    base = run_rms_fp8_ex(nq, w, 0, sc)
+    assert_bits_equal(base["q"], run_rms_fp8(nq, w, static_scale=sc)["q"], "_ex(flags=0) vs base entry point")
+
+
+def run_ln_ex(nq, w, flags, scale=None):
+    M, d = w["M"], w["d"]
+    x = to_dev_bf16(w["x"])
+    q_buf, q = guarded_u8(M, d)
+    s_buf, s = guarded_f32(M)
+    st = to_dev_f32([scale]) if scale is not None else None
+    nq.nq_layernorm_quant_fp8_ex(x[:, :d] if x.shape[1] != d else x, to_dev_f32(w["gamma"]),
+                                 to_dev_f32(w["beta"]), w["eps"], st, flags, q, None if st is not None else s)
+    torch.cuda.synchronize()
+    check_guard_u8(q_buf, M * d)
+    if st is None:
+        assert np.all(np.isnan(s_buf[M:].cpu().numpy()))
+    else:
+        assert np.all(np.isnan(s_buf.cpu().numpy())), "static form wrote scale_out"
+    return host_u8(q), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_layernorm_dynamic_full_config_sampled(nq, orc, fmt):
+    note(f"layernorm dynamic M=16384 d=4096 {fmt}")
+    w = W.layernorm_rows()
+    q, s = run_ln_ex(nq, w, nq.NQ_FLAG_E5M2 if fmt == "e5m2" else 0)
+    rows = sample_rows(w["M"], 96)
+    o = orc.layernorm_quant_fp8(w["x"][rows], w["gamma"], w["beta"], w["eps"], None, fmt=fmt)
+    assert_scales(s[rows], o["scale"], "ln dynamic scale")
+    assert_codes(q[rows], o["q"], "ln dynamic q", fmt=fmt)
+
+
+@pytest.mark.parametrize("d", [111, 256, 768, 4096, 16384])
+@pytest.mark.parametrize("M", [1, 7, 989, 1501])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_layernorm_dynamic_shapes(nq, orc, d, M, fmt):
+    """[LNQ] "Tests": batch 1 .. 989, hidden 111 .. 16384 (odd sizes take the
+    element-wise path), both FP8 formats; here with per-token scales."""
+    note(f"layernorm dynamic d={d} M={M} {fmt}")
+    w = W.layernorm_rows(M=M, d=d, seed=3 * d + M)
+    q, s = run_ln_ex(nq, w, nq.NQ_FLAG_E5M2 if fmt == "e5m2" else 0)
+    rows = sample_rows(M, 24)
+    o = orc.layernorm_quant_fp8(w["x"][rows], w["gamma"], w["beta"], w["eps"], None, fmt=fmt)
+    assert_scales(s[rows], o["scale"], "ln dynamic scale")
+    assert_codes(q[rows], o["q"], "ln dynamic q", fmt=fmt)
+
+
+@pytest.mark.parametrize("scale", [0.01, 1.0, 10.0])
+@pytest.mark.parametrize("d", [111, 4096])
+@pytest.mark.parametrize("M", [1, 989])
+def test_layernorm_static_e5m2(nq, orc, scale, d, M):
+    """[LNQ] "Tests": e5m2 at scales 0.01, 1 and 10."""
+    note(f"layernorm static e5m2 d={d} M={M} scale={scale}")
+    w = W.layernorm_rows(M=M, d=d, seed=d + 7 * M)
+    q, _ = run_ln_ex(nq, w, nq.NQ_FLAG_E5M2, scale)
+    rows = sample_rows(M, 24)
+    o = orc.layernorm_quant_fp8(w["x"][rows], w["gamma"], w["beta"], w["eps"], scale, fmt="e5m2")
+    assert_codes(q[rows], o["q"], "ln static e5m2 q", fmt="e5m2")
+
+
+def test_layernorm_dynamic_schedules_and_zero_rows(nq, orc):
+    """Many rows (gamma and beta staged) and few rows give identical bits; a
+    constant row gives y = beta, an all-zero row (beta = 0) scale 0."""
+    note("layernorm dynamic schedules / special rows")
+    w = W.layernorm_rows(M=2048, d=4096, seed=23)
+    x = w["x"].copy()
+    x[5] = W.to_bf16_bits(np.full(4096, -2.5, np.float32))
+    w = dict(w, x=x)
+    q, s = run_ln_ex(nq, w, 0)
+    o = orc.layernorm_quant_fp8(x[[5]], w["gamma"], w["beta"], w["eps"], None, want_y=True)
+    assert np.array_equal(o["y"][0], w["beta"])
+    assert_bits_equal(s[[5]].view(np.uint32), o["scale"].view(np.uint32), "constant-row scale")
+    assert_bits_equal(q[[5]], o["q"], "constant-row codes")
+    for lo, hi in ((0, 16), (1001, 1004), (2047, 2048)):
+        qs, ss = run_ln_ex(nq, dict(w, x=x[lo:hi], M=hi - lo), 0)
+        assert_bits_equal(qs, q[lo:hi], "ln dynamic q few-rows vs many-rows")
+        assert_bits_equal(ss.view(np.uint32), s[lo:hi].view(np.uint32), "ln dynamic scale")
+    wz = dict(w, x=np.zeros((4, 4096), np.uint16), beta=np.zeros(4096, np.float32), M=4)
+    qz, sz = run_ln_ex(nq, wz, nq.NQ_FLAG_E5M2)
+    assert np.all(sz == 0) and np.all((qz & 0x7F) == 0)
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+@pytest.mark.parametrize("M", [1, 32768])
+def test_group_e5m2(nq, orc, M, ue8m0):
+    note(f"group e5m2 M={M} ue8m0={ue8m0}")
+    w = W.group_t3(M)
+    x = to_dev_bf16(w["x"])
+    q_buf, q = guarded_u8(M, 4096)
+    s_buf, s = guarded_f32(M * 32)
+    nq.nq_per_token_group_quant_fp8_ex(x, q, s, 128, nq.NQ_SCALE_UE8M0 if ue8m0 else nq.NQ_SCALE_FP32,
+                                       nq.NQ_FLAG_E5M2)
+    torch.cuda.synchronize()
+    check_guard_u8(q_buf, M * 4096)
+    assert np.all(np.isnan(s_buf[M * 32:].cpu().numpy()))
+    qh, sh = host_u8(q), s.cpu().numpy().reshape(M, 32)
+    rows = sample_rows(M, 128)
+    o = orc.per_token_group_quant_fp8(w["x"][rows], 128, ue8m0=ue8m0, fmt="e5m2")
+    assert_bits_equal(sh[rows].view(np.uint32), o["scale"].view(np.uint32), "e5m2 group scales")
+    assert_bits_equal(qh[rows], o["q"], "e5m2 group codes")
+
+
+@pytest.mark.parametrize("bf16_source", [False, True])
+def test_rms_group_e5m2(nq, orc, bf16_source):
+    note(f"rms group e5m2 bf16_source={bf16_source}")
+    w = W.rms_group_7168(1001, seed=6)
+    M, d = 1001, 7168
+    x, r = to_dev_bf16(w["x"]), to_dev_bf16(w["residual"])
+    ro = torch.empty_like(r)
+    q = torch.empty(M, d, dtype=torch.uint8, device="cuda")
+    s = torch.empty(M, d // 128, dtype=torch.float32, device="cuda")
+    flags = nq.NQ_FLAG_E5M2 | (nq.NQ_FLAG_BF16_SOURCE if bf16_source else 0)
+    nq.nq_fused_add_rmsnorm_quant_fp8_group(x, r, ro, to_dev_f32(w["gamma"]), w["eps"], q, s, flags=flags)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 40)
+    o = orc.fused_add_rmsnorm_quant_fp8_group(w["x"][rows], w["residual"][rows], w["gamma"], w["eps"],
+                                              bf16_source=bf16_source, fmt="e5m2")
+    assert_bits_equal(host_u16(ro)[rows], o["residual_out"], "residual_out")
+    assert_scales(s.cpu().numpy()[rows], o["scale"], "e5m2 group scale")
+    assert_codes(host_u8(q)[rows], o["q"], "e5m2 fused group q", fmt="e5m2")
