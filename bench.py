@@ -214,6 +214,38 @@ class RmsGroupCase(Case):
                       f"M={M}, d={d}")
 
 
+class UnfusedCase(Case):
+    """The two-kernel pipeline the fusion replaces: add+RMSNorm -> bf16 rows,
+    then per-token FP8 of those rows.  One step = both launches; `bytes` is the
+    pipeline's own traffic (the bf16 round trip included)."""
+
+    def __init__(self, torch, nq, M, d=2816):
+        from fp4_quantization_amd import workloads as W, traffic
+        w = W.rms_2816(M)
+        self.bytes = M * traffic.unfused_add_rmsnorm_fp8_per_row(d) + 4 * d
+        self.fused_bytes = traffic.total(traffic.fused_add_rmsnorm_fp8(M, d))
+        x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
+        r = torch.from_numpy(w["residual"]).view(torch.bfloat16).cuda()
+        self.g = torch.from_numpy(w["gamma"]).cuda()
+        lib = nq.library()
+        self.fn1, self.fn2 = lib.nq_fused_add_rmsnorm_bf16, lib.nq_per_token_quant_fp8
+        self.bufs, self.args = [], []
+        for _ in range(_sets_for(self.bytes)):
+            b = dict(x=x.clone(), r=r.clone(), ro=torch.empty_like(r), n=torch.empty_like(r),
+                     q=torch.empty(M, d, dtype=torch.uint8, device="cuda"),
+                     s=torch.empty(M, dtype=torch.float32, device="cuda"))
+            self.bufs.append(b)
+            self.args.append(((b["x"].data_ptr(), d, b["r"].data_ptr(), d, b["ro"].data_ptr(), d, self.g.data_ptr(),
+                               w["eps"], b["n"].data_ptr(), d, M, d),
+                              (b["n"].data_ptr(), d, None, 0, b["q"].data_ptr(), d, b["s"].data_ptr(), M, d)))
+        self.label = f"unfused pipeline (add+RMSNorm -> bf16, then per-token FP8), M={M}, d={d}"
+
+    def step(self, i, stream):
+        a1, a2 = self.args[i % len(self.args)]
+        if self.fn1(*a1, stream) != 0 or self.fn2(*a2, stream) != 0:
+            raise RuntimeError(f"{self.label}: launch failed")
+
+
 class CopyCase(Case):
     """The 128-bit copy kernel over the same byte count: a same-box ceiling."""
 
@@ -497,12 +529,14 @@ def run_suite(torch, nq):
         ("nvfp4_slice_m1", lambda: Nvfp4Case(torch, nq, 1, sliced=True)),
         ("nvfp4_slice_m64", lambda: Nvfp4Case(torch, nq, 64, sliced=True)),
         ("nvfp4_slice_m8192", lambda: Nvfp4Case(torch, nq, 8192, sliced=True)),
+        ("unfused_2816_m8192", lambda: UnfusedCase(torch, nq, 8192)),
         ("copy_161MB", lambda: CopyCase(torch, nq, 161_524_736)),
     ]
     for name, make in cases:
         case = make()
         us_graph = time_graph(torch, case) * 1e3
         line = {"workload": name, "label": case.label, "bytes_per_call": case.bytes,
+                **({"fused_bytes_per_call": case.fused_bytes} if hasattr(case, "fused_bytes") else {}),
                 "us_per_call_graph": round(us_graph, 3),
                 "us_per_launch_events": round(time_launch_events(torch, case, 50) * 1e3, 3),
                 "GBps_graph": round(case.bytes / (us_graph * 1e-6) / 1e9, 1),

@@ -26,6 +26,7 @@ SOURCES = [
     "nq_layernorm_fp8.hip",
     "nq_rmsnorm_nvfp4.hip",
     "nq_group_fp8.hip",
+    "nq_unfused.hip",
     "nq_misc.hip",
 ]
 

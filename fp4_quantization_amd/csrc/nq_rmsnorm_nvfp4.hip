@@ -8,6 +8,11 @@
 // bf16 norm output, a fresh residual buffer, hidden % 16 == 0, loop bounds
 // uniform across the lanes that shuffle together).
 //
+// With NQ_FLAG_BF16_SOURCE the values quantized are bf16(y), the rounding a
+// bf16 norm_out stores, so the codes and block scales equal the standalone
+// quantizer applied to norm_out ([NVFP4] commit notes: re-quantizing the
+// fused op's own norm_out reproduces its outputs bit for bit).
+//
 // The row is held in registers exactly as in the per-token FP8 kernel.  A
 // 16-element block is two adjacent chunks, owned by lanes t and t^1 of the
 // same load instruction, so the block maximum is one cross-lane exchange.
@@ -33,6 +38,7 @@ struct RmsFp4Args {
     int64_t M;
     int d;
     float eps;
+    bool bf16_source;  // quantize bf16(y): the standalone quantizer applied to norm_out
 };
 
 // VEC additionally needs 4-byte aligned packed-code rows (one dword per chunk).
@@ -73,11 +79,15 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
         for (int k = 0; k < 8; ++k) {
             const float n = z[k] * rstd;
             y[k] = n * g[k];
-            amax = fmaxf(amax, fabsf(y[k]));
         }
-        if (a.norm_out)
-            nio.store16(e, e < d, make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
-                                             pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])));
+        if (a.norm_out || a.bf16_source) {
+            const uint4 nw = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                        pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+            nio.store16(e, e < d, nw);  // dropped when norm_out is NULL
+            if (a.bf16_source) unpack_bf16x8(nw, y);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(y[k]));
         // Block of 16 = this chunk and the partner lane's (same load
         // instruction, lanes t and t^1).
         amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
@@ -108,17 +118,18 @@ struct RmsFp4Kernel {
 
 using namespace nq;
 
-extern "C" nq_status nq_rmsnorm_quant_nvfp4(
+extern "C" nq_status nq_rmsnorm_quant_nvfp4_ex(
     const uint16_t* x, int64_t ld_x,
     const uint16_t* residual_in, int64_t ld_r,
     uint16_t* residual_out, int64_t ld_ro,
     const float* gamma, float eps,
-    const float* global_scale,
+    const float* global_scale, uint32_t flags,
     uint8_t* q_packed, int64_t ld_q,
     uint8_t* block_scale, int64_t ld_sf,
     uint16_t* norm_out, int64_t ld_n,
     int64_t M, int64_t d, void* stream)
 {
+    if ((flags & ~(uint32_t)NQ_FLAG_BF16_SOURCE) != 0) return NQ_ERR_ARG;
     if (M < 0 || d <= 0 || d > NQ_MAX_D || d % 16 != 0 || M > kMaxRows) return NQ_ERR_SHAPE;
     if (!(eps >= 0.0f) || eps > 1e30f) return NQ_ERR_ARG;
     if (bad_ld(ld_x, d) || bad_ld(ld_q, d / 2) || bad_ld(ld_sf, d / 16)) return NQ_ERR_STRIDE;
@@ -149,6 +160,22 @@ extern "C" nq_status nq_rmsnorm_quant_nvfp4(
     a.global_scale = global_scale; a.q = q_packed; a.sf = block_scale; a.norm_out = norm_out;
     a.ld_x = ld_x; a.ld_r = ld_r; a.ld_ro = ld_ro; a.ld_q = ld_q; a.ld_sf = ld_sf; a.ld_n = ld_n;
     a.M = M; a.d = (int)d; a.eps = eps;
+    a.bf16_source = (flags & NQ_FLAG_BF16_SOURCE) != 0;
     if (!launch_row_shape<RmsFp4Kernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
+}
+
+extern "C" nq_status nq_rmsnorm_quant_nvfp4(
+    const uint16_t* x, int64_t ld_x,
+    const uint16_t* residual_in, int64_t ld_r,
+    uint16_t* residual_out, int64_t ld_ro,
+    const float* gamma, float eps,
+    const float* global_scale,
+    uint8_t* q_packed, int64_t ld_q,
+    uint8_t* block_scale, int64_t ld_sf,
+    uint16_t* norm_out, int64_t ld_n,
+    int64_t M, int64_t d, void* stream)
+{
+    return nq_rmsnorm_quant_nvfp4_ex(x, ld_x, residual_in, ld_r, residual_out, ld_ro, gamma, eps, global_scale,
+                                     0u, q_packed, ld_q, block_scale, ld_sf, norm_out, ld_n, M, d, stream);
 }

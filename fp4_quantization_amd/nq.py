@@ -45,6 +45,10 @@ _SIGS = {
     "nq_per_token_group_quant_fp8": [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _i64, _vp, _vp],
     "nq_rmsnorm_quant_nvfp4": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _f32, _vp, _vp, _i64, _vp, _i64,
                                _vp, _i64, _i64, _i64, _vp],
+    "nq_rmsnorm_quant_nvfp4_ex": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _f32, _vp, _u32, _vp, _i64, _vp, _i64,
+                                  _vp, _i64, _i64, _i64, _vp],
+    "nq_fused_add_rmsnorm_bf16": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _f32, _vp, _i64, _i64, _i64, _vp],
+    "nq_per_token_quant_fp8": [_vp, _i64, _vp, _u32, _vp, _i64, _vp, _i64, _i64, _vp],
     "nq_diag_codec": [_i32, _vp, _vp, _i64, _vp],
     "nq_diag_copy": [_vp, _vp, _i64, _vp],
 }
@@ -275,6 +279,53 @@ def nq_rmsnorm_quant_nvfp4(x, residual_in, residual_out, gamma, eps, global_scal
         _vec(global_scale, torch.float32, "global_scale", 1), pq, ldq, psf, ldsf, pn, ldn,
         M, d, _stream(stream))
     _check(st, "nq_rmsnorm_quant_nvfp4")
+
+
+def nq_rmsnorm_quant_nvfp4_ex(x, residual_in, residual_out, gamma, eps, global_scale, flags,
+                              q_packed, block_scale, norm_out=None, stream=None):
+    """(Residual-add +) RMSNorm + NVFP4 with an option flag (include/nq.h)."""
+    M, d = x.shape
+    px, ldx = _mat(x, _BF16, "x")
+    pr, ldr = _mat(residual_in, _BF16, "residual_in", d)
+    pro, ldro = _mat(residual_out, _BF16, "residual_out", d)
+    pq, ldq = _mat(q_packed, (torch.uint8,), "q_packed", d // 2)
+    psf, ldsf = _mat(block_scale, _CODES8, "block_scale", d // 16)
+    pn, ldn = _mat(norm_out, _BF16, "norm_out", d)
+    st = _lib.nq_rmsnorm_quant_nvfp4_ex(
+        px, ldx, pr, ldr, pro, ldro, _vec(gamma, torch.float32, "gamma", d), float(eps),
+        _vec(global_scale, torch.float32, "global_scale", 1), int(flags), pq, ldq, psf, ldsf, pn, ldn,
+        M, d, _stream(stream))
+    _check(st, "nq_rmsnorm_quant_nvfp4_ex")
+
+
+def nq_fused_add_rmsnorm_bf16(x, residual_in, residual_out, gamma, eps, out, stream=None):
+    """(Residual-add +) RMSNorm with a bf16 output: the first kernel of the
+    unfused pipeline (include/nq.h)."""
+    M, d = x.shape
+    px, ldx = _mat(x, _BF16, "x")
+    pr, ldr = _mat(residual_in, _BF16, "residual_in", d)
+    pro, ldro = _mat(residual_out, _BF16, "residual_out", d)
+    po, ldo = _mat(out, _BF16, "out", d)
+    for t, n in ((residual_in, "residual_in"), (residual_out, "residual_out"), (out, "out")):
+        if t is not None and t.size(0) != M:
+            raise ValueError(f"{n}: expected {M} rows")
+    st = _lib.nq_fused_add_rmsnorm_bf16(px, ldx, pr, ldr, pro, ldro, _vec(gamma, torch.float32, "gamma", d),
+                                        float(eps), po, ldo, M, d, _stream(stream))
+    _check(st, "nq_fused_add_rmsnorm_bf16")
+
+
+def nq_per_token_quant_fp8(x, static_scale, flags, q_out, scale_out, stream=None):
+    """FP8 of bf16 rows with per-token (or static) scales: the second kernel
+    of the unfused pipeline (include/nq.h)."""
+    M, d = x.shape
+    px, ldx = _mat(x, _BF16, "x")
+    pq, ldq = _mat(q_out, _CODES8, "q_out", d)
+    if q_out.size(0) != M:
+        raise ValueError(f"q_out: expected {M} rows")
+    st = _lib.nq_per_token_quant_fp8(
+        px, ldx, _vec(static_scale, torch.float32, "static_scale", 1), int(flags), pq, ldq,
+        _vec(scale_out, torch.float32, "scale_out", M if static_scale is None else None), M, d, _stream(stream))
+    _check(st, "nq_per_token_quant_fp8")
 
 
 def nq_diag_codec(kind: int, x: torch.Tensor, out: torch.Tensor, stream=None):

@@ -295,6 +295,59 @@ nq_status nq_rmsnorm_quant_nvfp4(
     uint16_t* norm_out, int64_t ld_n,
     int64_t M, int64_t d, void* stream);
 
+/*
+ * The same NVFP4 op with an option: flags 0 or NQ_FLAG_BF16_SOURCE (the
+ * values quantized are bf16(y_i), so the codes and block scales equal the
+ * standalone quantizer applied to the bf16 norm_out -- [NVFP4] commit notes:
+ * re-quantizing the fused op's own norm_out reproduces its outputs bit for
+ * bit).  NQ_ERR_ARG for other bits.
+ */
+nq_status nq_rmsnorm_quant_nvfp4_ex(
+    const uint16_t* x, int64_t ld_x,
+    const uint16_t* residual_in, int64_t ld_r,
+    uint16_t* residual_out, int64_t ld_ro,
+    const float* gamma, float eps,
+    const float* global_scale, uint32_t flags,
+    uint8_t* q_packed, int64_t ld_q,
+    uint8_t* block_scale, int64_t ld_sf,
+    uint16_t* norm_out, int64_t ld_n,
+    int64_t M, int64_t d, void* stream);
+
+/*
+ * The unfused pipeline the fused ops replace ([FUSE] "TL;DR", "Where
+ * norm+quant sits": the norm writes a bf16 activation that a second kernel
+ * reads back and quantizes).  Run back to back they reproduce the unfused
+ * codes and the traffic the fusion removes.
+ *
+ * nq_fused_add_rmsnorm_bf16: z_i, residual_out_i, rstd and y_i exactly as
+ *   nq_fused_add_rmsnorm_quant_fp8; out_i = bf16(y_i).
+ *     out  [M, d] bf16, row stride ld_o (written)
+ *
+ * nq_per_token_quant_fp8: FP8 of bf16 rows x, the quantization step of
+ *   nq_fused_add_rmsnorm_quant_fp8 on y_i = x_i:
+ *     dynamic (static_scale == NULL): s = max_i |x_i| / fmax -> scale_out[m],
+ *       q_i = fp8(x_i / s) (0 if s == 0)
+ *     static: q_i = fp8(x_i * (1 / static_scale[0]))
+ *   fmax = 448 (e4m3) or 57344 (flags = NQ_FLAG_E5M2; NQ_ERR_ARG for other bits)
+ *     x          [M, d] bf16, row stride ld_x
+ *     q_out      [M, d] FP8 codes, row stride ld_q
+ *     scale_out  [M] fp32 (dynamic only)
+ */
+nq_status nq_fused_add_rmsnorm_bf16(
+    const uint16_t* x, int64_t ld_x,
+    const uint16_t* residual_in, int64_t ld_r,
+    uint16_t* residual_out, int64_t ld_ro,
+    const float* gamma, float eps,
+    uint16_t* out, int64_t ld_o,
+    int64_t M, int64_t d, void* stream);
+
+nq_status nq_per_token_quant_fp8(
+    const uint16_t* x, int64_t ld_x,
+    const float* static_scale, uint32_t flags,
+    uint8_t* q_out, int64_t ld_q,
+    float* scale_out,
+    int64_t M, int64_t d, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* nq_status_string(nq_status status);
 

@@ -49,6 +49,10 @@ def lib():
                                                     i64, i64, v]
     L.nq_layernorm_quant_fp8_ex.argtypes = [v, i64, v, v, f32, v, u32, v, i64, v, i64, i64, v]
     L.nq_per_token_group_quant_fp8_ex.argtypes = [v, i64, i64, i64, i32, i32, u32, v, i64, v, v]
+    L.nq_rmsnorm_quant_nvfp4_ex.argtypes = [v, i64, v, i64, v, i64, v, f32, v, u32, v, i64, v, i64, v, i64, i64,
+                                            i64, v]
+    L.nq_fused_add_rmsnorm_bf16.argtypes = [v, i64, v, i64, v, i64, v, f32, v, i64, i64, i64, v]
+    L.nq_per_token_quant_fp8.argtypes = [v, i64, v, u32, v, i64, v, i64, i64, v]
     L.nq_per_token_group_quant_fp8.argtypes = [v, i64, i64, i64, i32, i32, v, i64, v, v]
     L.nq_rmsnorm_quant_nvfp4.argtypes = [v, i64, v, i64, v, i64, v, f32, v, v, i64, v, i64, v, i64, i64, i64, v]
     L.nq_diag_codec.argtypes = [i32, v, v, i64, v]
@@ -201,6 +205,34 @@ def test_ex_entry_points_validation(lib):
     assert grp(flags=1) == NQ_ERR_ARG
     assert grp(flags=2, s=None) == NQ_ERR_NULL
     assert grp(flags=2, s=X + 64) == NQ_ERR_ALIAS
+
+
+def test_unfused_pair_and_nvfp4_ex_validation(lib):
+    norm = lambda **k: lib.nq_fused_add_rmsnorm_bf16(
+        X, 256, k.get("r", R), 256, k.get("ro", RO), 256, G, k.get("eps", 1e-6), k.get("o", N),
+        k.get("ld_o", 256), k.get("M", 4), 256, None)
+    assert norm(M=0) == NQ_OK
+    assert norm(o=None) == NQ_ERR_NULL
+    assert norm(ro=None) == NQ_ERR_NULL
+    assert norm(ld_o=255) == NQ_ERR_STRIDE
+    assert norm(eps=-1.0) == NQ_ERR_ARG
+    assert norm(o=X + 2) == NQ_ERR_ALIAS
+    assert norm(o=RO + 64) == NQ_ERR_ALIAS
+    quant = lambda **k: lib.nq_per_token_quant_fp8(
+        k.get("x", X), 256, k.get("ss", None), k.get("flags", 0), k.get("q", Q), k.get("ld_q", 256),
+        k.get("sc", SC), k.get("M", 4), 256, None)
+    assert quant(M=0, flags=2) == NQ_OK
+    assert quant(flags=1) == NQ_ERR_ARG
+    assert quant(sc=None) == NQ_ERR_NULL
+    assert quant(ss=S, sc=None, M=0) == NQ_OK
+    assert quant(ld_q=100) == NQ_ERR_STRIDE
+    assert quant(q=X + 16) == NQ_ERR_ALIAS
+    assert quant(sc=Q + 8) == NQ_ERR_ALIAS
+    fp4 = lambda **k: lib.nq_rmsnorm_quant_nvfp4_ex(
+        X, 2112, None, 0, None, 0, G, 1e-6, S, k.get("flags", 0), Q, 768, SC, 96, None, 0, k.get("M", 2),
+        1536, None)
+    assert fp4(M=0, flags=1) == NQ_OK
+    assert fp4(flags=2) == NQ_ERR_ARG          # no e5m2 form of NVFP4
 
 
 def test_nvfp4_validation(lib):
