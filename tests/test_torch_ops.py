@@ -1,0 +1,201 @@
+"""The torch.library custom ops (fp4_quantization_amd/torch_ops.py).
+
+CPU: every op traces under FakeTensorMode with the right output shapes and
+dtypes and returns fresh tensors (no output aliases an input).
+GPU: each op equals the C entry point it wraps bit for bit;
+torch.library.opcheck passes; compiled code (torch.compile, full graph) gives
+the eager result; and a poisoned-kernel probe ("Fusing RMSNorm and FP8
+Quantization Under torch.compile", "Gating": replace the kernel with a
+poison returning zeros and check that the compiled output changes) shows the
+compiled graph calls the HIP kernel at run time instead of a traced constant.
+"""
+import numpy as np
+import pytest
+import torch
+from torch._subclasses.fake_tensor import FakeTensorMode
+
+from fp4_quantization_amd import workloads as W
+
+
+@pytest.fixture(scope="module")
+def ops():
+    import fp4_quantization_amd.torch_ops as m
+    return m
+
+
+def _fake_inputs(M=4, d=2816):
+    x = torch.empty(M, d, dtype=torch.bfloat16, device="cuda")
+    r = torch.empty(M, d, dtype=torch.bfloat16, device="cuda")
+    g = torch.empty(d, dtype=torch.float32, device="cuda")
+    s = torch.empty(1, dtype=torch.float32, device="cuda")
+    return x, r, g, s
+
+
+@pytest.mark.parametrize("e5m2", [False, True])
+def test_fake_shapes_and_dtypes(ops, e5m2):
+    f8 = torch.float8_e5m2 if e5m2 else torch.float8_e4m3fn
+    with FakeTensorMode():
+        x, r, g, s = _fake_inputs()
+        M, d = x.shape
+        q, sc, ro = torch.ops.nq.add_rmsnorm_fp8(x, r, g, 1e-6, e5m2)
+        assert (q.shape, q.dtype, sc.shape, sc.dtype, ro.shape, ro.dtype) == \
+            ((M, d), f8, (M,), torch.float32, (M, d), torch.bfloat16)
+        q, sc = torch.ops.nq.rmsnorm_fp8(x, g, 1e-6, e5m2)
+        assert (q.dtype, sc.shape) == (f8, (M,))
+        q, ro = torch.ops.nq.add_rmsnorm_fp8_static(x, r, g, 1e-6, s, e5m2)
+        assert (q.dtype, ro.dtype) == (f8, torch.bfloat16)
+        assert torch.ops.nq.rmsnorm_fp8_static(x, g, 1e-6, s, e5m2).shape == (M, d)
+        q, sc, ro = torch.ops.nq.add_rmsnorm_fp8_group(x, r, g, 1e-6, True, False, e5m2)
+        assert (q.dtype, sc.shape, sc.dtype) == (f8, (M, d // 128), torch.float32)
+        q, sc = torch.ops.nq.rmsnorm_fp8_group(x, g, 1e-6, False, True, e5m2)
+        assert sc.shape == (M, d // 128)
+        q, sc = torch.ops.nq.group_quant_fp8(x, False, e5m2)
+        assert (q.dtype, sc.shape) == (f8, (M, d // 128))
+        b = torch.empty(d, dtype=torch.float32, device="cuda")
+        assert torch.ops.nq.layernorm_fp8_static(x, g, b, 1e-5, s, e5m2).dtype == f8
+        q, sc = torch.ops.nq.layernorm_fp8(x, g, b, 1e-5, e5m2)
+        assert (q.dtype, sc.shape) == (f8, (M,))
+        q, sc = torch.ops.nq.per_token_quant_fp8(x, e5m2)
+        assert (q.dtype, sc.shape) == (f8, (M,))
+    with FakeTensorMode():
+        x, r, g, s = _fake_inputs(d=7168)
+        q, sf, ro = torch.ops.nq.add_rmsnorm_nvfp4(x, r, g, 1e-6, s, False)
+        assert (q.shape, q.dtype, sf.shape, sf.dtype) == ((4, 3584), torch.uint8, (4, 448), torch.uint8)
+        buf = torch.empty(4, 2112, dtype=torch.bfloat16, device="cuda")
+        q, sf = torch.ops.nq.rmsnorm_nvfp4(buf[:, :1536], g[:1536], 1e-6, s, True)
+        assert (q.shape, sf.shape) == ((4, 768), (4, 96))
+        n, ro = torch.ops.nq.add_rmsnorm_bf16(x, r, g, 1e-6)
+        assert n.shape == ro.shape == (4, 7168)
+
+
+def test_schemas_declare_no_mutation_or_aliasing(ops):
+    for name in ops.OPS:
+        schema = getattr(torch.ops.nq, name).default._schema
+        assert not schema.is_mutable, name
+        for ret in schema.returns:
+            assert ret.alias_info is None, (name, ret)
+
+
+# -------------------------------------------------------------- on the GPU --
+
+def _inputs(M=64, d=2816, seed=3):
+    w = W.rms_2816(M, seed=seed) if d == 2816 else W.rms_rows(M, d, 0, 1.0, seed=seed)
+    x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
+    r = torch.from_numpy(w["residual"]).view(torch.bfloat16).cuda()
+    g = torch.from_numpy(w["gamma"]).cuda()
+    return w, x, r, g
+
+
+def _bits(t):
+    return t.view(torch.uint8).cpu().numpy() if t.element_size() == 1 else t.view(torch.int16).cpu().numpy() \
+        if t.element_size() == 2 else t.view(torch.int32).cpu().numpy()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("e5m2", [False, True])
+def test_ops_equal_the_c_entry_points(ops, e5m2):
+    from fp4_quantization_amd import nq
+    w, x, r, g = _inputs()
+    M, d = x.shape
+    fl = nq.NQ_FLAG_E5M2 if e5m2 else 0
+    q, s, ro = torch.ops.nq.add_rmsnorm_fp8(x, r, g, w["eps"], e5m2)
+    q2 = torch.empty(M, d, dtype=torch.uint8, device="cuda")
+    s2 = torch.empty(M, device="cuda")
+    ro2 = torch.empty_like(r)
+    nq.nq_fused_add_rmsnorm_quant_fp8_ex(x, r, ro2, g, w["eps"], None, fl, q2, s2)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(q), _bits(q2)) and np.array_equal(_bits(s), _bits(s2))
+    assert np.array_equal(_bits(ro), _bits(ro2))
+    assert ro.data_ptr() != r.data_ptr()                     # fresh, not in place
+    assert np.array_equal(_bits(r), w["residual"].view(np.int16))  # the input is untouched
+    qg, sg, _ = torch.ops.nq.add_rmsnorm_fp8_group(x, r, g, w["eps"], False, False, e5m2)
+    qg2 = torch.empty(M, d, dtype=torch.uint8, device="cuda")
+    sg2 = torch.empty(M, d // 128, device="cuda")
+    nq.nq_fused_add_rmsnorm_quant_fp8_group(x, r, torch.empty_like(r), g, w["eps"], qg2, sg2, flags=fl)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(qg), _bits(qg2)) and np.array_equal(_bits(sg), _bits(sg2))
+    n, _ = torch.ops.nq.add_rmsnorm_bf16(x, r, g, w["eps"])
+    qu, su = torch.ops.nq.per_token_quant_fp8(n, e5m2)
+    qu2 = torch.empty(M, d, dtype=torch.uint8, device="cuda")
+    su2 = torch.empty(M, device="cuda")
+    nq.nq_per_token_quant_fp8(n, None, fl, qu2, su2)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(qu), _bits(qu2)) and np.array_equal(_bits(su), _bits(su2))
+
+
+@pytest.mark.gpu
+def test_opcheck(ops):
+    w, x, r, g = _inputs(M=16)
+    b = torch.zeros_like(g)
+    sc = torch.tensor([0.05], device="cuda")
+    xs, rs, gs = x[:, :1536].contiguous(), r[:, :1536].contiguous(), g[:1536].contiguous()
+    gsc = torch.tensor([W.NVFP4_NOMINAL_GLOBAL_SCALE], device="cuda")
+    cases = [
+        (torch.ops.nq.add_rmsnorm_fp8, (x, r, g, 1e-6, False)),
+        (torch.ops.nq.rmsnorm_fp8, (x, g, 1e-6, True)),
+        (torch.ops.nq.add_rmsnorm_fp8_static, (x, r, g, 1e-6, sc, False)),
+        (torch.ops.nq.rmsnorm_fp8_static, (x, g, 1e-6, sc, False)),
+        (torch.ops.nq.add_rmsnorm_fp8_group, (x, r, g, 1e-6, True, False, False)),
+        (torch.ops.nq.rmsnorm_fp8_group, (x, g, 1e-6, False, True, True)),
+        (torch.ops.nq.group_quant_fp8, (x, False, False)),
+        (torch.ops.nq.layernorm_fp8_static, (x, g, b, 1e-5, sc, False)),
+        (torch.ops.nq.layernorm_fp8, (x, g, b, 1e-5, True)),
+        (torch.ops.nq.add_rmsnorm_nvfp4, (xs, rs, gs, 1e-6, gsc, False)),
+        (torch.ops.nq.rmsnorm_nvfp4, (xs, gs, 1e-6, gsc, True)),
+        (torch.ops.nq.add_rmsnorm_bf16, (x, r, g, 1e-6)),
+        (torch.ops.nq.per_token_quant_fp8, (x, False)),
+    ]
+    assert len(cases) == len(ops.OPS)
+    for op, args in cases:
+        torch.library.opcheck(op, args, test_utils=("test_schema", "test_faketensor", "test_aot_dispatch_static"))
+
+
+def _norm_linear(x, r, g, wt):
+    """A norm feeding an FP8 GEMM (dequantized here): the hand-off the
+    fusion targets ([FUSE] "Where norm+quant sits")."""
+    q, s, z = torch.ops.nq.add_rmsnorm_fp8(x, r, g, 1e-6, False)
+    y = q.to(torch.float32) * s[:, None]
+    return y @ wt, z
+
+
+@pytest.mark.gpu
+def test_compiled_graph_matches_eager_and_calls_the_kernel(ops):
+    w, x, r, g = _inputs(M=32)
+    wt = torch.randn(2816, 64, device="cuda", generator=torch.Generator(device="cuda").manual_seed(0))
+    eager, z = _norm_linear(x, r, g, wt)
+    compiled = torch.compile(_norm_linear, backend="aot_eager", fullgraph=True)
+    out, z2 = compiled(x, r, g, wt)
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager) and torch.equal(z2, z)
+    assert out.abs().sum() > 0
+    # Poisoned-kernel probe: with the op's GPU kernel replaced by one that
+    # returns zeros, the same compiled function must return zeros -- the
+    # graph calls the kernel when it runs.
+    real = ops.add_rmsnorm_fp8._init_fn
+    try:
+        ops.add_rmsnorm_fp8.register_kernel(
+            "cuda", lambda x, residual, gamma, eps, e5m2=False: (
+                torch.zeros(x.shape, dtype=torch.float8_e4m3fn, device=x.device),
+                torch.zeros(x.shape[0], device=x.device), torch.zeros_like(x)))
+        poisoned, _ = compiled(x, r, g, wt)
+        torch.cuda.synchronize()
+        assert poisoned.abs().sum() == 0
+    finally:
+        ops.add_rmsnorm_fp8.register_kernel("cuda", real)
+    again, _ = compiled(x, r, g, wt)
+    torch.cuda.synchronize()
+    assert torch.equal(again, eager)
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(600)
+def test_inductor_compiled_norm_linear(ops):
+    """Full inductor compilation (generated kernels around the custom op)."""
+    w, x, r, g = _inputs(M=32)
+    wt = torch.randn(2816, 64, device="cuda", generator=torch.Generator(device="cuda").manual_seed(1))
+    eager, z = _norm_linear(x, r, g, wt)
+    compiled = torch.compile(_norm_linear, fullgraph=True)
+    out, z2 = compiled(x, r, g, wt)
+    torch.cuda.synchronize()
+    assert torch.equal(z2, z)
+    torch.testing.assert_close(out, eager, rtol=1e-5, atol=1e-5)
