@@ -358,6 +358,12 @@ struct RowIO<true, POLICY, T> {
         const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off(i, live), 0, POLICY);
         return make_uint4(v.x, v.y, v.z, v.w);
     }
+    // 8 bytes starting at element i
+    __device__ __forceinline__ uint2 load8(int i, bool live) const
+    {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)off(i, live), 0, POLICY);
+        return make_uint2(v.x, v.y);
+    }
     __device__ __forceinline__ void store16(int i, bool live, uint4 w) const
     {
         const u32x4_t v = {w.x, w.y, w.z, w.w};
@@ -411,6 +417,14 @@ struct RowIO<false, POLICY, T> {
                 row[i + k] = v;
             }
         }
+    }
+    __device__ __forceinline__ uint2 load8(int i, bool live) const
+    {
+        uint8_t b[8];
+        load_bytes<8>(i, live, b);
+        uint2 w;
+        __builtin_memcpy(&w, b, 8);
+        return w;
     }
     __device__ __forceinline__ uint4 load16(int i, bool live) const
     {

@@ -20,8 +20,8 @@ namespace nq {
 
 struct LnFp8Args {
     const uint16_t* x;
-    const float* gamma;
-    const float* beta;
+    const void* gamma;      // fp32, or bf16 when vec_bf16
+    const void* beta;
     const float* scale;     // static per-tensor scale, or NULL: dynamic per-token
     uint8_t* q;
     float* scale_out;       // [M] per-token scales (dynamic only)
@@ -30,9 +30,10 @@ struct LnFp8Args {
     int d;
     float eps;
     bool e5m2;              // output format (e4m3 otherwise)
+    bool vec_bf16;          // gamma and beta are bf16
 };
 
-template <int TEAM, int CPL, bool VEC, bool STAGE, Fp8 F = Fp8::E4M3, bool DYN = false,
+template <int TEAM, int CPL, bool VEC, bool STAGE, Fp8 F = Fp8::E4M3, bool DYN = false, bool GB = false,
           int BLOCK = row_block<TEAM, CPL, 2, VEC, STAGE>()>
 __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
 {
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
     const RowMap m = row_map<TEAM, BLOCK>(a.M);
     const int d = a.d;
     const RowIO<VEC, kLoadStream, uint16_t> xio(a.x, a.ld_x, m, d);
-    using SV = SharedVectors<TEAM, CPL, VEC, 2, BLOCK, STAGE>;
+    using SV = SharedVectors<TEAM, CPL, VEC, 2, BLOCK, STAGE, GB>;
     __shared__ typename SV::Lds lds_gb;
     SV gb({a.gamma, a.beta}, d);
     const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d);
@@ -159,13 +160,19 @@ struct LnFp8Kernel {
     template <bool STAGE>
     static void launch(const LnFp8Args& a, dim3 grid, dim3 block, hipStream_t s)
     {
+        if (a.vec_bf16) go<STAGE, true>(a, grid, block, s);
+        else go<STAGE, false>(a, grid, block, s);
+    }
+    template <bool STAGE, bool GB>
+    static void go(const LnFp8Args& a, dim3 grid, dim3 block, hipStream_t s)
+    {
         const bool dyn = a.scale == nullptr;
         if (a.e5m2) {
-            if (dyn) hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2, true>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2, false>), grid, block, 0, s, a);
+            if (dyn) hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2, true, GB>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2, false, GB>), grid, block, 0, s, a);
         } else {
-            if (dyn) hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3, true>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3, false>), grid, block, 0, s, a);
+            if (dyn) hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3, true, GB>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_layernorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3, false, GB>), grid, block, 0, s, a);
         }
     }
 };
@@ -176,13 +183,14 @@ using namespace nq;
 
 extern "C" nq_status nq_layernorm_quant_fp8_ex(
     const uint16_t* x, int64_t ld_x,
-    const float* gamma, const float* beta, float eps,
+    const void* gamma, const void* beta, float eps,
     const float* scale, uint32_t flags,
     uint8_t* q_out, int64_t ld_q,
     float* scale_out,
     int64_t M, int64_t d, void* stream)
 {
-    if ((flags & ~(uint32_t)NQ_FLAG_E5M2) != 0) return NQ_ERR_ARG;
+    if ((flags & ~(uint32_t)(NQ_FLAG_E5M2 | NQ_FLAG_GAMMA_BF16)) != 0) return NQ_ERR_ARG;
+    const int64_t gsz = (flags & NQ_FLAG_GAMMA_BF16) ? 2 : 4;
     if (M < 0 || d <= 0 || d > NQ_MAX_D || M > kMaxRows) return NQ_ERR_SHAPE;
     if (!(eps >= 0.0f) || eps > 1e30f) return NQ_ERR_ARG;
     if (bad_ld(ld_x, d) || bad_ld(ld_q, d)) return NQ_ERR_STRIDE;
@@ -190,8 +198,8 @@ extern "C" nq_status nq_layernorm_quant_fp8_ex(
     if (!x || !gamma || !beta || !q_out) return NQ_ERR_NULL;
     if (!scale && !scale_out) return NQ_ERR_NULL;  // dynamic scales need somewhere to go
 
-    const Region in[] = {region(x, M, ld_x, d, 2), region(gamma, 1, d, d, 4),
-                         region(beta, 1, d, d, 4), region(scale, 1, 1, 1, 4)};
+    const Region in[] = {region(x, M, ld_x, d, 2), region(gamma, 1, d, d, gsz),
+                         region(beta, 1, d, d, gsz), region(scale, 1, 1, 1, 4)};
     const Region out[] = {region(q_out, M, ld_q, d, 1), region(scale ? nullptr : scale_out, 1, M, M, 4)};
     if (any_alias(in, out)) return NQ_ERR_ALIAS;
 
@@ -205,6 +213,7 @@ extern "C" nq_status nq_layernorm_quant_fp8_ex(
     a.scale_out = scale ? nullptr : scale_out;
     a.ld_x = ld_x; a.ld_q = ld_q; a.M = M; a.d = (int)d; a.eps = eps;
     a.e5m2 = (flags & NQ_FLAG_E5M2) != 0;
+    a.vec_bf16 = (flags & NQ_FLAG_GAMMA_BF16) != 0;
     if (!launch_row_shape<LnFp8Kernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
 }

@@ -29,7 +29,7 @@ struct RmsFp8Args {
     const uint16_t* x;
     const uint16_t* r;      // NULL: residual-less
     uint16_t* ro;           // residual_out (NULL iff r is NULL)
-    const float* gamma;
+    const void* gamma;      // fp32, or bf16 when gamma_bf16
     const float* static_scale;  // NULL: dynamic per-token scale
     uint8_t* q;
     float* scale_out;
@@ -39,9 +39,10 @@ struct RmsFp8Args {
     int d;
     float eps;
     bool e5m2;              // output format (e4m3 otherwise)
+    bool gamma_bf16;
 };
 
-template <int TEAM, int CPL, bool VEC, bool STAGE, Fp8 F = Fp8::E4M3,
+template <int TEAM, int CPL, bool VEC, bool STAGE, Fp8 F = Fp8::E4M3, bool GB = false,
           int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
 __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
 {
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
     const int t = threadIdx.x % TEAM;
     const RowMap m = row_map<TEAM, BLOCK>(a.M);
     const int d = a.d;
-    using SV = SharedVectors<TEAM, CPL, VEC, 1, BLOCK, STAGE>;
+    using SV = SharedVectors<TEAM, CPL, VEC, 1, BLOCK, STAGE, GB>;
     __shared__ typename SV::Lds lds_gamma;
     SV gamma({a.gamma}, d);
 
@@ -126,8 +127,13 @@ struct RmsFp8Kernel {
     template <bool STAGE>
     static void launch(const RmsFp8Args& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3>), grid, block, 0, s, a);
+        if (a.gamma_bf16) {
+            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3, true>), grid, block, 0, s, a);
+        } else {
+            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2, false>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3, false>), grid, block, 0, s, a);
+        }
     }
 };
 
@@ -139,14 +145,15 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_ex(
     const uint16_t* x, int64_t ld_x,
     const uint16_t* residual_in, int64_t ld_r,
     uint16_t* residual_out, int64_t ld_ro,
-    const float* gamma, float eps,
+    const void* gamma, float eps,
     const float* static_scale, uint32_t flags,
     uint8_t* q_out, int64_t ld_q,
     float* scale_out,
     uint16_t* norm_out, int64_t ld_n,
     int64_t M, int64_t d, void* stream)
 {
-    if ((flags & ~(uint32_t)NQ_FLAG_E5M2) != 0) return NQ_ERR_ARG;
+    if ((flags & ~(uint32_t)(NQ_FLAG_E5M2 | NQ_FLAG_GAMMA_BF16)) != 0) return NQ_ERR_ARG;
+    const int64_t gsz = (flags & NQ_FLAG_GAMMA_BF16) ? 2 : 4;
     if (M < 0 || d <= 0 || d > NQ_MAX_D || M > kMaxRows) return NQ_ERR_SHAPE;
     if (!(eps >= 0.0f) || eps > 1e30f) return NQ_ERR_ARG;
     if (bad_ld(ld_x, d) || bad_ld(ld_q, d)) return NQ_ERR_STRIDE;
@@ -158,7 +165,7 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_ex(
     if ((residual_in == nullptr) != (residual_out == nullptr)) return NQ_ERR_NULL;
 
     const Region in[] = {region(x, M, ld_x, d, 2), region(residual_in, M, ld_r, d, 2),
-                         region(gamma, 1, d, d, 4), region(static_scale, 1, 1, 1, 4)};
+                         region(gamma, 1, d, d, gsz), region(static_scale, 1, 1, 1, 4)};
     const Region out[] = {region(residual_out, M, ld_ro, d, 2), region(q_out, M, ld_q, d, 1),
                           region(static_scale ? nullptr : scale_out, 1, M, M, 4),
                           region(norm_out, M, ld_n, d, 2)};
@@ -181,6 +188,7 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_ex(
     a.ld_x = ld_x; a.ld_r = ld_r; a.ld_ro = ld_ro; a.ld_q = ld_q; a.ld_n = ld_n;
     a.M = M; a.d = (int)d; a.eps = eps;
     a.e5m2 = (flags & NQ_FLAG_E5M2) != 0;
+    a.gamma_bf16 = (flags & NQ_FLAG_GAMMA_BF16) != 0;
     if (!launch_row_shape<RmsFp8Kernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
 }

@@ -28,7 +28,7 @@ struct RmsGroupArgs {
     const uint16_t* x;
     const uint16_t* r;      // NULL: residual-less
     uint16_t* ro;           // NULL iff r is NULL
-    const float* gamma;
+    const void* gamma;      // fp32, or bf16 when gamma_bf16
     uint8_t* q;
     float* scale_out;       // [M, d / 128], row stride ld_s
     uint16_t* norm_out;     // optional
@@ -39,9 +39,10 @@ struct RmsGroupArgs {
     int ue8m0;              // scales rounded up to powers of two
     int bf16_source;        // quantize bf16(y) (the unfused pipeline's values)
     bool e5m2;              // output format (e4m3 otherwise)
+    bool gamma_bf16;
 };
 
-template <int TEAM, int CPL, bool VEC, bool STAGE, Fp8 F = Fp8::E4M3,
+template <int TEAM, int CPL, bool VEC, bool STAGE, Fp8 F = Fp8::E4M3, bool GB = false,
           int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
 __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8_group(RmsGroupArgs a)
 {
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8_group(RmsGroupArgs a)
     const int t = threadIdx.x % TEAM;
     const RowMap m = row_map<TEAM, BLOCK>(a.M);
     const int d = a.d;
-    using SV = SharedVectors<TEAM, CPL, VEC, 1, BLOCK, STAGE>;
+    using SV = SharedVectors<TEAM, CPL, VEC, 1, BLOCK, STAGE, GB>;
     __shared__ typename SV::Lds lds_gamma;
     SV gamma({a.gamma}, d);
 
@@ -106,8 +107,13 @@ struct RmsGroupKernel {
     template <bool STAGE>
     static void launch(const RmsGroupArgs& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E5M2>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E4M3>), grid, block, 0, s, a);
+        if (a.gamma_bf16) {
+            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E5M2, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E4M3, true>), grid, block, 0, s, a);
+        } else {
+            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E5M2, false>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E4M3, false>), grid, block, 0, s, a);
+        }
     }
 };
 
@@ -119,7 +125,7 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_group(
     const uint16_t* x, int64_t ld_x,
     const uint16_t* residual_in, int64_t ld_r,
     uint16_t* residual_out, int64_t ld_ro,
-    const float* gamma, float eps,
+    const void* gamma, float eps,
     int32_t group_size, int32_t scale_mode, uint32_t flags,
     uint8_t* q_out, int64_t ld_q,
     float* scale_out, int64_t ld_s,
@@ -128,7 +134,8 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_group(
 {
     if (group_size != kRowGroup) return NQ_ERR_ARG;
     if (scale_mode != NQ_SCALE_FP32 && scale_mode != NQ_SCALE_UE8M0) return NQ_ERR_ARG;
-    if ((flags & ~(uint32_t)(NQ_FLAG_BF16_SOURCE | NQ_FLAG_E5M2)) != 0) return NQ_ERR_ARG;
+    if ((flags & ~(uint32_t)(NQ_FLAG_BF16_SOURCE | NQ_FLAG_E5M2 | NQ_FLAG_GAMMA_BF16)) != 0) return NQ_ERR_ARG;
+    const int64_t gsz = (flags & NQ_FLAG_GAMMA_BF16) ? 2 : 4;
     if (M < 0 || d <= 0 || d > NQ_MAX_D || d % group_size != 0 || M > kMaxRows) return NQ_ERR_SHAPE;
     if (!(eps >= 0.0f) || eps > 1e30f) return NQ_ERR_ARG;
     const int64_t G = d / group_size;
@@ -140,7 +147,7 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_group(
     if ((residual_in == nullptr) != (residual_out == nullptr)) return NQ_ERR_NULL;
 
     const Region in[] = {region(x, M, ld_x, d, 2), region(residual_in, M, ld_r, d, 2),
-                         region(gamma, 1, d, d, 4)};
+                         region(gamma, 1, d, d, gsz)};
     const Region out[] = {region(residual_out, M, ld_ro, d, 2), region(q_out, M, ld_q, d, 1),
                           region(scale_out, M, ld_s, G, 4), region(norm_out, M, ld_n, d, 2)};
     if (any_alias(in, out, /*exact_in=*/1, /*exact_out=*/0)) return NQ_ERR_ALIAS;
@@ -163,6 +170,7 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_group(
     a.ue8m0 = scale_mode == NQ_SCALE_UE8M0;
     a.bf16_source = (flags & NQ_FLAG_BF16_SOURCE) != 0;
     a.e5m2 = (flags & NQ_FLAG_E5M2) != 0;
+    a.gamma_bf16 = (flags & NQ_FLAG_GAMMA_BF16) != 0;
     if (!launch_row_shape<RmsGroupKernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
 }

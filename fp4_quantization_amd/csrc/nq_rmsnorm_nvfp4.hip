@@ -29,7 +29,7 @@ struct RmsFp4Args {
     const uint16_t* x;
     const uint16_t* r;
     uint16_t* ro;
-    const float* gamma;
+    const void* gamma;      // fp32, or bf16 when gamma_bf16
     const float* global_scale;
     uint8_t* q;        // [M, d/2]
     uint8_t* sf;       // [M, d/16]
@@ -39,10 +39,11 @@ struct RmsFp4Args {
     int d;
     float eps;
     bool bf16_source;  // quantize bf16(y): the standalone quantizer applied to norm_out
+    bool gamma_bf16;
 };
 
 // VEC additionally needs 4-byte aligned packed-code rows (one dword per chunk).
-template <int TEAM, int CPL, bool VEC, bool STAGE, int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
+template <int TEAM, int CPL, bool VEC, bool STAGE, bool GB = false, int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
 __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
 {
     using S = TeamShape<TEAM, BLOCK>;
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
     const int t = threadIdx.x % TEAM;
     const RowMap m = row_map<TEAM, BLOCK>(a.M);
     const int d = a.d;
-    using SV = SharedVectors<TEAM, CPL, VEC, 1, BLOCK, STAGE>;
+    using SV = SharedVectors<TEAM, CPL, VEC, 1, BLOCK, STAGE, GB>;
     __shared__ typename SV::Lds lds_gamma;
     SV gamma({a.gamma}, d);
 
@@ -110,7 +111,8 @@ struct RmsFp4Kernel {
     template <bool STAGE>
     static void launch(const RmsFp4Args& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        hipLaunchKernelGGL((k_add_rmsnorm_nvfp4<TEAM, CPL, VEC, STAGE>), grid, block, 0, s, a);
+        if (a.gamma_bf16) hipLaunchKernelGGL((k_add_rmsnorm_nvfp4<TEAM, CPL, VEC, STAGE, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_add_rmsnorm_nvfp4<TEAM, CPL, VEC, STAGE, false>), grid, block, 0, s, a);
     }
 };
 
@@ -122,14 +124,15 @@ extern "C" nq_status nq_rmsnorm_quant_nvfp4_ex(
     const uint16_t* x, int64_t ld_x,
     const uint16_t* residual_in, int64_t ld_r,
     uint16_t* residual_out, int64_t ld_ro,
-    const float* gamma, float eps,
+    const void* gamma, float eps,
     const float* global_scale, uint32_t flags,
     uint8_t* q_packed, int64_t ld_q,
     uint8_t* block_scale, int64_t ld_sf,
     uint16_t* norm_out, int64_t ld_n,
     int64_t M, int64_t d, void* stream)
 {
-    if ((flags & ~(uint32_t)NQ_FLAG_BF16_SOURCE) != 0) return NQ_ERR_ARG;
+    if ((flags & ~(uint32_t)(NQ_FLAG_BF16_SOURCE | NQ_FLAG_GAMMA_BF16)) != 0) return NQ_ERR_ARG;
+    const int64_t gsz = (flags & NQ_FLAG_GAMMA_BF16) ? 2 : 4;
     if (M < 0 || d <= 0 || d > NQ_MAX_D || d % 16 != 0 || M > kMaxRows) return NQ_ERR_SHAPE;
     if (!(eps >= 0.0f) || eps > 1e30f) return NQ_ERR_ARG;
     if (bad_ld(ld_x, d) || bad_ld(ld_q, d / 2) || bad_ld(ld_sf, d / 16)) return NQ_ERR_STRIDE;
@@ -140,7 +143,7 @@ extern "C" nq_status nq_rmsnorm_quant_nvfp4_ex(
     if ((residual_in == nullptr) != (residual_out == nullptr)) return NQ_ERR_NULL;
 
     const Region in[] = {region(x, M, ld_x, d, 2), region(residual_in, M, ld_r, d, 2),
-                         region(gamma, 1, d, d, 4), region(global_scale, 1, 1, 1, 4)};
+                         region(gamma, 1, d, d, gsz), region(global_scale, 1, 1, 1, 4)};
     const Region out[] = {region(residual_out, M, ld_ro, d, 2), region(q_packed, M, ld_q, d / 2, 1),
                           region(block_scale, M, ld_sf, d / 16, 1), region(norm_out, M, ld_n, d, 2)};
     if (any_alias(in, out, /*exact_in=*/1, /*exact_out=*/0)) return NQ_ERR_ALIAS;
@@ -161,6 +164,7 @@ extern "C" nq_status nq_rmsnorm_quant_nvfp4_ex(
     a.ld_x = ld_x; a.ld_r = ld_r; a.ld_ro = ld_ro; a.ld_q = ld_q; a.ld_sf = ld_sf; a.ld_n = ld_n;
     a.M = M; a.d = (int)d; a.eps = eps;
     a.bf16_source = (flags & NQ_FLAG_BF16_SOURCE) != 0;
+    a.gamma_bf16 = (flags & NQ_FLAG_GAMMA_BF16) != 0;
     if (!launch_row_shape<RmsFp4Kernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
 }

@@ -115,22 +115,27 @@ constexpr int row_block()
     return default_block<TEAM>();
 }
 
-template <int TEAM, int CPL, bool VEC, int NV, int BLOCK, bool STAGE>
+template <int TEAM, int CPL, bool VEC, int NV, int BLOCK, bool STAGE, bool BF16 = false>
 class SharedVectors {
   public:
     using S = TeamShape<TEAM, BLOCK>;
-    static constexpr int kSlots = TEAM * CPL * 2;  // 16-byte slots covering one row's chunks
+    static constexpr int kSlots = TEAM * CPL * 2;  // 16-byte fp32 slots covering one row's chunks
     static constexpr bool kStaged = STAGE && VEC && stages_vectors(TEAM, CPL, NV, BLOCK);
     static constexpr int kPer = kStaged ? (kSlots + S::kBlock - 1) / S::kBlock : 1;
     typedef uint4 Lds[kStaged ? NV : 1][kStaged ? kSlots : 1];
     static_assert(!kStaged || kSlots * 16 * NV <= 64 * 1024, "staged vectors fit one block's LDS");
 
-    __device__ __forceinline__ SharedVectors(const float* const (&p)[NV], int d) : d_(d)
+    // The vectors are fp32 or (BF16) bf16; both are read through a
+    // 2-byte-element view, so element e of an fp32 vector starts at 2e.
+    __device__ __forceinline__ SharedVectors(const void* const (&p)[NV], int d) : d_(d)
     {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) io_[v] = RowIO<VEC, kKeep, float>(p[v], d, vector_map(), d);
+        for (int v = 0; v < NV; ++v)
+            io_[v] = RowIO<VEC, kKeep, uint16_t>(static_cast<const uint16_t*>(p[v]), 0, vector_map(),
+                                                 BF16 ? d : 2 * d);
     }
-    // Issue the cooperative loads (staged only).
+    // Issue the cooperative loads (staged only): fp32 slot i holds elements
+    // 4i .. 4i+3, loaded as 16 bytes, or as 8 bytes of bf16 widened at publish.
     __device__ __forceinline__ void issue()
     {
         if constexpr (kStaged) {
@@ -139,11 +144,16 @@ class SharedVectors {
 #pragma unroll
                 for (int u = 0; u < kPer; ++u) {
                     const int i = u * S::kBlock + (int)threadIdx.x;
-                    held_[v][u] = io_[v].load16(i * 4, i * 4 < d_);
+                    if constexpr (BF16) {
+                        const uint2 h = io_[v].load8(i * 4, i * 4 < d_);
+                        held_[v][u] = make_uint4(h.x, h.y, 0u, 0u);
+                    } else {
+                        held_[v][u] = io_[v].load16(i * 8, i * 4 < d_);
+                    }
                 }
         }
     }
-    // Write the staged vectors to LDS (staged only; before the first
+    // Write the staged vectors to LDS as fp32 (staged only; before the first
     // reduction, which every lane of the block reaches).
     __device__ __forceinline__ void publish(Lds& lds)
     {
@@ -153,7 +163,9 @@ class SharedVectors {
 #pragma unroll
                 for (int u = 0; u < kPer; ++u) {
                     const int i = u * S::kBlock + (int)threadIdx.x;
-                    if (i < kSlots) lds[v][i] = held_[v][u];
+                    uint4 w = held_[v][u];
+                    if constexpr (BF16) w = make_uint4(w.x << 16, w.x & 0xFFFF0000u, w.y << 16, w.y & 0xFFFF0000u);
+                    if (i < kSlots) lds[v][i] = w;
                 }
             if constexpr (TEAM <= kWave) __syncthreads();
         }
@@ -167,13 +179,19 @@ class SharedVectors {
             g[2] = __uint_as_float(a.z); g[3] = __uint_as_float(a.w);
             g[4] = __uint_as_float(b.x); g[5] = __uint_as_float(b.y);
             g[6] = __uint_as_float(b.z); g[7] = __uint_as_float(b.w);
+        } else if constexpr (BF16) {
+            unpack_bf16x8(io_[v].load16(e, e < d_), g);
         } else {
-            load_f32x8(io_[v], e, e < d_, g);
+            const uint4 a = io_[v].load16(2 * e, e < d_), b = io_[v].load16(2 * e + 8, e < d_);
+            g[0] = __uint_as_float(a.x); g[1] = __uint_as_float(a.y);
+            g[2] = __uint_as_float(a.z); g[3] = __uint_as_float(a.w);
+            g[4] = __uint_as_float(b.x); g[5] = __uint_as_float(b.y);
+            g[6] = __uint_as_float(b.z); g[7] = __uint_as_float(b.w);
         }
     }
 
   private:
-    RowIO<VEC, kKeep, float> io_[NV];
+    RowIO<VEC, kKeep, uint16_t> io_[NV];
     uint4 held_[kStaged ? NV : 1][kPer];
     int d_;
 };

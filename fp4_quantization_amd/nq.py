@@ -67,6 +67,7 @@ NQ_SCALE_FP32 = 0
 NQ_SCALE_UE8M0 = 1
 NQ_FLAG_BF16_SOURCE = 1
 NQ_FLAG_E5M2 = 2
+NQ_FLAG_GAMMA_BF16 = 4
 NQ_CODEC_E4M3 = 0
 NQ_CODEC_E2M1 = 1
 NQ_CODEC_BF16 = 2
@@ -133,6 +134,16 @@ def _vec(t: torch.Tensor | None, dtype, name: str, n: int | None = None):
     return t.data_ptr()
 
 
+def _gvec(*ts, n: int, names=("gamma", "beta")):
+    """Pointers of the per-row vectors (gamma, beta) and the flag bit for
+    their dtype: all fp32, or all bf16 (NQ_FLAG_GAMMA_BF16)."""
+    dt = ts[0].dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"{names[0]}: dtype {dt}, expected float32 or bfloat16")
+    ptrs = tuple(_vec(t, dt, nm, n) for t, nm in zip(ts, names))
+    return ptrs, (NQ_FLAG_GAMMA_BF16 if dt == torch.bfloat16 else 0)
+
+
 def _check(status: int, where: str):
     if status != NQ_OK:
         raise NQError(status, where)
@@ -179,9 +190,10 @@ def nq_fused_add_rmsnorm_quant_fp8_group(x, residual_in, residual_out, gamma, ep
                  (scale_out, "scale_out"), (norm_out, "norm_out")):
         if t is not None and t.size(0) != M:
             raise ValueError(f"{n}: expected {M} rows")
+    (pg,), gf = _gvec(gamma, n=d)
     st = _lib.nq_fused_add_rmsnorm_quant_fp8_group(
-        px, ldx, pr, ldr, pro, ldro, _vec(gamma, torch.float32, "gamma", d), float(eps),
-        int(group_size), int(scale_mode), int(flags), pq, ldq, ps, lds, pn, ldn, M, d, _stream(stream))
+        px, ldx, pr, ldr, pro, ldro, pg, float(eps),
+        int(group_size), int(scale_mode), int(flags) | gf, pq, ldq, ps, lds, pn, ldn, M, d, _stream(stream))
     _check(st, "nq_fused_add_rmsnorm_quant_fp8_group")
 
 
@@ -198,9 +210,10 @@ def nq_fused_add_rmsnorm_quant_fp8_ex(x, residual_in, residual_out, gamma, eps, 
                  (norm_out, "norm_out")):
         if t is not None and t.size(0) != M:
             raise ValueError(f"{n}: expected {M} rows")
+    (pg,), gf = _gvec(gamma, n=d)
     st = _lib.nq_fused_add_rmsnorm_quant_fp8_ex(
-        px, ldx, pr, ldr, pro, ldro, _vec(gamma, torch.float32, "gamma", d), float(eps),
-        _vec(static_scale, torch.float32, "static_scale", 1), int(flags), pq, ldq,
+        px, ldx, pr, ldr, pro, ldro, pg, float(eps),
+        _vec(static_scale, torch.float32, "static_scale", 1), int(flags) | gf, pq, ldq,
         _vec(scale_out, torch.float32, "scale_out", M if static_scale is None else None),
         pn, ldn, M, d, _stream(stream))
     _check(st, "nq_fused_add_rmsnorm_quant_fp8_ex")
@@ -214,9 +227,9 @@ def nq_layernorm_quant_fp8_ex(x, gamma, beta, eps, scale, flags, q_out, scale_ou
     pq, ldq = _mat(q_out, _CODES8, "q_out", d)
     if q_out.size(0) != M:
         raise ValueError(f"q_out: expected {M} rows")
+    (pg, pb), gf = _gvec(gamma, beta, n=d)
     st = _lib.nq_layernorm_quant_fp8_ex(
-        px, ldx, _vec(gamma, torch.float32, "gamma", d), _vec(beta, torch.float32, "beta", d),
-        float(eps), _vec(scale, torch.float32, "scale", 1), int(flags), pq, ldq,
+        px, ldx, pg, pb, float(eps), _vec(scale, torch.float32, "scale", 1), int(flags) | gf, pq, ldq,
         _vec(scale_out, torch.float32, "scale_out", M if scale is None else None), M, d, _stream(stream))
     _check(st, "nq_layernorm_quant_fp8_ex")
 
@@ -291,9 +304,10 @@ def nq_rmsnorm_quant_nvfp4_ex(x, residual_in, residual_out, gamma, eps, global_s
     pq, ldq = _mat(q_packed, (torch.uint8,), "q_packed", d // 2)
     psf, ldsf = _mat(block_scale, _CODES8, "block_scale", d // 16)
     pn, ldn = _mat(norm_out, _BF16, "norm_out", d)
+    (pg,), gf = _gvec(gamma, n=d)
     st = _lib.nq_rmsnorm_quant_nvfp4_ex(
-        px, ldx, pr, ldr, pro, ldro, _vec(gamma, torch.float32, "gamma", d), float(eps),
-        _vec(global_scale, torch.float32, "global_scale", 1), int(flags), pq, ldq, psf, ldsf, pn, ldn,
+        px, ldx, pr, ldr, pro, ldro, pg, float(eps),
+        _vec(global_scale, torch.float32, "global_scale", 1), int(flags) | gf, pq, ldq, psf, ldsf, pn, ldn,
         M, d, _stream(stream))
     _check(st, "nq_rmsnorm_quant_nvfp4_ex")
 

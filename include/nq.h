@@ -74,6 +74,10 @@ typedef int nq_status;
 #define NQ_FLAG_BF16_SOURCE 1u  /* quantize bf16(y) instead of the fp32 y */
 #define NQ_FLAG_E5M2 2u         /* FP8 codes in OCP e5m2 (largest finite 57344) instead of e4m3:
                                    dynamic scales divide by 57344, e5m2() clamps to +-57344 */
+#define NQ_FLAG_GAMMA_BF16 4u   /* gamma (and beta) are bf16 [d] instead of fp32: each value is
+                                   widened exactly, so the results equal those of the fp32 vector
+                                   holding the same values (16-byte alignment still selects the
+                                   vector path) */
 
 /*
  * Fused (residual-add +) RMSNorm + per-token FP8 e4m3.
@@ -117,15 +121,16 @@ nq_status nq_fused_add_rmsnorm_quant_fp8(
 
 /*
  * The same op with an output-format choice ([LNQ] "Description" and "Tests":
- * the FP8 output may be e4m3 or e5m2).  flags: 0 or NQ_FLAG_E5M2 (NQ_ERR_ARG
- * for other bits); every other argument as above.  With NQ_FLAG_E5M2 the
+ * the FP8 output may be e4m3 or e5m2).  flags: any of NQ_FLAG_E5M2,
+ * NQ_FLAG_GAMMA_BF16 (NQ_ERR_ARG for other bits); every other argument as
+ * above (gamma fp32, or bf16 with NQ_FLAG_GAMMA_BF16).  With NQ_FLAG_E5M2 the
  * dynamic scale is max_i |y_i| / 57344 and codes are e5m2.
  */
 nq_status nq_fused_add_rmsnorm_quant_fp8_ex(
     const uint16_t* x, int64_t ld_x,
     const uint16_t* residual_in, int64_t ld_r,
     uint16_t* residual_out, int64_t ld_ro,
-    const float* gamma, float eps,
+    const void* gamma, float eps,
     const float* static_scale, uint32_t flags,
     uint8_t* q_out, int64_t ld_q,
     float* scale_out,
@@ -169,12 +174,13 @@ nq_status nq_layernorm_quant_fp8(
  *                            q_i = fp8(y_i / s)  (one correctly rounded
  *                            quotient per element; 0 when s == 0)
  *   fmax = 448 (e4m3) or 57344 (NQ_FLAG_E5M2)
- *   flags      0 or NQ_FLAG_E5M2 (NQ_ERR_ARG for other bits)
+ *   flags      any of NQ_FLAG_E5M2, NQ_FLAG_GAMMA_BF16 (gamma and beta bf16);
+ *              NQ_ERR_ARG for other bits
  *   scale_out  [M] fp32, required when scale is NULL
  */
 nq_status nq_layernorm_quant_fp8_ex(
     const uint16_t* x, int64_t ld_x,
-    const float* gamma, const float* beta, float eps,
+    const void* gamma, const void* beta, float eps,
     const float* scale, uint32_t flags,
     uint8_t* q_out, int64_t ld_q,
     float* scale_out,
@@ -242,7 +248,8 @@ nq_status nq_per_token_group_quant_fp8_ex(
  *   group_size   128 (NQ_ERR_ARG otherwise); d % group_size == 0
  *   scale_mode   NQ_SCALE_FP32 or NQ_SCALE_UE8M0 (NQ_ERR_ARG otherwise)
  *   flags        any of NQ_FLAG_BF16_SOURCE, NQ_FLAG_E5M2 (then 448 above is
- *                57344 and the codes are e5m2); NQ_ERR_ARG for other bits
+ *                57344 and the codes are e5m2), NQ_FLAG_GAMMA_BF16 (gamma is
+ *                bf16); NQ_ERR_ARG for other bits
  *   q_out        [M, d] e4m3 codes, row stride ld_q
  *   scale_out    [M, d / group_size] fp32, row stride ld_s (>= d / group_size)
  *   norm_out     [M, d] bf16, row stride ld_n, or NULL
@@ -251,7 +258,7 @@ nq_status nq_fused_add_rmsnorm_quant_fp8_group(
     const uint16_t* x, int64_t ld_x,
     const uint16_t* residual_in, int64_t ld_r,
     uint16_t* residual_out, int64_t ld_ro,
-    const float* gamma, float eps,
+    const void* gamma, float eps,
     int32_t group_size, int32_t scale_mode, uint32_t flags,
     uint8_t* q_out, int64_t ld_q,
     float* scale_out, int64_t ld_s,
@@ -296,17 +303,17 @@ nq_status nq_rmsnorm_quant_nvfp4(
     int64_t M, int64_t d, void* stream);
 
 /*
- * The same NVFP4 op with an option: flags 0 or NQ_FLAG_BF16_SOURCE (the
+ * The same NVFP4 op with options: flags any of NQ_FLAG_BF16_SOURCE (the
  * values quantized are bf16(y_i), so the codes and block scales equal the
  * standalone quantizer applied to the bf16 norm_out -- [NVFP4] commit notes:
  * re-quantizing the fused op's own norm_out reproduces its outputs bit for
- * bit).  NQ_ERR_ARG for other bits.
+ * bit), NQ_FLAG_GAMMA_BF16 (gamma is bf16).  NQ_ERR_ARG for other bits.
  */
 nq_status nq_rmsnorm_quant_nvfp4_ex(
     const uint16_t* x, int64_t ld_x,
     const uint16_t* residual_in, int64_t ld_r,
     uint16_t* residual_out, int64_t ld_ro,
-    const float* gamma, float eps,
+    const void* gamma, float eps,
     const float* global_scale, uint32_t flags,
     uint8_t* q_packed, int64_t ld_q,
     uint8_t* block_scale, int64_t ld_sf,

@@ -137,7 +137,7 @@ def test_rmsnorm_fp8_group_validation(lib):
     assert call(M=0, ro=R, mode=1, flags=1) == NQ_OK
     assert call(gs=64) == NQ_ERR_ARG
     assert call(mode=2) == NQ_ERR_ARG
-    assert call(flags=4) == NQ_ERR_ARG         # unknown bit
+    assert call(flags=0x100) == NQ_ERR_ARG     # unknown bit
     assert call(eps=-1.0) == NQ_ERR_ARG
     assert call(d=2800, ld_x=2800, ld_r=2800, ld_ro=2800, ld_q=2800) == NQ_ERR_SHAPE  # d % 128
     assert call(ld_s=21) == NQ_ERR_STRIDE
@@ -184,7 +184,7 @@ def test_ex_entry_points_validation(lib):
         k.get("sc", SC), None, 0, k.get("M", 4), 256, None)
     assert rms(M=0, flags=2) == NQ_OK
     assert rms(flags=1) == NQ_ERR_ARG          # the bf16-source bit is not an option here
-    assert rms(flags=6) == NQ_ERR_ARG
+    assert rms(flags=0x102) == NQ_ERR_ARG       # unknown bit
     assert rms(flags=2, sc=None) == NQ_ERR_NULL
     assert rms(flags=2, q=X) == NQ_ERR_ALIAS
     ln = lambda **k: lib.nq_layernorm_quant_fp8_ex(
@@ -192,7 +192,7 @@ def test_ex_entry_points_validation(lib):
         k.get("M", 2), 512, None)
     assert ln(M=0) == NQ_OK
     assert ln(M=0, flags=2, s=S) == NQ_OK
-    assert ln(flags=8) == NQ_ERR_ARG
+    assert ln(flags=0x100) == NQ_ERR_ARG
     assert ln(so=None) == NQ_ERR_NULL          # dynamic without scale_out
     assert ln(so=Q + 16) == NQ_ERR_ALIAS       # scale_out over the codes
     assert ln(so=G + 4) == NQ_ERR_ALIAS        # scale_out over gamma

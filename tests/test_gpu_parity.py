@@ -836,3 +836,84 @@ def test_fused_vs_unfused_on_gpu(nq, orc):
     y = orc.fused_add_rmsnorm_quant_fp8(w["x"], w["residual"], w["gamma"], w["eps"], want_y=True)["y"]
     ev = lambda q, s: np.abs(orc.e4m3_decode(q).astype(np.float64) * s[:, None] - y).sum()
     assert ev(fused["q"], fused["scale"]) < ev(unf["q"], unf["scale"])
+
+
+# ------------------------------------------------------- bf16 gamma / beta ----
+# NQ_FLAG_GAMMA_BF16: gamma (and beta) as bf16 vectors.  Widening is exact,
+# so the oracle takes the same values as fp32 and the results must agree bit
+# for bit, on the staged (many rows), per-lane (few rows) and element-wise
+# paths.
+
+def _bf16_vec(v):
+    bits = W.to_bf16_bits(np.asarray(v, np.float32))
+    return bits, W.bf16_bits_to_f32(bits), to_dev_bf16(bits)
+
+
+@pytest.mark.parametrize("M", [3, 1101])
+@pytest.mark.parametrize("d", [2816, 7168, 111])
+def test_bf16_gamma_rmsnorm_fp8(nq, orc, M, d):
+    note(f"bf16 gamma rms fp8 d={d} M={M}")
+    w = W.rms_rows(M, d, 2, 20.0, seed=d + M)
+    _, g32, gdev = _bf16_vec(w["gamma"])
+    x, r = to_dev_bf16(w["x"]), to_dev_bf16(w["residual"])
+    ro = torch.empty_like(r)
+    q = torch.empty(M, d, dtype=torch.uint8, device="cuda")
+    s = torch.empty(M, dtype=torch.float32, device="cuda")
+    nq.nq_fused_add_rmsnorm_quant_fp8_ex(x, r, ro, gdev, w["eps"], None, 0, q, s)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 32)
+    o = orc.fused_add_rmsnorm_quant_fp8(w["x"][rows], w["residual"][rows], g32, w["eps"])
+    assert_bits_equal(host_u16(ro)[rows], o["residual_out"], "residual_out")
+    assert_scales(s.cpu().numpy()[rows], o["scale"], "scale")
+    assert_codes(host_u8(q)[rows], o["q"], "q")
+    # and it is the fp32-gamma call on the widened values, bit for bit
+    q2 = torch.empty_like(q)
+    s2 = torch.empty_like(s)
+    nq.nq_fused_add_rmsnorm_quant_fp8_ex(x, r, torch.empty_like(r), to_dev_f32(g32), w["eps"], None, 0, q2, s2)
+    torch.cuda.synchronize()
+    assert_bits_equal(host_u8(q), host_u8(q2), "bf16 gamma vs fp32 gamma of the same values")
+
+
+def test_bf16_gamma_group_and_nvfp4(nq, orc):
+    note("bf16 gamma fused group / nvfp4")
+    w = W.rms_group_7168(1001, seed=8)
+    M, d = 1001, 7168
+    _, g32, gdev = _bf16_vec(w["gamma"])
+    x, r = to_dev_bf16(w["x"]), to_dev_bf16(w["residual"])
+    q = torch.empty(M, d, dtype=torch.uint8, device="cuda")
+    s = torch.empty(M, d // 128, dtype=torch.float32, device="cuda")
+    nq.nq_fused_add_rmsnorm_quant_fp8_group(x, r, torch.empty_like(r), gdev, w["eps"], q, s)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 32)
+    o = orc.fused_add_rmsnorm_quant_fp8_group(w["x"][rows], w["residual"][rows], g32, w["eps"])
+    assert_scales(s.cpu().numpy()[rows], o["scale"], "group scale")
+    assert_codes(host_u8(q)[rows], o["q"], "group q")
+    sg = calibrated_sg(orc, dict(w, gamma=g32))
+    qf = torch.empty(M, d // 2, dtype=torch.uint8, device="cuda")
+    sf = torch.empty(M, d // 16, dtype=torch.uint8, device="cuda")
+    nq.nq_rmsnorm_quant_nvfp4_ex(x, r, torch.empty_like(r), gdev, w["eps"], to_dev_f32([sg]), 0, qf, sf)
+    torch.cuda.synchronize()
+    on = orc.rmsnorm_quant_nvfp4(w["x"][rows], w["residual"][rows], g32, w["eps"], sg)
+    assert_codes(host_u8(sf)[rows], on["sf"], "nvfp4 block scales")
+    assert_codes(unpack_nibbles(host_u8(qf)[rows]), unpack_nibbles(on["q"]), "nvfp4 codes", fmt="e2m1")
+
+
+@pytest.mark.parametrize("d", [111, 4096])
+@pytest.mark.parametrize("M", [1, 1501])
+@pytest.mark.parametrize("dynamic", [False, True])
+def test_bf16_gamma_beta_layernorm(nq, orc, d, M, dynamic):
+    note(f"bf16 gamma/beta layernorm d={d} M={M} dynamic={dynamic}")
+    w = W.layernorm_rows(M=M, d=d, seed=d + 5 * M)
+    _, g32, gdev = _bf16_vec(w["gamma"])
+    _, b32, bdev = _bf16_vec(w["beta"])
+    x = to_dev_bf16(w["x"])
+    q = torch.empty(M, d, dtype=torch.uint8, device="cuda")
+    s = torch.empty(M, dtype=torch.float32, device="cuda")
+    sc = None if dynamic else to_dev_f32([w["scale"]])
+    nq.nq_layernorm_quant_fp8_ex(x, gdev, bdev, w["eps"], sc, 0, q, s if dynamic else None)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 24)
+    o = orc.layernorm_quant_fp8(w["x"][rows], g32, b32, w["eps"], None if dynamic else w["scale"])
+    if dynamic:
+        assert_scales(s.cpu().numpy()[rows], o["scale"], "ln scale")
+    assert_codes(host_u8(q)[rows], o["q"], "ln q")
