@@ -461,6 +461,30 @@ def summarize_trace(stats_csv, out_md, command):
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+SUITE_TRACE_SUMMARY = os.path.join(ROOT, "profiles", "suite_kernel_trace.md")
+SUITE_TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_suite -o suite --output-format csv -- "
+                       "python3 bench.py --suite --no-cpu-baseline")
+
+
+def summarize_suite(stats_csv, out_md):
+    """Text summary of a rocprofv3 --kernel-trace --stats run of the suite:
+    every kernel instance (template arguments name the row shape, team x
+    chunks, staging, output format), its calls and average duration."""
+    rows = sorted(_csv(stats_csv), key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# rocprofv3 kernel trace: every workload of `bench.py --suite`", "",
+             f"Command (repository root): `{SUITE_TRACE_COMMAND}`", "",
+             "Kernel template arguments: team lanes, chunks per lane, 128-bit path, staged shared "
+             "vectors, then (where present) output format (0 e4m3, 1 e5m2), dynamic scale, bf16 gamma, "
+             "and lanes per block.  The suite's own per-call figures (graph-replayed, events) are in "
+             "its stderr lines; these durations come from the profiler, with its overhead.", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("|", "\\|")
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def summarize_counters(fetch_csv, write_csv, out_md, commands):
     """HBM bytes per launch of the main kernel from FETCH_SIZE / WRITE_SIZE
     (KiB per dispatch), each scaled by what the same counter reads for the
@@ -555,9 +579,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-mode", action="store_true",
                     help="short fixed run for rocprofv3: copy reference + main kernel steps")
+    ap.add_argument("--summarize-suite", metavar="STATS_CSV",
+                    help="write profiles/suite_kernel_trace.md from a rocprofv3 --stats CSV of the suite")
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
                     help="write the profiles/ summaries from rocprofv3 output and exit")
     args = ap.parse_args()
+
+    if args.summarize_suite:
+        summarize_suite(args.summarize_suite, SUITE_TRACE_SUMMARY)
+        return
 
     if args.summarize:
         stats, fetch, write = args.summarize
