@@ -462,8 +462,12 @@ def summarize_trace(stats_csv, out_md, command):
 
 
 SUITE_TRACE_SUMMARY = os.path.join(ROOT, "profiles", "suite_kernel_trace.md")
-SUITE_TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_suite -o suite --output-format csv -- "
-                       "python3 bench.py --suite --no-cpu-baseline")
+
+
+def _profile_dir(csv_path):
+    """The rocprofv3 output directory a CSV came from, relative to the
+    repository root (what the recorded command's -d names)."""
+    return os.path.relpath(os.path.dirname(os.path.abspath(csv_path)), ROOT)
 
 
 def summarize_suite(stats_csv, out_md):
@@ -471,8 +475,10 @@ def summarize_suite(stats_csv, out_md):
     every kernel instance (template arguments name the row shape, team x
     chunks, staging, output format), its calls and average duration."""
     rows = sorted(_csv(stats_csv), key=lambda r: -float(r["TotalDurationNs"]))
+    command = (f"rocprofv3 --kernel-trace --stats -d {_profile_dir(stats_csv)} -o suite --output-format csv -- "
+               "python3 bench.py --suite --no-cpu-baseline")
     lines = ["# rocprofv3 kernel trace: every workload of `bench.py --suite`", "",
-             f"Command (repository root): `{SUITE_TRACE_COMMAND}`", "",
+             f"Command (repository root): `{command}`", "",
              "Kernel template arguments: team lanes, chunks per lane, 128-bit path, staged shared "
              "vectors, then (where present) output format (0 e4m3, 1 e5m2), dynamic scale, bf16 gamma, "
              "and lanes per block.  The suite's own per-call figures (graph-replayed, events) are in "
@@ -592,12 +598,12 @@ def main():
     if args.summarize:
         stats, fetch, write = args.summarize
         summarize_trace(stats, os.path.join(ROOT, "profiles", "rmsnorm_fp8_m8192_d2816_kernel_trace.md"),
-                        "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_kt -o kt --output-format csv -- "
+                        f"rocprofv3 --kernel-trace --stats -d {_profile_dir(stats)} -o kt --output-format csv -- "
                         "python3 bench.py --no-cpu-baseline")
         summarize_counters(fetch, write, COUNTER_SUMMARY,
-                           ["rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o fetch --output-format csv "
+                           [f"rocprofv3 --pmc FETCH_SIZE -d {_profile_dir(fetch)} -o fetch --output-format csv "
                             "-- python3 bench.py --profile-mode",
-                            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o write --output-format csv "
+                            f"rocprofv3 --pmc WRITE_SIZE -d {_profile_dir(write)} -o write --output-format csv "
                             "-- python3 bench.py --profile-mode"])
         return
 

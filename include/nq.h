@@ -41,7 +41,7 @@
  *   binary32 number).
  * Aliasing.  No output may overlap an input or another output, except that
  *   residual_out may be exactly residual_in (same pointer, same ld: in-place
- *   residual update, [FUSE] "FAQ").  Overlap is judged on address ranges.
+ *   residual update, [FUSE] "FAQ").  Overlap is decided on address ranges.
  * Threads.  The library keeps no mutable global state; calls are thread-safe.
  */
 #ifndef NQ_H

@@ -251,7 +251,7 @@ def test_nvfp4_validation(lib):
     assert call(ld_sf=95) == NQ_ERR_STRIDE
     assert call(sf=Q + 10) == NQ_ERR_ALIAS
     # the output may not be placed in the unread columns of x's own rows:
-    # overlap is judged on address ranges
+    # overlap is decided on address ranges
     assert call(q=X + 2 * 1536) == NQ_ERR_ALIAS
 
 
