@@ -368,28 +368,60 @@ def time_graph(torch, case, calls=20, replays=50, warm_ms=25.0):
     return float(np.median(times)) / calls
 
 
-def cpu_baseline(budget_s=10.0):
-    """The oracle (plain single-threaded C) on a bounded sample of the same
-    workload: 512-row slices of the M=8192, d=2816 rows, taken in order and
-    wrapping around, until about budget_s seconds of CPU work; reported in
-    GB/s of the same algorithmic bytes."""
+def _oracle_rows(w, lo, batch):
     import oracle
+    lo %= 8192
+    oracle.fused_add_rmsnorm_quant_fp8(w["x"][lo:lo + batch], w["residual"][lo:lo + batch], w["gamma"], w["eps"])
+
+
+def cpu_baseline(single_s=6.0, parallel_s=2.0):
+    """The oracle (plain C) on a bounded sample of the same workload:
+    512-row slices of the M=8192, d=2816 rows, taken in order and wrapping
+    around, reported in GB/s of the same algorithmic bytes.  First on one
+    thread for about single_s seconds, then row-parallel on the host's cores
+    (at most 16: the share of one GPU) for about parallel_s seconds of wall
+    time -- the unchanged oracle called from a thread pool, each call working
+    on its own rows (ctypes releases the interpreter lock during the call).
+    `value` is the row-parallel rate over the cores it used."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
     from fp4_quantization_amd import workloads as W, traffic
     w = W.rms_2816(8192, 0)
     oracle.lib()
-    rows, elapsed, batch = 0, 0.0, 512
-    t0 = time.perf_counter()
-    while elapsed < budget_s:
-        lo = rows % 8192
-        oracle.fused_add_rmsnorm_quant_fp8(w["x"][lo:lo + batch], w["residual"][lo:lo + batch],
-                                           w["gamma"], w["eps"])
+    batch = 512
+
+    def gbps(rows, seconds):
+        rd, wr = traffic.fused_add_rmsnorm_fp8(rows, 2816)
+        return (rd + wr) / seconds / 1e9
+
+    rows, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < single_s:
+        _oracle_rows(w, rows, batch)
         rows += batch
-        elapsed = time.perf_counter() - t0
-    rd, wr = traffic.fused_add_rmsnorm_fp8(rows, 2816)
-    return {"value": round((rd + wr) / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} rows ({rows / 8192:.2f} passes over the M=8192, d=2816 workload, seed 0) "
-                      f"in {elapsed:.1f} s, single-threaded, host {platform.processor() or platform.machine()}, "
-                      f"{os.cpu_count()} cores visible"}
+    single = gbps(rows, time.perf_counter() - t0)
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(16, cores))
+
+    def worker(k):
+        done, start = 0, time.perf_counter()
+        while time.perf_counter() - start < parallel_s:
+            _oracle_rows(w, (k + done * threads) * batch, batch)
+            done += 1
+        return done * batch
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        prow = sum(ex.map(worker, range(threads)))
+    pel = time.perf_counter() - t0
+    return {"value": round(gbps(prow, pel), 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": round(single, 4),
+            "sample": f"{prow} rows ({prow / 8192:.2f} passes over the M=8192, d=2816 workload, seed 0) in "
+                      f"{pel:.1f} s on {threads} threads; single-threaded {rows} rows in {single_s:.0f} s; host "
+                      f"{platform.processor() or platform.machine()}, {cores} cores available"}
 
 
 # ------------------------------------------------------- counter traffic --
