@@ -247,7 +247,9 @@ class UnfusedCase(Case):
 
 
 class CopyCase(Case):
-    """The 128-bit copy kernel over the same byte count: a same-box ceiling."""
+    """The 128-bit copy kernel over the same byte count: a same-box ceiling
+    (and, at 16 bytes, the time of one near-empty launch: the floor under
+    every M = 1 figure)."""
 
     def __init__(self, torch, nq, nbytes):
         n = nbytes // 2 // 16 * 16
@@ -593,6 +595,7 @@ def run_suite(torch, nq):
         ("nvfp4_slice_m8192", lambda: Nvfp4Case(torch, nq, 8192, sliced=True)),
         ("unfused_2816_m8192", lambda: UnfusedCase(torch, nq, 8192)),
         ("copy_161MB", lambda: CopyCase(torch, nq, 161_524_736)),
+        ("launch_floor_copy_32B", lambda: CopyCase(torch, nq, 32)),
     ]
     for name, make in cases:
         case = make()

@@ -45,7 +45,7 @@ __device__ __forceinline__ float rms_front(const uint16_t* x, int64_t ld_x, cons
         xw[j] = xio.load16(e, e < d);
         rw[j] = rio.load16(e, e < d);
     }
-    vecs.issue();
+    vecs.issue(t);
 
     // z = bf16(x + r), kept packed; residual write-back; sum of z^2.
     double acc = 0.0;

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t1) * 8;
         float g[8], z[8];
-        gamma.chunk(lds_gamma, 0, e, g);
+        gamma.chunk(lds_gamma, 0, j, e, g);
         unpack_bf16x8(zw[j], z);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {

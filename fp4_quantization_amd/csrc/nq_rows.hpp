@@ -122,6 +122,11 @@ class SharedVectors {
     static constexpr int kSlots = TEAM * CPL * 2;  // 16-byte fp32 slots covering one row's chunks
     static constexpr bool kStaged = STAGE && VEC && stages_vectors(TEAM, CPL, NV, BLOCK);
     static constexpr int kPer = kStaged ? (kSlots + S::kBlock - 1) / S::kBlock : 1;
+    // Unstaged instances with at most 2 chunks per lane (the few-rows
+    // shapes, where latency rules) load each lane's chunks with the row
+    // loads instead of after the first reduction, taking one memory round
+    // trip off the critical path for at most 16 more registers per vector.
+    static constexpr bool kPrefetch = !kStaged && CPL <= 2;
     typedef uint4 Lds[kStaged ? NV : 1][kStaged ? kSlots : 1];
     static_assert(!kStaged || kSlots * 16 * NV <= 64 * 1024, "staged vectors fit one block's LDS");
 
@@ -134,10 +139,25 @@ class SharedVectors {
             io_[v] = RowIO<VEC, kKeep, uint16_t>(static_cast<const uint16_t*>(p[v]), 0, vector_map(),
                                                  BF16 ? d : 2 * d);
     }
-    // Issue the cooperative loads (staged only): fp32 slot i holds elements
-    // 4i .. 4i+3, loaded as 16 bytes, or as 8 bytes of bf16 widened at publish.
-    __device__ __forceinline__ void issue()
+    // Issue the loads: staged, the block's cooperative loads (fp32 slot i
+    // holds elements 4i .. 4i+3, loaded as 16 bytes, or as 8 bytes of bf16
+    // widened at publish); prefetching, lane t's own chunks.
+    __device__ __forceinline__ void issue(int t)
     {
+        if constexpr (kPrefetch) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    const int e = (j * TEAM + t) * 8;
+                    if constexpr (BF16) {
+                        pre_[v][j][0] = io_[v].load16(e, e < d_);
+                    } else {
+                        pre_[v][j][0] = io_[v].load16(2 * e, e < d_);
+                        pre_[v][j][1] = io_[v].load16(2 * e + 8, e < d_);
+                    }
+                }
+        }
         if constexpr (kStaged) {
 #pragma unroll
             for (int v = 0; v < NV; ++v)
@@ -170,10 +190,20 @@ class SharedVectors {
             if constexpr (TEAM <= kWave) __syncthreads();
         }
     }
-    // 8 fp32 of vector v from element e (zeros past the end).
-    __device__ __forceinline__ void chunk(const Lds& lds, int v, int e, float g[8]) const
+    // 8 fp32 of vector v from element e = (j * TEAM + t) * 8 (zeros past the end).
+    __device__ __forceinline__ void chunk(const Lds& lds, int v, int j, int e, float g[8]) const
     {
-        if constexpr (kStaged) {
+        if constexpr (kPrefetch) {
+            if constexpr (BF16) {
+                unpack_bf16x8(pre_[v][j][0], g);
+            } else {
+                const uint4 a = pre_[v][j][0], b = pre_[v][j][1];
+                g[0] = __uint_as_float(a.x); g[1] = __uint_as_float(a.y);
+                g[2] = __uint_as_float(a.z); g[3] = __uint_as_float(a.w);
+                g[4] = __uint_as_float(b.x); g[5] = __uint_as_float(b.y);
+                g[6] = __uint_as_float(b.z); g[7] = __uint_as_float(b.w);
+            }
+        } else if constexpr (kStaged) {
             const uint4 a = lds[v][e / 4], b = lds[v][e / 4 + 1];
             g[0] = __uint_as_float(a.x); g[1] = __uint_as_float(a.y);
             g[2] = __uint_as_float(a.z); g[3] = __uint_as_float(a.w);
@@ -193,6 +223,7 @@ class SharedVectors {
   private:
     RowIO<VEC, kKeep, uint16_t> io_[NV];
     uint4 held_[kStaged ? NV : 1][kPer];
+    uint4 pre_[kPrefetch ? NV : 1][kPrefetch ? CPL : 1][BF16 ? 1 : 2];
     int d_;
 };
 
