@@ -306,14 +306,16 @@ __device__ __forceinline__ float div_by(float y, float s, float inv)
 // Cache policies (the aux bits of gfx950 buffer instructions: bit 0 sc0,
 // bit 1 nt, bit 4 sc1), chosen by measurement on MI355X for these streams:
 // inputs read once are non-temporal, bf16 row outputs (residual, norm_out)
-// are written with sc1, quantized codes non-temporal; gamma / beta use the
-// default policy so every row finds them cached.
+// are written with sc1, quantized codes non-temporal, per-group and NVFP4
+// block scale rows (small pieces per row) with sc0 -- 0.3 to 1 % faster than
+// non-temporal; gamma / beta use the default policy.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kLoadStream = 2;              // nt
 constexpr int kStoreRows = 16;              // sc1
 constexpr int kStoreCodes = 2;              // nt
+constexpr int kStoreScales = 1;             // sc0: small scale rows, written in pieces
 constexpr int kKeep = 0;                    // default
 constexpr uint32_t kOOB = 0x80000000u;      // beyond any resource size used here
 constexpr int kRsrcWord3 = 0x00020000;      // gfx9-family raw buffer descriptor word 3

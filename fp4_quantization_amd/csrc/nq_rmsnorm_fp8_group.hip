@@ -63,8 +63,10 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8_group(RmsGroupArgs a)
 
     const RowIO<VEC, kStoreRows, uint16_t> nio(a.norm_out, a.ld_n, m, d);
     const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d);
-    const RowIO<VEC, kStoreCodes, float> sio(a.scale_out, a.ld_s, m, d / kRowGroup);
+    const RowIO<VEC, kStoreScales, float> sio(a.scale_out, a.ld_s, m, d / kRowGroup);
     const int t1 = opaque(t);
+    const bool ue8m0 = a.ue8m0 != 0;
+    float sc[CPL];  // this lane's group scale of each chunk
 #pragma unroll
     for (int j = 0; j < CPL; ++j) opaque(zw[j]);
 #pragma unroll
@@ -89,15 +91,24 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8_group(RmsGroupArgs a)
         for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(y[k]));
         // The group's 16 lanes: every lane of the DPP row gets its maximum.
         amax = max16_dpp(amax);
-        float s = amax / fp8_max<F>();
-        if (a.ue8m0) s = pow2_ceil(s);
+        const float s0 = amax / fp8_max<F>();
+        const float s = ue8m0 ? pow2_ceil(s0) : s0;
         const float inv = s > 0.0f ? 1.0f / s : 0.0f;
         float v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = y[k] * inv;
         qio.store8(e, e < d, fp8x8<F>(v));
-        sio.store4(e / kRowGroup, e < d && (t1 & 15) == 0, __float_as_uint(s));
+        sc[j] = s;
     }
+    // Every lane of a DPP row holds its group's scale for each chunk, so lane
+    // t = 16q + j stores chunk j's scale: one store instruction per
+    // wavefront carries all of its groups' scales.
+    const int sel = t1 & 15;
+    float mine = sc[0];
+#pragma unroll
+    for (int j = 1; j < CPL; ++j) mine = sel == j ? sc[j] : mine;
+    const int es = (sel * TEAM + t1 - sel) * 8;  // first element of chunk sel's group
+    sio.store4(es / kRowGroup, sel < CPL && es < d, __float_as_uint(mine));
 }
 
 template <int TEAM, int CPL, bool VEC>

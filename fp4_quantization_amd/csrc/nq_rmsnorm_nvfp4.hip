@@ -65,7 +65,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
 
     const RowIO<VEC, kStoreRows, uint16_t> nio(a.norm_out, a.ld_n, m, d);
     const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d / 2);
-    const RowIO<VEC, kStoreCodes, uint8_t> sfio(a.sf, a.ld_sf, m, d / 16);
+    const RowIO<VEC, kStoreScales, uint8_t> sfio(a.sf, a.ld_sf, m, d / 16);
     const int t1 = opaque(t);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) opaque(zw[j]);
