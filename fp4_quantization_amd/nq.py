@@ -72,6 +72,7 @@ NQ_CODEC_E4M3 = 0
 NQ_CODEC_E2M1 = 1
 NQ_CODEC_BF16 = 2
 NQ_CODEC_E5M2 = 3
+NQ_MAX_D = 32768  # widest row of the row kernels (include/nq.h)
 
 
 class NQError(RuntimeError):

@@ -147,6 +147,7 @@ def test_rmsnorm_fp8_group_validation(lib):
     assert call(s=Q + 64) == NQ_ERR_ALIAS
     assert call(s=G + 64) == NQ_ERR_ALIAS
     assert call(ro=R + 2) == NQ_ERR_ALIAS
+    assert call(d=32896, ld_x=32896, ld_r=32896, ld_ro=32896, ld_q=32896, ld_s=257) == NQ_ERR_SHAPE  # > NQ_MAX_D
 
 
 def test_layernorm_fp8_validation(lib):
@@ -160,6 +161,7 @@ def test_layernorm_fp8_validation(lib):
     assert call(q=X) == NQ_ERR_ALIAS
     assert call(q=S) == NQ_ERR_ALIAS
     assert call(d=-3) == NQ_ERR_SHAPE
+    assert call(d=32776, ld_x=32776, ld_q=32776) == NQ_ERR_SHAPE  # > NQ_MAX_D
 
 
 def test_group_fp8_validation(lib):
@@ -218,6 +220,8 @@ def test_unfused_pair_and_nvfp4_ex_validation(lib):
     assert norm(eps=-1.0) == NQ_ERR_ARG
     assert norm(o=X + 2) == NQ_ERR_ALIAS
     assert norm(o=RO + 64) == NQ_ERR_ALIAS
+    assert lib.nq_fused_add_rmsnorm_bf16(X, 32776, R, 32776, RO, 32776, G, 1e-6, N, 32776, 4, 32776,
+                                         None) == NQ_ERR_SHAPE  # > NQ_MAX_D
     quant = lambda **k: lib.nq_per_token_quant_fp8(
         k.get("x", X), 256, k.get("ss", None), k.get("flags", 0), k.get("q", Q), k.get("ld_q", 256),
         k.get("sc", SC), k.get("M", 4), 256, None)
@@ -228,6 +232,7 @@ def test_unfused_pair_and_nvfp4_ex_validation(lib):
     assert quant(ld_q=100) == NQ_ERR_STRIDE
     assert quant(q=X + 16) == NQ_ERR_ALIAS
     assert quant(sc=Q + 8) == NQ_ERR_ALIAS
+    assert lib.nq_per_token_quant_fp8(X, 32776, None, 0, Q, 32776, SC, 4, 32776, None) == NQ_ERR_SHAPE
     fp4 = lambda **k: lib.nq_rmsnorm_quant_nvfp4_ex(
         X, 2112, None, 0, None, 0, G, 1e-6, S, k.get("flags", 0), Q, 768, SC, 96, None, 0, k.get("M", 2),
         1536, None)
@@ -243,6 +248,7 @@ def test_nvfp4_validation(lib):
         k.get("d", 1536), None)
     assert call(M=0) == NQ_OK                      # residual-less column slice
     assert call(d=1544, ld_q=772, ld_sf=97) == NQ_ERR_SHAPE   # d % 16
+    assert call(d=32784, ld_x=32784, ld_q=16392, ld_sf=2049) == NQ_ERR_SHAPE  # > NQ_MAX_D
     assert call(gs=None) == NQ_ERR_NULL
     assert call(sf=None) == NQ_ERR_NULL
     assert call(r=R, ld_r=1536, ld_ro=1536) == NQ_ERR_NULL   # residual_in without residual_out
@@ -268,3 +274,18 @@ def test_binding_imports_without_gpu():
     import fp4_quantization_amd.nq as nq
     assert "gfx950" in nq.nq_version()
     assert nq.nq_status_string(-4).startswith("an output overlaps")
+
+
+def test_binding_constants_match_the_header():
+    """The Python binding's NQ_* constants are the header's values, and every
+    scale mode, flag, codec and the row-width limit is exported."""
+    import fp4_quantization_amd.nq as nq
+    text = open(HEADER).read()
+    defs = {k: int(v) for k, v in re.findall(r"^#define (NQ_[A-Z0-9_]+) \(?(-?\d+)u?\)?", text, re.M)}
+    needed = [k for k in defs if k.startswith(("NQ_SCALE_", "NQ_FLAG_", "NQ_CODEC_")) or k == "NQ_MAX_D"]
+    assert len(needed) >= 9
+    for k in needed:
+        assert getattr(nq, k) == defs[k], k
+    for k, v in defs.items():
+        if hasattr(nq, k):
+            assert getattr(nq, k) == v, k

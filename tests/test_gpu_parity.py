@@ -917,3 +917,48 @@ def test_bf16_gamma_beta_layernorm(nq, orc, d, M, dynamic):
     if dynamic:
         assert_scales(s.cpu().numpy()[rows], o["scale"], "ln scale")
     assert_codes(host_u8(q)[rows], o["q"], "ln q")
+
+
+# ------------------------------------------------ the largest hidden size ----
+# NQ_MAX_D = 32768 is the widest row every row kernel takes (one team of
+# 1024 lanes, four 8-element chunks each, shared vectors read straight from
+# memory: two fp32 vectors of 32768 do not fit one block's LDS).
+
+@pytest.mark.parametrize("M", [1, 67])
+def test_max_hidden_size_every_row_entry_point(nq, orc, M):
+    d = nq.NQ_MAX_D
+    note(f"d=NQ_MAX_D={d} M={M}: layernorm static / dynamic e4m3 / dynamic e5m2")
+    w = W.layernorm_rows(M=M, d=d, seed=M + 31)
+    q = run_ln(nq, w)
+    rows = sample_rows(M, 12)
+    o = orc.layernorm_quant_fp8(w["x"][rows], w["gamma"], w["beta"], w["eps"], w["scale"])
+    assert_codes(q[rows], o["q"], "ln q")
+    for fmt, fl in (("e4m3", 0), ("e5m2", nq.NQ_FLAG_E5M2)):
+        q, s = run_ln_ex(nq, w, fl)
+        o = orc.layernorm_quant_fp8(w["x"][rows], w["gamma"], w["beta"], w["eps"], None, fmt=fmt)
+        assert_scales(s[rows], o["scale"], f"ln dynamic scale {fmt}")
+        assert_codes(q[rows], o["q"], f"ln dynamic q {fmt}", fmt=fmt)
+
+    note(f"d={d} M={M}: add+RMSNorm+NVFP4 with norm_out")
+    w = W.rms_rows(M, d, 4, 20.0, seed=M + 32)
+    sg = calibrated_sg(orc, w)
+    got = run_nvfp4(nq, w, sg, norm_out=True)
+    compare_nvfp4(orc, w, got, rows, sg, norm_out=True)
+
+    note(f"d={d} M={M}: unfused pair")
+    got = run_unfused(nq, w)
+    f = orc.fused_add_rmsnorm_quant_fp8(w["x"][rows], w["residual"][rows], w["gamma"], w["eps"], d=d,
+                                        want_norm_out=True)
+    assert_bits_equal(got["residual_out"][rows], f["residual_out"], "residual_out")
+    assert_bits_equal(got["norm"][rows], f["norm_out"], "bf16 norm output")
+    u = orc.unfused_rmsnorm_quant_fp8(w["x"][rows], w["residual"][rows], w["gamma"], w["eps"])
+    assert_scales(got["scale"][rows], u["scale"], "unfused scale")
+    assert_codes(got["q"][rows], u["q"], "unfused q")
+
+    note(f"K={d} M={M}: standalone group quantizer")
+    wg = W.group_t3(M, K=d, seed=M + 33)
+    for ue in (False, True):
+        q, s = run_group(nq, wg["x"], ue)
+        o = orc.per_token_group_quant_fp8(wg["x"][rows], 128, ue8m0=ue)
+        assert_bits_equal(s[rows].view(np.uint32), o["scale"].view(np.uint32), "group scales")
+        assert_bits_equal(q[rows], o["q"], "group codes")
