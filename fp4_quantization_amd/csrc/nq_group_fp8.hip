@@ -12,8 +12,8 @@
 // column group i % (K/128)) is owned by 16 lanes, 8 elements (one 128-bit
 // load) each, so a wavefront covers 4 groups and each of its load
 // instructions reads 1 KB of contiguous row.  The group maximum is four DPP
-// steps inside a 16-lane DPP row.  Each lane handles UNROLL groups, all
-// loads issued before the first use.
+// steps inside a 16-lane DPP row.  Each lane handles kGroupUnroll groups,
+// all loads issued before the first use.
 #include "nq_device.hpp"
 #include "nq_host.hpp"
 
