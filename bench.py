@@ -19,7 +19,10 @@ in one hipGraph and replayed once, timed with HIP events on the replay
 stream; each step is one launch, so `roofline.achieved` (bytes over the
 kernel's average launch duration) is the same figure.  `eager_ms_per_step`
 times the same K steps as plain launches, `m1_us_per_call` is the
-graph-amortized time of one M=1 call.  The default warmup (1000 untimed
+graph-amortized time of one M=1 call, and `copy_reference` is a plain
+128-bit copy of the same byte count on the same GPU (a same-box ceiling for
+this read/write mix; `value_over_copy` above 1 means the kernel moves its
+bytes faster than that copy).  The default warmup (1000 untimed
 launches, ~27 ms of sustained load) brings the GPU to its steady clocks
 before the timed steps: measured on MI355X, after only 20 warmup launches
 the first two replays of the graph ran ~5% slower than later ones.  `--suite` also prints one
@@ -467,7 +470,7 @@ def summarize_trace(stats_csv, out_md, command):
              f"Command (repository root): `{command}`", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in rows:
-        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+        lines.append(f"| `{_short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     main = [r for r in rows if r["Name"].startswith(MAIN_KERNEL_PREFIX) and "128, 3" in r["Name"]]
     if main:
@@ -491,7 +494,9 @@ def summarize_trace(stats_csv, out_md, command):
                 lines += [f"- timed window (dispatches {w}..{w + k - 1}, the graph replay): {rate(timed)}",
                           f"- warmup dispatches 0..{w - 1}: {rate(sum(dur[:w]) / w)}",
                           f"- eager reference run ({w + k}..{w + 2 * k - 1}): {rate(sum(dur[w + k:w + 2 * k]) / k)}"]
-        lines += ["", "The many short calls of the other shape are the M=1 latency measurements."]
+        lines += ["", "The many short calls of the other shape are the M=1 latency measurements; "
+                  "`k_diag_copy` is the same-byte-count copy behind `copy_reference` (warmup replays "
+                  "included), and the torch kernels fill its buffers."]
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -502,6 +507,13 @@ def _profile_dir(csv_path):
     """The rocprofv3 output directory a CSV came from, relative to the
     repository root (what the recorded command's -d names)."""
     return os.path.relpath(os.path.dirname(os.path.abspath(csv_path)), ROOT)
+
+
+def _short_name(name, width=160):
+    """Kernel name for a Markdown table: pipes escaped, long library
+    template names cut (the profiler CSV keeps them whole)."""
+    name = name.replace("|", "\\|")
+    return name if len(name) <= width else name[: width - 3] + "..."
 
 
 def summarize_suite(stats_csv, out_md):
@@ -519,8 +531,7 @@ def summarize_suite(stats_csv, out_md):
              "its stderr lines; these durations come from the profiler, with its overhead.", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in rows:
-        name = r["Name"].replace("|", "\\|")
-        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+        lines.append(f"| `{_short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
@@ -685,6 +696,13 @@ def main():
     m1_us = time_graph(torch, m1, calls=100) * 1e3
     m1_ev_ms = time_launch_events(torch, m1, 200)
     del m1
+    # same-box ceiling: a plain 128-bit copy moving the same byte count
+    # (half read, half written), graph-replayed like the suite's figures
+    cp = CopyCase(torch, nq, case_bytes_8192())
+    copy_us = time_graph(torch, cp) * 1e3
+    copy_gbps = cp.bytes / (copy_us * 1e-6) / 1e9
+    del cp
+    torch.cuda.empty_cache()
 
     if args.suite:
         run_suite(torch, nq)
@@ -705,6 +723,8 @@ def main():
         "m1_us_per_launch_events": round(m1_ev_ms * 1e3, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_bytes},
+        "copy_reference": {"us_per_call": round(copy_us, 3), "GBps": round(copy_gbps, 1),
+                           "value_over_copy": round(value / copy_gbps, 4)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
