@@ -31,10 +31,12 @@ inline bool overlaps(const Region& a, const Region& b)
 
 inline bool aligned(const void* p, uintptr_t bytes) { return ((uintptr_t)p % bytes) == 0; }
 
-// Bounds that keep every offset a kernel forms in range: row offsets in
-// int64, and the per-wavefront buffer offsets (at most 4 rows of at most
-// 2^24 elements of at most 4 bytes) below 2^31.
-constexpr int64_t kMaxRows = int64_t(1) << 40;
+// Bounds that keep every offset formed on the host or in a kernel in range:
+// a tensor's extent (M - 1) * ld + cols stays below 2^60 elements, so its
+// byte size (at most 4 bytes each) and every int64 row offset fit without
+// overflow; the per-wavefront buffer offsets (at most 4 rows of at most 2^24
+// elements of at most 4 bytes) stay below 2^31.
+constexpr int64_t kMaxRows = int64_t(1) << 36;
 constexpr int64_t kMaxLd = int64_t(1) << 24;
 
 inline bool bad_ld(int64_t ld, int64_t cols) { return ld < cols || ld > kMaxLd; }

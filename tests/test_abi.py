@@ -125,6 +125,29 @@ def test_rmsnorm_fp8_validation(lib):
     assert rms(lib, q=G) == NQ_ERR_ALIAS
 
 
+def test_extreme_rows_and_strides_are_checked_without_overflow(lib):
+    """At the row limit (2^36 rows) and the stride limit (2^24 elements) the
+    host still forms every address range exactly: an overlapping output is
+    found (NQ_ERR_ALIAS), one more row is a shape error."""
+    big_m, big_ld = 1 << 36, 1 << 24
+    assert rms(lib, M=big_m + 1) == NQ_ERR_SHAPE
+    assert rms(lib, M=big_m, ld_x=big_ld, ld_r=big_ld, ld_ro=big_ld, ld_q=big_ld, q=X + 100) == NQ_ERR_ALIAS
+    assert rms(lib, ld_x=big_ld + 1) == NQ_ERR_STRIDE
+    ln = lambda **k: lib.nq_layernorm_quant_fp8(
+        X, k.get("ld", 512), G, B, 1e-5, S, k.get("q", Q), k.get("ld", 512), k.get("M", 2), 512, None)
+    assert ln(M=big_m + 1) == NQ_ERR_SHAPE
+    assert ln(M=big_m, ld=big_ld, q=X + 4096) == NQ_ERR_ALIAS
+    fp4 = lambda **k: lib.nq_rmsnorm_quant_nvfp4(
+        X, k.get("ld", 2112), None, 0, None, 0, G, 1e-6, S, k.get("q", Q), k.get("ld_q", 768), SC,
+        k.get("ld_sf", 96), None, 0, k.get("M", 2), 1536, None)
+    assert fp4(M=big_m + 1) == NQ_ERR_SHAPE
+    assert fp4(M=big_m, ld=big_ld, ld_q=big_ld, ld_sf=big_ld, q=X + 64) == NQ_ERR_ALIAS
+    grp = lambda **k: lib.nq_per_token_group_quant_fp8(
+        X, k.get("ld", 4096), k.get("M", 2), 4096, 128, 0, k.get("q", Q), k.get("ld", 4096), SC, None)
+    assert grp(M=big_m) == NQ_ERR_SHAPE        # M * K / 128 must stay below 2^31
+    assert grp(M=(1 << 31) // 32 - 1, ld=big_ld, q=X + 64) == NQ_ERR_ALIAS
+
+
 def test_rmsnorm_fp8_group_validation(lib):
     def call(**kw):
         a = dict(x=X, ld_x=2816, r=R, ld_r=2816, ro=RO, ld_ro=2816, g=G, eps=1e-6, gs=128, mode=0,
