@@ -57,8 +57,10 @@ typedef int nq_status;
 
 #define NQ_OK 0
 #define NQ_ERR_NULL (-1)        /* a mandatory pointer is NULL */
-#define NQ_ERR_SHAPE (-2)       /* M < 0, d <= 0, d above NQ_MAX_D, d % 16 for NVFP4, K % group */
-#define NQ_ERR_STRIDE (-3)      /* a leading dimension is smaller than the row length */
+#define NQ_ERR_SHAPE (-2)       /* M < 0, M above 2^36, d <= 0, d above NQ_MAX_D, d % 16 for
+                                   NVFP4, K % group, M * K / 128 of 2^31 or more for group quant */
+#define NQ_ERR_STRIDE (-3)      /* a leading dimension is smaller than the row length or above
+                                   2^24 elements */
 #define NQ_ERR_ALIAS (-4)       /* an output overlaps an input or another output */
 #define NQ_ERR_LAUNCH (-5)      /* the HIP launch failed (hipGetLastError) */
 #define NQ_ERR_ARG (-6)         /* an argument value is outside its domain (eps, mode, group) */
