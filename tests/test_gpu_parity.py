@@ -962,3 +962,74 @@ def test_max_hidden_size_every_row_entry_point(nq, orc, M):
         o = orc.per_token_group_quant_fp8(wg["x"][rows], 128, ue8m0=ue)
         assert_bits_equal(s[rows].view(np.uint32), o["scale"].view(np.uint32), "group scales")
         assert_bits_equal(q[rows], o["q"], "group codes")
+
+
+# ------------------------------------------------------ graph capture ------
+# "RMSNorm/FusedRMSNorm + Quant kernels cuda graph fixes" ("Changes"): every
+# scale is read on the device when the kernel runs, so a captured graph
+# follows updates of the scale tensors, and the kernels hold no host state.
+
+def _all_ops(nq, t, o):
+    """One call of every entry point, inputs from `t`, outputs into `o`."""
+    nq.nq_fused_add_rmsnorm_quant_fp8(t["x"], t["r"], o["ro"], t["g"], 1e-6, None, o["q1"], o["s1"])
+    nq.nq_fused_add_rmsnorm_quant_fp8(t["x"], t["r"], o["ro2"], t["g"], 1e-6, t["ss"], o["q2"], None)
+    nq.nq_fused_add_rmsnorm_quant_fp8_group(t["x"], t["r"], o["ro3"], t["g"], 1e-6, o["q3"], o["s3"],
+                                            scale_mode=nq.NQ_SCALE_UE8M0)
+    nq.nq_rmsnorm_quant_nvfp4(t["x"], t["r"], o["ro4"], t["g"], 1e-6, t["gs"], o["q4"], o["sf4"])
+    nq.nq_per_token_group_quant_fp8(t["x"], o["q5"], o["s5"])
+    nq.nq_layernorm_quant_fp8(t["x"], t["g"], t["b"], 1e-5, t["ss"], o["q6"])
+    nq.nq_layernorm_quant_fp8_ex(t["x"], t["g"], t["b"], 1e-5, None, nq.NQ_FLAG_E5M2, o["q7"], o["s7"])
+    nq.nq_fused_add_rmsnorm_bf16(t["x"], t["r"], o["ro8"], t["g"], 1e-6, o["n8"])
+    nq.nq_per_token_quant_fp8(o["n8"], None, 0, o["q8"], o["s8"])
+
+
+def _outputs(M, d):
+    u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device="cuda")
+    bf = lambda: torch.empty(M, d, dtype=torch.bfloat16, device="cuda")
+    f32 = lambda *s: torch.empty(*s, dtype=torch.float32, device="cuda")
+    return dict(ro=bf(), q1=u8(M, d), s1=f32(M), ro2=bf(), q2=u8(M, d), ro3=bf(), q3=u8(M, d),
+                s3=f32(M, d // 128), ro4=bf(), q4=u8(M, d // 2), sf4=u8(M, d // 16), q5=u8(M, d),
+                s5=f32(M * (d // 128)), q6=u8(M, d), q7=u8(M, d), s7=f32(M), ro8=bf(), n8=bf(),
+                q8=u8(M, d), s8=f32(M))
+
+
+def test_graph_replay_every_entry_point(nq):
+    """All entry points captured in one graph and replayed five times, with
+    new inputs copied in and the scale tensors changed by eager torch work
+    between replays; every output of every replay equals an eager call."""
+    note("graph replay of every entry point")
+    M, d = 96, 2816
+    t = dict(x=torch.empty(M, d, dtype=torch.bfloat16, device="cuda"),
+             r=torch.empty(M, d, dtype=torch.bfloat16, device="cuda"),
+             g=to_dev_f32(W.rms_2816(1)["gamma"]), b=to_dev_f32(np.full(d, 0.05, np.float32)),
+             ss=to_dev_f32([0.05]), gs=to_dev_f32([W.NVFP4_NOMINAL_GLOBAL_SCALE]))
+    w0 = W.rms_2816(M, seed=40)
+    t["x"].copy_(to_dev_bf16(w0["x"]))
+    t["r"].copy_(to_dev_bf16(w0["residual"]))
+    o = _outputs(M, d)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _all_ops(nq, t, o)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _all_ops(nq, t, o)
+    for k, (sc, gsc) in enumerate(((0.05, 1.0), (0.01, 0.5), (1.0, 2.0), (10.0, 0.25), (0.05, 1.0))):
+        w = W.rms_2816(M, seed=41 + k)
+        t["x"].copy_(to_dev_bf16(w["x"]))
+        t["r"].copy_(to_dev_bf16(w["residual"]))
+        t["ss"].fill_(sc)
+        t["gs"].fill_(W.NVFP4_NOMINAL_GLOBAL_SCALE * gsc)
+        for v in o.values():
+            v.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        e = _outputs(M, d)
+        _all_ops(nq, t, e)
+        torch.cuda.synchronize()
+        for name in o:
+            assert_bits_equal(host_u8(o[name].view(torch.uint8)), host_u8(e[name].view(torch.uint8)),
+                              f"replay {k}: {name}")
