@@ -132,7 +132,7 @@ def test_rms_fp8_static_scale(nq, orc, scale):
     compare_rms_fp8(orc, w, got, np.arange(64), static_scale=scale)
 
 
-@pytest.mark.parametrize("d", [8, 16, 32, 111, 128, 136, 1000, 2048, 4104, 8208, 16384, 32768])
+@pytest.mark.parametrize("d", [1, 3, 7, 8, 16, 32, 111, 128, 136, 1000, 2048, 4104, 8208, 16384, 32768])
 @pytest.mark.parametrize("M", [3, 1101])
 def test_rms_fp8_ragged_d(nq, orc, d, M):
     note(f"rms fp8 ragged d={d} M={M}")
@@ -380,7 +380,7 @@ def test_layernorm_full_config_sampled(nq, orc):
     assert_codes(q[rows], o["q"], "ln q")
 
 
-@pytest.mark.parametrize("d", [111, 256, 768, 4096, 16384])
+@pytest.mark.parametrize("d", [1, 3, 111, 256, 768, 4096, 16384])
 @pytest.mark.parametrize("M", [1, 7, 1501])
 def test_layernorm_shapes(nq, orc, d, M):
     note(f"layernorm d={d} M={M}")
@@ -640,7 +640,7 @@ def test_layernorm_dynamic_full_config_sampled(nq, orc, fmt):
     assert_codes(q[rows], o["q"], "ln dynamic q", fmt=fmt)
 
 
-@pytest.mark.parametrize("d", [111, 256, 768, 4096, 16384])
+@pytest.mark.parametrize("d", [1, 3, 111, 256, 768, 4096, 16384])
 @pytest.mark.parametrize("M", [1, 7, 989, 1501])
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 def test_layernorm_dynamic_shapes(nq, orc, d, M, fmt):
