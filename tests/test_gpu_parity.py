@@ -1033,3 +1033,44 @@ def test_graph_replay_every_entry_point(nq):
         for name in o:
             assert_bits_equal(host_u8(o[name].view(torch.uint8)), host_u8(e[name].view(torch.uint8)),
                               f"replay {k}: {name}")
+
+
+def test_concurrent_host_threads_on_their_own_streams(nq):
+    """The library keeps no mutable global state: four host threads, each
+    with its own stream and outputs, call the entry points at once (ctypes
+    releases the interpreter lock during the C call); every result equals the
+    single-threaded one."""
+    import threading
+    note("concurrent host threads")
+    M, d, n_threads, reps = 64, 2816, 4, 12
+    w = W.rms_2816(M, seed=50)
+    t = dict(x=to_dev_bf16(w["x"]), r=to_dev_bf16(w["residual"]), g=to_dev_f32(w["gamma"]),
+             b=to_dev_f32(np.full(d, 0.05, np.float32)), ss=to_dev_f32([0.05]),
+             gs=to_dev_f32([W.NVFP4_NOMINAL_GLOBAL_SCALE]))
+    ref = _outputs(M, d)
+    _all_ops(nq, t, ref)
+    torch.cuda.synchronize()
+    outs = [_outputs(M, d) for _ in range(n_threads)]
+    streams = [torch.cuda.Stream() for _ in range(n_threads)]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(reps):
+                    _all_ops(nq, t, outs[i])
+        except Exception as exc:  # reported below; a thread's exception is otherwise lost
+            errors.append(exc)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(n_threads)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, o in enumerate(outs):
+        for name in o:
+            assert_bits_equal(host_u8(o[name].view(torch.uint8)), host_u8(ref[name].view(torch.uint8)),
+                              f"thread {i}: {name}")
