@@ -426,7 +426,19 @@ def cpu_baseline(single_s=6.0, parallel_s=2.0):
             "single_thread_value": round(single, 4),
             "sample": f"{prow} rows ({prow / 8192:.2f} passes over the M=8192, d=2816 workload, seed 0) in "
                       f"{pel:.1f} s on {threads} threads; single-threaded {rows} rows in {single_s:.0f} s; host "
-                      f"{platform.processor() or platform.machine()}, {cores} cores available"}
+                      f"{_cpu_model()}, {cores} cores available"}
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name (Linux), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 # ------------------------------------------------------- counter traffic --
