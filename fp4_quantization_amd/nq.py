@@ -346,16 +346,22 @@ def nq_per_token_quant_fp8(x, static_scale, flags, q_out, scale_out, stream=None
 def nq_diag_codec(kind: int, x: torch.Tensor, out: torch.Tensor, stream=None):
     """Apply the kernels' device conversion routine element-wise (include/nq.h)."""
     n = x.numel()
-    want = torch.int16 if kind == NQ_CODEC_BF16 else torch.uint8
-    if out.dtype not in (want, torch.bfloat16 if kind == NQ_CODEC_BF16 else torch.uint8):
-        raise TypeError("nq_diag_codec: wrong output dtype")
-    st = _lib.nq_diag_codec(int(kind), _vec(x, torch.float32, "x", n), out.data_ptr(), n,
-                            _stream(stream))
+    px = _vec(x, torch.float32, "x", n)
+    if kind == NQ_CODEC_BF16:
+        if out.dtype not in (torch.int16, torch.bfloat16):
+            raise TypeError(f"out: dtype {out.dtype}, expected int16 or bfloat16 bits")
+        pout = _vec(out, out.dtype, "out", n)
+    else:
+        pout = _vec(out, torch.uint8, "out", n)
+    st = _lib.nq_diag_codec(int(kind), px, pout, n, _stream(stream))
     _check(st, "nq_diag_codec")
 
 
 def nq_diag_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     """128-bit device copy of src's bytes into dst (include/nq.h)."""
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("nq_diag_copy: destination too small")
