@@ -145,6 +145,13 @@ def _gvec(*ts, n: int, names=("gamma", "beta")):
     return ptrs, (NQ_FLAG_GAMMA_BF16 if dt == torch.bfloat16 else 0)
 
 
+def _same_rows(M: int, **tensors):
+    """Every given matrix has the input's M rows."""
+    for name, t in tensors.items():
+        if t is not None and t.size(0) != M:
+            raise ValueError(f"{name}: expected {M} rows")
+
+
 def _check(status: int, where: str):
     if status != NQ_OK:
         raise NQError(status, where)
@@ -288,6 +295,8 @@ def nq_rmsnorm_quant_nvfp4(x, residual_in, residual_out, gamma, eps, global_scal
     pq, ldq = _mat(q_packed, (torch.uint8,), "q_packed", d // 2)
     psf, ldsf = _mat(block_scale, _CODES8, "block_scale", d // 16)
     pn, ldn = _mat(norm_out, _BF16, "norm_out", d)
+    _same_rows(M, residual_in=residual_in, residual_out=residual_out, q_packed=q_packed,
+               block_scale=block_scale, norm_out=norm_out)
     st = _lib.nq_rmsnorm_quant_nvfp4(
         px, ldx, pr, ldr, pro, ldro, _vec(gamma, torch.float32, "gamma", d), float(eps),
         _vec(global_scale, torch.float32, "global_scale", 1), pq, ldq, psf, ldsf, pn, ldn,
@@ -305,6 +314,8 @@ def nq_rmsnorm_quant_nvfp4_ex(x, residual_in, residual_out, gamma, eps, global_s
     pq, ldq = _mat(q_packed, (torch.uint8,), "q_packed", d // 2)
     psf, ldsf = _mat(block_scale, _CODES8, "block_scale", d // 16)
     pn, ldn = _mat(norm_out, _BF16, "norm_out", d)
+    _same_rows(M, residual_in=residual_in, residual_out=residual_out, q_packed=q_packed,
+               block_scale=block_scale, norm_out=norm_out)
     (pg,), gf = _gvec(gamma, n=d)
     st = _lib.nq_rmsnorm_quant_nvfp4_ex(
         px, ldx, pr, ldr, pro, ldro, pg, float(eps),

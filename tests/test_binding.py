@@ -78,3 +78,36 @@ def test_wrong_dtypes_are_refused(nq):
             continue
         with pytest.raises(TypeError):
             call()
+
+
+@pytest.mark.gpu
+def test_row_count_mismatches_are_refused(nq):
+    """An output (or residual) with fewer rows than the input is refused
+    before the call: the kernel would otherwise write past it."""
+    dev = {k: v.cuda() for k, v in _host().items()}
+    short = {k: v[: M - 1] if v.dim() == 2 else v for k, v in dev.items()}
+    for key in ("r", "ro", "q", "qf", "sf", "n", "sg"):
+        t = dict(dev)
+        t[key] = short[key]
+        for name, call in _calls(nq, t).items():
+            if name.startswith("nq_diag") or key not in _uses(name):
+                continue
+            with pytest.raises(ValueError, match="rows|elements"):
+                call()
+
+
+def _uses(name):
+    """The matrix arguments each entry point takes, by the keys of _host()."""
+    return {
+        "nq_fused_add_rmsnorm_quant_fp8": ("r", "ro", "q"),
+        "nq_fused_add_rmsnorm_quant_fp8_ex": ("r", "ro", "q"),
+        "nq_fused_add_rmsnorm_quant_fp8_group": ("r", "ro", "q", "sg"),
+        "nq_layernorm_quant_fp8": ("q",),
+        "nq_layernorm_quant_fp8_ex": ("q",),
+        "nq_per_token_group_quant_fp8": ("q",),
+        "nq_per_token_group_quant_fp8_ex": ("q",),
+        "nq_rmsnorm_quant_nvfp4": ("r", "ro", "qf", "sf"),
+        "nq_rmsnorm_quant_nvfp4_ex": ("r", "ro", "qf", "sf"),
+        "nq_fused_add_rmsnorm_bf16": ("r", "ro", "n"),
+        "nq_per_token_quant_fp8": ("q",),
+    }[name]
