@@ -491,10 +491,6 @@ __device__ __forceinline__ float opaque(float v)
     return v;
 }
 
-// bf16 -0.0 in both halves: x + (-0) == x exactly for every x (also -0),
-// so a residual-less row runs the residual-add code path unchanged.
-constexpr uint32_t kNegZeroBf16x2 = 0x80008000u;
-
 __device__ __forceinline__ void unpack_bf16x8(uint4 w, float v[8])
 {
     v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);

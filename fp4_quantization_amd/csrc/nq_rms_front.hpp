@@ -9,8 +9,8 @@
 // exactly); [NVFP4] "RMSNorm nvfp4 quant fusion for DS V3.2 / Kimi-K2.5"
 // (commit notes: optional residual, fresh or in-place residual buffer).
 //
-//   z_i  = bf16(x_i + r_i)   (x_i when residual-less: adding bf16 -0.0 leaves
-//                             x unchanged bit for bit, so one code path)
+//   z_i  = bf16(x_i + r_i), or x_i itself when residual-less (RES false: a
+//          separate instance with no add, repacking or write-back)
 //   rstd = 1 / sqrt(sum z_i^2 / d + eps), the sum in binary64 (every z_i^2 is
 //          exact there), rounded to binary32 once, so the result does not
 //          depend on the reduction tree.
@@ -27,44 +27,61 @@ namespace nq {
 // across the reduction.  `vecs` are the block's shared vectors:
 // their cooperative loads are issued with the row loads and they are
 // published before the reduction's barrier.
-template <int TEAM, int CPL, bool VEC, class SV>
+template <int TEAM, int CPL, bool VEC, bool RES, class SV>
 __device__ __forceinline__ float rms_front(const uint16_t* x, int64_t ld_x, const uint16_t* r, int64_t ld_r,
                                            uint16_t* ro, int64_t ld_ro, const RowMap& m, int t, int d, float eps,
                                            SV& vecs, typename SV::Lds& lds_vec, double* lds_sum, uint4 (&zw)[CPL])
 {
     const RowIO<VEC, kLoadStream, uint16_t> xio(x, ld_x, m, d);
-    const RowIO<VEC, kLoadStream, uint16_t> rio(r, ld_r, m, d);
-    const RowIO<VEC, kStoreRows, uint16_t> roio(ro, ld_ro, m, d);
-
-    // Issue every load of the row before the first use.
-    const uint32_t rfill = r != nullptr ? 0u : kNegZeroBf16x2;
-    uint4 xw[CPL], rw[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int e = (j * TEAM + t) * 8;
-        xw[j] = xio.load16(e, e < d);
-        rw[j] = rio.load16(e, e < d);
-    }
-    vecs.issue(t);
-
-    // z = bf16(x + r), kept packed; residual write-back; sum of z^2.
     double acc = 0.0;
+    if constexpr (RES) {
+        const RowIO<VEC, kLoadStream, uint16_t> rio(r, ld_r, m, d);
+        const RowIO<VEC, kStoreRows, uint16_t> roio(ro, ld_ro, m, d);
+        // Issue every load of the row before the first use.
+        uint4 xw[CPL], rw[CPL];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int e = (j * TEAM + t) * 8;
-        float xv[8], rv[8], z[8];
-        unpack_bf16x8(xw[j], xv);
-        unpack_bf16x8(make_uint4(rw[j].x | rfill, rw[j].y | rfill, rw[j].z | rfill, rw[j].w | rfill), rv);
-        uint32_t p[4];
+        for (int j = 0; j < CPL; ++j) {
+            const int e = (j * TEAM + t) * 8;
+            xw[j] = xio.load16(e, e < d);
+            rw[j] = rio.load16(e, e < d);
+        }
+        vecs.issue(t);
+        // z = bf16(x + r), kept packed; residual write-back; sum of z^2.
 #pragma unroll
-        for (int k = 0; k < 4; ++k) p[k] = pack_bf16x2(xv[2 * k] + rv[2 * k], xv[2 * k + 1] + rv[2 * k + 1]);
-        zw[j] = make_uint4(p[0], p[1], p[2], p[3]);
-        roio.store16(e, e < d, zw[j]);  // dropped when residual-less
-        unpack_bf16x8(zw[j], z);
+        for (int j = 0; j < CPL; ++j) {
+            const int e = (j * TEAM + t) * 8;
+            float xv[8], rv[8], z[8];
+            unpack_bf16x8(xw[j], xv);
+            unpack_bf16x8(rw[j], rv);
+            uint32_t p[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const double zd = (double)z[k];
-            acc = fma(zd, zd, acc);  // z^2 is exact in binary64
+            for (int k = 0; k < 4; ++k) p[k] = pack_bf16x2(xv[2 * k] + rv[2 * k], xv[2 * k + 1] + rv[2 * k + 1]);
+            zw[j] = make_uint4(p[0], p[1], p[2], p[3]);
+            roio.store16(e, e < d, zw[j]);
+            unpack_bf16x8(zw[j], z);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const double zd = (double)z[k];
+                acc = fma(zd, zd, acc);  // z^2 is exact in binary64
+            }
+        }
+    } else {
+        // Residual-less: z is x itself (a bf16 value).
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int e = (j * TEAM + t) * 8;
+            zw[j] = xio.load16(e, e < d);
+        }
+        vecs.issue(t);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            float z[8];
+            unpack_bf16x8(zw[j], z);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const double zd = (double)z[k];
+                acc = fma(zd, zd, acc);
+            }
         }
     }
     __builtin_amdgcn_sched_barrier(0);

@@ -42,7 +42,7 @@ struct RmsGroupArgs {
     bool gamma_bf16;
 };
 
-template <int TEAM, int CPL, bool VEC, bool STAGE, Fp8 F = Fp8::E4M3, bool GB = false,
+template <int TEAM, int CPL, bool VEC, bool STAGE, Fp8 F = Fp8::E4M3, bool GB = false, bool RES = true,
           int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
 __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8_group(RmsGroupArgs a)
 {
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8_group(RmsGroupArgs a)
     SV gamma({a.gamma}, d);
 
     uint4 zw[CPL];
-    const float rstd = rms_front<TEAM, CPL, VEC>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
+    const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
                                                  lds_gamma, lds_sum, zw);
 
     const RowIO<VEC, kStoreRows, uint16_t> nio(a.norm_out, a.ld_n, m, d);
@@ -118,12 +118,18 @@ struct RmsGroupKernel {
     template <bool STAGE>
     static void launch(const RmsGroupArgs& a, dim3 grid, dim3 block, hipStream_t s)
     {
+        if (a.r != nullptr) go<STAGE, true>(a, grid, block, s);
+        else go<STAGE, false>(a, grid, block, s);
+    }
+    template <bool STAGE, bool RES>
+    static void go(const RmsGroupArgs& a, dim3 grid, dim3 block, hipStream_t s)
+    {
         if (a.gamma_bf16) {
-            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E5M2, true>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E4M3, true>), grid, block, 0, s, a);
+            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E5M2, true, RES>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E4M3, true, RES>), grid, block, 0, s, a);
         } else {
-            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E5M2, false>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E4M3, false>), grid, block, 0, s, a);
+            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E5M2, false, RES>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E4M3, false, RES>), grid, block, 0, s, a);
         }
     }
 };

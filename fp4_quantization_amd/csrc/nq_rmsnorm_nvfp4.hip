@@ -43,7 +43,8 @@ struct RmsFp4Args {
 };
 
 // VEC additionally needs 4-byte aligned packed-code rows (one dword per chunk).
-template <int TEAM, int CPL, bool VEC, bool STAGE, bool GB = false, int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
+template <int TEAM, int CPL, bool VEC, bool STAGE, bool GB = false, bool RES = true,
+          int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
 __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
 {
     using S = TeamShape<TEAM, BLOCK>;
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
     const float sg = a.global_scale[0];  // issued early: read on the device at run time
 
     uint4 zw[CPL];
-    const float rstd = rms_front<TEAM, CPL, VEC>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
+    const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
                                                  lds_gamma, lds_sum, zw);
     const float G = 1.0f / sg;  // encode scale
 
@@ -111,8 +112,14 @@ struct RmsFp4Kernel {
     template <bool STAGE>
     static void launch(const RmsFp4Args& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        if (a.gamma_bf16) hipLaunchKernelGGL((k_add_rmsnorm_nvfp4<TEAM, CPL, VEC, STAGE, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_add_rmsnorm_nvfp4<TEAM, CPL, VEC, STAGE, false>), grid, block, 0, s, a);
+        if (a.r != nullptr) go<STAGE, true>(a, grid, block, s);
+        else go<STAGE, false>(a, grid, block, s);
+    }
+    template <bool STAGE, bool RES>
+    static void go(const RmsFp4Args& a, dim3 grid, dim3 block, hipStream_t s)
+    {
+        if (a.gamma_bf16) hipLaunchKernelGGL((k_add_rmsnorm_nvfp4<TEAM, CPL, VEC, STAGE, true, RES>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_add_rmsnorm_nvfp4<TEAM, CPL, VEC, STAGE, false, RES>), grid, block, 0, s, a);
     }
 };
 

@@ -33,7 +33,7 @@ struct RmsBf16Args {
     float eps;
 };
 
-template <int TEAM, int CPL, bool VEC, bool STAGE, int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
+template <int TEAM, int CPL, bool VEC, bool STAGE, bool RES = true, int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
 __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_bf16(RmsBf16Args a)
 {
     using S = TeamShape<TEAM, BLOCK>;
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_bf16(RmsBf16Args a)
     SV gamma({a.gamma}, d);
 
     uint4 zw[CPL];
-    const float rstd = rms_front<TEAM, CPL, VEC>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
+    const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
                                                  lds_gamma, lds_sum, zw);
 
     const RowIO<VEC, kStoreRows, uint16_t> oio(a.out, a.ld_o, m, d);
@@ -77,7 +77,8 @@ struct RmsBf16Kernel {
     template <bool STAGE>
     static void launch(const RmsBf16Args& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        hipLaunchKernelGGL((k_add_rmsnorm_bf16<TEAM, CPL, VEC, STAGE>), grid, block, 0, s, a);
+        if (a.r != nullptr) hipLaunchKernelGGL((k_add_rmsnorm_bf16<TEAM, CPL, VEC, STAGE, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_add_rmsnorm_bf16<TEAM, CPL, VEC, STAGE, false>), grid, block, 0, s, a);
     }
 };
 
