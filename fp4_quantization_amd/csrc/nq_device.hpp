@@ -21,6 +21,9 @@ namespace nq {
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr float kE4M3Max = 448.0f; // largest finite OCP e4m3fn value
 constexpr float kE2M1Max = 6.0f;   // largest E2M1 magnitude
+constexpr float kInvE2M1Max = 0x1.555556p-3f;   // RN(1/6)
+// amax at or above 6 * 2^-126 gives a normal amax / 6 (with margin: 2^-120).
+constexpr float kMinNormalE2M1Quotient = 0x1p-120f;
 
 // ------------------------------------------------------------ bf16 -------
 // A bf16 is the upper half of a binary32, so widening is exact.

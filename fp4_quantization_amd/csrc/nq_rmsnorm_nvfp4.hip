@@ -48,7 +48,9 @@ template <int TEAM, int CPL, bool VEC, bool STAGE, bool GB = false, bool RES = t
 __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
 {
     using S = TeamShape<TEAM, BLOCK>;
+    static_assert(BLOCK >= 128, "128 lanes fill the block-scale table");
     __shared__ double lds_sum[S::kWaves];
+    __shared__ float lds_mult[128];  // RN(G / value(code)) for every block-scale code
 
     const int t = threadIdx.x % TEAM;
     const RowMap m = row_map<TEAM, BLOCK>(a.M);
@@ -63,6 +65,13 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
     const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
                                                  lds_gamma, lds_sum, zw);
     const float G = 1.0f / sg;  // encode scale
+    // The element multiplier depends only on the block-scale code: one
+    // correctly rounded quotient per code and block instead of one per chunk.
+    if (threadIdx.x < 128) {
+        const float sfd = e4m3_value(threadIdx.x);
+        lds_mult[threadIdx.x] = sfd > 0.0f ? G / sfd : 0.0f;
+    }
+    __syncthreads();
 
     const RowIO<VEC, kStoreRows, uint16_t> nio(a.norm_out, a.ld_n, m, d);
     const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d / 2);
@@ -93,10 +102,13 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
         // Block of 16 = this chunk and the partner lane's (same load
         // instruction, lanes t and t^1).
         amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-        const float per = amax / kE2M1Max;
-        const uint32_t sf = e4m3x4(per * G, 0.0f, 0.0f, 0.0f) & 0xFFu;
-        const float sfd = e4m3_value(sf);
-        const float mult = sfd > 0.0f ? G / sfd : 0.0f;
+        // per = RN(amax / 6): Markstein's correction is exact for a normal
+        // quotient; a wavefront holding a smaller one takes the division.
+        float per = div_by(amax, kE2M1Max, kInvE2M1Max);
+        if (__builtin_amdgcn_ballot_w64(amax < kMinNormalE2M1Quotient) != 0)
+            if (amax < kMinNormalE2M1Quotient) per = amax / kE2M1Max;
+        const uint32_t sf = e4m3x4(per * G, 0.0f, 0.0f, 0.0f) & 0x7Fu;  // amax >= 0: codes 0 .. 0x7E
+        const float mult = lds_mult[sf];
         float v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = y[k] * mult;

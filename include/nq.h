@@ -288,7 +288,9 @@ nq_status nq_fused_add_rmsnorm_quant_fp8_group(
  *   residual_in  [M, d] bf16, row stride ld_r, or NULL (residual-less)
  *   residual_out [M, d] bf16, row stride ld_ro; NULL iff residual_in is NULL
  *   gamma        [d] fp32
- *   global_scale one fp32 on the device (> 0)
+ *   global_scale one fp32 on the device, at least 2^-118 (then G / value(sf)
+ *                is finite for every block-scale code; below that a zero
+ *                element can meet an infinite multiplier, outside the contract)
  *   q_packed     [M, d/2] bytes, row stride ld_q (in bytes)
  *   block_scale  [M, d/16] e4m3 codes, row stride ld_sf, linear layout
  *   norm_out     [M, d] bf16, row stride ld_n, or NULL

@@ -1074,3 +1074,30 @@ def test_concurrent_host_threads_on_their_own_streams(nq):
         for name in o:
             assert_bits_equal(host_u8(o[name].view(torch.uint8)), host_u8(ref[name].view(torch.uint8)),
                               f"thread {i}: {name}")
+
+
+def test_nvfp4_tiny_block_maxima(nq, orc):
+    """Blocks whose maximum |y| lies near or below 6 * 2^-126: amax / 6 is
+    then (nearly) subnormal, where the kernel's three-operation quotient is not
+    exact and the wavefront takes the division instead.  A global scale of
+    2^-118 turns those tiny blocks into ordinary (and e4m3-subnormal) scale
+    codes, so a wrong quotient would show in the codes; it also keeps every
+    G / value(code) finite (with s_g below 2^-118 the smallest codes' element
+    multipliers overflow, and a zero element times an infinite multiplier is
+    outside the encodings' domain)."""
+    note("nvfp4 tiny block maxima")
+    M, d = 16, 256
+    w = W.rms_rows(M, d, 0, 1.0, seed=77)
+    g = np.ones(d, np.float32)
+    for b, k in enumerate((0, 115, 117, 118, 119, 120, 121, 122, 123, 124, 125, 126, 127, 130, 140, 149)):
+        g[16 * b:16 * (b + 1)] = np.float32(2.0 ** -k)
+    w = dict(w, gamma=g)
+    sg = float(np.float32(2.0 ** -118))
+    got = run_nvfp4(nq, w, sg, norm_out=True)
+    o = orc.rmsnorm_quant_nvfp4(w["x"], w["residual"], g, w["eps"], sg, want_norm_out=True, want_y=True)
+    assert_bits_equal(got["sf"], o["sf"], "block scales")
+    assert_bits_equal(got["q"], o["q"], "packed codes")
+    assert_bits_equal(got["norm_out"], o["norm_out"], "norm_out")
+    # many blocks below the threshold carry real (non-zero) scale codes
+    amax = np.abs(o["y"]).reshape(M, -1, 16).max(axis=2)
+    assert ((amax < 2.0 ** -120) & (o["sf"] > 0)).sum() >= 50
