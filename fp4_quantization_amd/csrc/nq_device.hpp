@@ -119,23 +119,17 @@ __device__ __forceinline__ float e4m3_value(uint32_t c)
 #ifndef NQ_E2M1_SOFTWARE
 // Native gfx950 conversion.  The scale operand is 1.0 (the block
 // multiplier is applied beforehand with an ordinary binary32 multiply, so
-// the rounding input is exactly that product); the input is clamped to
-// [-6, 6] first.
+// the rounding input is exactly that product).  No clamp: measured on
+// MI355X, the conversion saturates by itself (every value >= 6, infinity
+// included, gives code 7; <= -6 gives 15), so it equals the nearest-even
+// code of the value clamped to [-6, 6] for every non-NaN input.
 __device__ __forceinline__ uint32_t e2m1x8(const float v[8])
 {
     uint32_t w = 0;
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-        w, __builtin_amdgcn_fmed3f(v[0], -kE2M1Max, kE2M1Max),
-        __builtin_amdgcn_fmed3f(v[1], -kE2M1Max, kE2M1Max), 1.0f, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-        w, __builtin_amdgcn_fmed3f(v[2], -kE2M1Max, kE2M1Max),
-        __builtin_amdgcn_fmed3f(v[3], -kE2M1Max, kE2M1Max), 1.0f, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-        w, __builtin_amdgcn_fmed3f(v[4], -kE2M1Max, kE2M1Max),
-        __builtin_amdgcn_fmed3f(v[5], -kE2M1Max, kE2M1Max), 1.0f, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
-        w, __builtin_amdgcn_fmed3f(v[6], -kE2M1Max, kE2M1Max),
-        __builtin_amdgcn_fmed3f(v[7], -kE2M1Max, kE2M1Max), 1.0f, 3);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
     return w;
 }
 #else

@@ -82,8 +82,11 @@ def test_e5m2_device_codec_edges(nq, orc):
         assert np.array_equal(got, orc.e5m2_encode(v[:n]))
 
 
-@pytest.mark.parametrize("exp_field", list(range(121, 130)))
+@pytest.mark.parametrize("exp_field", list(range(121, 130)) + [0, 1, 100, 130, 131, 160, 200, 254])
 def test_e2m1_device_codec_exhaustive(nq, orc, exp_field):
+    """Every binary32 of the binade, both signs: the rounding binades around
+    the E2M1 magnitudes, the subnormals, and binades far above 6 where the
+    conversion must saturate to code 7 / 15."""
     for sign in (0, 1):
         v = _binade(exp_field, sign)
         got = _run(nq, nq.NQ_CODEC_E2M1, v)
@@ -93,7 +96,7 @@ def test_e2m1_device_codec_exhaustive(nq, orc, exp_field):
 
 
 def test_e2m1_device_codec_edges(nq, orc):
-    v = np.array([0.0, -0.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 6.5, 7.0, 100.0, 1e30,
+    v = np.array([0.0, -0.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 6.5, 7.0, 100.0, 1e30, np.inf, -np.inf,
                   -0.25, -0.75, -5.0, -6.0, -7.0, -1e30, 1e-30, -1e-30, 1e-40, -1e-40,
                   np.nextafter(np.float32(0.25), np.float32(1)), np.nextafter(np.float32(5.0), np.float32(0))],
                  np.float32)
