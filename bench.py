@@ -49,6 +49,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused add+RMSNorm+FP8-quant GB/s & % HBM peak, M=8192 d=2816; µs/call M=1"
 HBM_PEAK_GBPS = 8000.0
 MAIN_KERNEL_SOURCES = ["fp4_quantization_amd/csrc/nq_rmsnorm_fp8.hip",
+                       "fp4_quantization_amd/csrc/nq_rms_front.hpp",
                        "fp4_quantization_amd/csrc/nq_device.hpp",
                        "fp4_quantization_amd/csrc/nq_rows.hpp"]
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "rmsnorm_fp8_m8192_d2816_hbm_counters.md")
