@@ -1101,3 +1101,38 @@ def test_nvfp4_tiny_block_maxima(nq, orc):
     # many blocks below the threshold carry real (non-zero) scale codes
     amax = np.abs(o["y"]).reshape(M, -1, 16).max(axis=2)
     assert ((amax < 2.0 ** -120) & (o["sf"] > 0)).sum() >= 50
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+def test_group_scales_of_tiny_groups(nq, orc, ue8m0):
+    """Group maxima down to 2^-119 (scales near and below the normal range,
+    subnormal in fp32 mode) for the standalone quantizer (bf16 x scaled per
+    group) and the fused kernel (gamma scaled per group), both scale modes.
+    Every scale stays above 2^-128, so RN(1 / s) is finite."""
+    note(f"group scales of tiny groups ue8m0={ue8m0}")
+    ks = (0, 100, 110, 113, 114, 115, 116, 117, 118, 119)
+    M, K = 24, 128 * len(ks)
+    rng = np.random.default_rng(5)
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    for gi, k in enumerate(ks):
+        xf[:, 128 * gi:128 * (gi + 1)] *= np.float32(2.0 ** -k)
+    x = W.to_bf16_bits(xf)
+    q, s = run_group(nq, x, ue8m0)
+    o = orc.per_token_group_quant_fp8(x, 128, ue8m0=ue8m0)
+    assert np.all((o["scale"] == 0) | (o["scale"] > 2.0 ** -128))
+    assert (o["scale"] < 2.0 ** -124).sum() > 0
+    if not ue8m0:  # subnormal scales (UE8M0 rounds them up to 2^-126)
+        assert (o["scale"] < 2.0 ** -126).sum() > 0
+    assert_bits_equal(s.view(np.uint32), o["scale"].view(np.uint32), "standalone scales")
+    assert_bits_equal(q, o["q"], "standalone codes")
+
+    w = W.rms_rows(M, K, 0, 1.0, seed=6)
+    g = np.ones(K, np.float32)
+    for gi, k in enumerate(ks):
+        g[128 * gi:128 * (gi + 1)] = np.float32(2.0 ** -k)
+    w = dict(w, gamma=g)
+    got = run_rms_group(nq, w, ue8m0=ue8m0)
+    fo = orc.fused_add_rmsnorm_quant_fp8_group(w["x"], w["residual"], g, w["eps"], ue8m0=ue8m0)
+    assert np.all((fo["scale"] == 0) | (fo["scale"] > 2.0 ** -128))
+    assert_bits_equal(got["scale"].view(np.uint32), fo["scale"].view(np.uint32), "fused scales")
+    assert_bits_equal(got["q"], fo["q"], "fused codes")
