@@ -26,7 +26,11 @@ bytes faster than that copy).  The default warmup (1000 untimed
 launches, ~27 ms of sustained load) brings the GPU to its steady clocks
 before the timed steps: measured on MI355X, after only 20 warmup launches
 the first two replays of the graph ran ~5% slower than later ones.  `--suite` also prints one
-line per workload (all five) to stderr.  `--profile-mode` runs a short fixed
+line per workload (all five configurations and their variants) to stderr:
+each timed alone (`us_per_call_graph`: graphs of 20 calls, median of 50
+replays after ~25 ms of warm replays) and all together, round-robin
+(`us_per_call_interleaved`: every workload's graph replayed once per round,
+median of 100 rounds).  `--profile-mode` runs a short fixed
 sequence meant to be wrapped by rocprofv3.  `--summarize` turns rocprofv3
 output into the text summaries kept under profiles/.
 """
@@ -374,6 +378,45 @@ def time_graph(torch, case, calls=20, replays=50, warm_ms=25.0):
     return float(np.median(times)) / calls
 
 
+def time_graphs_interleaved(torch, cases, calls=20, rounds=100, warm_rounds=10):
+    """Per-call times of several workloads measured round-robin: one graph of
+    `calls` launches per workload, then `rounds` rounds that replay every
+    graph once each, with events around each replay and no synchronization
+    in between; the median over rounds of each workload's replay time, per
+    call.  Interleaving spreads clock and thermal drift over all workloads
+    alike instead of favouring whichever was timed first."""
+    graphs = []
+    for case in cases:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(3):
+                case.step(i, s.cuda_stream)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            h = torch.cuda.current_stream().cuda_stream
+            for i in range(calls):
+                case.step(i, h)
+        graphs.append(g)
+    for _ in range(warm_rounds):
+        for g in graphs:
+            g.replay()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in graphs]
+          for _ in range(rounds)]
+    for r in range(rounds):
+        for g, (e0, e1) in zip(graphs, ev[r]):
+            e0.record()
+            g.replay()
+            e1.record()
+    torch.cuda.synchronize()
+    out = [float(np.median([ev[r][k][0].elapsed_time(ev[r][k][1]) for r in range(rounds)])) / calls
+           for k in range(len(graphs))]
+    del graphs
+    return out
+
+
 def _oracle_rows(w, lo, batch):
     import oracle
     lo %= 8192
@@ -621,18 +664,26 @@ def run_suite(torch, nq):
         ("copy_161MB", lambda: CopyCase(torch, nq, 161_524_736)),
         ("launch_floor_copy_32B", lambda: CopyCase(torch, nq, 32)),
     ]
-    for name, make in cases:
+    built, lines = [], []
+    for name, make in cases:  # each workload alone: warm replays, then timed replays back to back
         case = make()
         us_graph = time_graph(torch, case) * 1e3
-        line = {"workload": name, "label": case.label, "bytes_per_call": case.bytes,
-                **({"fused_bytes_per_call": case.fused_bytes} if hasattr(case, "fused_bytes") else {}),
-                "us_per_call_graph": round(us_graph, 3),
-                "us_per_launch_events": round(time_launch_events(torch, case, 50) * 1e3, 3),
-                "GBps_graph": round(case.bytes / (us_graph * 1e-6) / 1e9, 1),
-                "pct_hbm_peak_graph": round(100 * case.bytes / (us_graph * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)}
+        lines.append({"workload": name, "label": case.label, "bytes_per_call": case.bytes,
+                      **({"fused_bytes_per_call": case.fused_bytes} if hasattr(case, "fused_bytes") else {}),
+                      "us_per_call_graph": round(us_graph, 3),
+                      "us_per_launch_events": round(time_launch_events(torch, case, 50) * 1e3, 3),
+                      "GBps_graph": round(case.bytes / (us_graph * 1e-6) / 1e9, 1),
+                      "pct_hbm_peak_graph": round(100 * case.bytes / (us_graph * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)})
+        built.append(case)
+    # all workloads together, round-robin (every case keeps its buffer sets resident)
+    inter = time_graphs_interleaved(torch, built)
+    for line, case, ms in zip(lines, built, inter):
+        us = ms * 1e3
+        line["us_per_call_interleaved"] = round(us, 3)
+        line["pct_hbm_peak_interleaved"] = round(100 * case.bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)
         log(json.dumps(line))
-        del case
-        torch.cuda.empty_cache()
+    del built
+    torch.cuda.empty_cache()
 
 
 def main():
