@@ -116,7 +116,6 @@ __device__ __forceinline__ float e4m3_value(uint32_t c)
 // ------------------------------------------------------------ E2M1 -------
 // E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 (codes 0-7), bit 3 the sign.
 // Two values -> one byte, the first in bits 0-3 ([NVFP4]: packed E2M1).
-#ifndef NQ_E2M1_SOFTWARE
 // Native gfx950 conversion.  The scale operand is 1.0 (the block
 // multiplier is applied beforehand with an ordinary binary32 multiply, so
 // the rounding input is exactly that product).  No clamp: measured on
@@ -132,25 +131,6 @@ __device__ __forceinline__ uint32_t e2m1x8(const float v[8])
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
     return w;
 }
-#else
-// Comparison form: each threshold is a midpoint between neighbouring
-// magnitudes; ">" at a midpoint whose lower neighbour has the even code
-// and ">=" where the upper one does implements ties-to-even.
-__device__ __forceinline__ uint32_t e2m1_code(float v)
-{
-    const float a = fabsf(v);
-    uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
-                 (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
-    return c | (__float_as_uint(v) >> 31 << 3);
-}
-__device__ __forceinline__ uint32_t e2m1x8(const float v[8])
-{
-    uint32_t w = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) w |= e2m1_code(v[k]) << (4 * k);
-    return w;
-}
-#endif
 
 // ------------------------------------------------------- reductions -------
 // Within a 16-lane DPP row: xor 1 and xor 2 inside each quad, then the

@@ -35,10 +35,12 @@
  *   Misaligned pointers or strides are not errors: they select a slower
  *   element-wise path with identical results.
  * Device-side preconditions (documented, not checked: checking would need a
- *   host synchronization): inputs and scales are finite, static scales and
- *   the NVFP4 global scale are > 0, and no group or row has a non-zero
- *   absolute maximum below 448 * 2^-126 (so every derived scale is a normal
- *   binary32 number).
+ *   host synchronization): inputs and scales are finite; static scales are
+ *   > 0 and the NVFP4 global scale is at least 2^-118; no row or group has a
+ *   non-zero absolute maximum below fmax * 2^-128 (fmax = 448, or 57344 for
+ *   e5m2), where the reciprocal of its scale would overflow (subnormal
+ *   scales above that are handled exactly); with eps = 0 no row is all
+ *   zero.
  * Aliasing.  No output may overlap an input or another output, except that
  *   residual_out may be exactly residual_in (same pointer, same ld: in-place
  *   residual update, [FUSE] "FAQ").  Overlap is decided on address ranges.
@@ -103,7 +105,7 @@ typedef int nq_status;
  *   residual_in  [M, d] bf16, row stride ld_r, or NULL       (read)
  *   residual_out [M, d] bf16, row stride ld_ro; NULL iff residual_in is NULL
  *   gamma        [d] fp32                                   (read)
- *   eps          > 0 added inside the square root
+ *   eps          >= 0, added inside the square root
  *   static_scale one fp32 on the device, or NULL for dynamic per-token scales
  *   q_out        [M, d] e4m3 codes, row stride ld_q          (written)
  *   scale_out    [M] fp32 per-token scales; required when dynamic, unused
