@@ -15,7 +15,7 @@
 //
 // The row is held in registers exactly as in the per-token FP8 kernel.  A
 // 16-element block is two adjacent chunks, owned by lanes t and t^1 of the
-// same load instruction, so the block maximum is one cross-lane exchange.
+// same load instruction, so the block maximum is one DPP exchange.
 // Lanes past the end of the row still execute every exchange with zeros
 // (d % 16 == 0 keeps both halves of a block on the same side of the end).
 #include "nq_device.hpp"
@@ -100,13 +100,15 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
 #pragma unroll
         for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(y[k]));
         // Block of 16 = this chunk and the partner lane's (same load
-        // instruction, lanes t and t^1).
-        amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+        // instruction, lanes t and t^1: one DPP exchange inside a quad).
+        amax = fmaxf(amax, dpp_f32<kDppXor1>(amax));
         // per = RN(amax / 6): Markstein's correction is exact for a normal
-        // quotient; a wavefront holding a smaller one takes the division.
+        // quotient (and gives 0 for 0); a wavefront holding a smaller
+        // non-zero maximum takes the division.
         float per = div_by(amax, kE2M1Max, kInvE2M1Max);
-        if (__builtin_amdgcn_ballot_w64(amax < kMinNormalE2M1Quotient) != 0)
-            if (amax < kMinNormalE2M1Quotient) per = amax / kE2M1Max;
+        const bool tiny = amax > 0.0f && amax < kMinNormalE2M1Quotient;
+        if (__builtin_amdgcn_ballot_w64(tiny) != 0)
+            if (tiny) per = amax / kE2M1Max;
         const uint32_t sf = e4m3x4(per * G, 0.0f, 0.0f, 0.0f) & 0x7Fu;  // amax >= 0: codes 0 .. 0x7E
         const float mult = lds_mult[sf];
         float v[8];
