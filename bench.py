@@ -105,6 +105,7 @@ class RmsFp8Case(Case):
         w = W.rms_2816(M, seed) if d == 2816 else W.rms_small(seed, M)
         rd, wr = traffic.fused_add_rmsnorm_fp8(M, d, residual=True, static=static)
         self.bytes = rd + wr
+        self.elements = M * d
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         r = torch.from_numpy(w["residual"]).view(torch.bfloat16).cuda()
         self.g = torch.from_numpy(w["gamma"]).cuda()
@@ -130,6 +131,7 @@ class GroupCase(Case):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.group_t3(M, K)
         self.bytes = traffic.total(traffic.group_fp8(M, K))
+        self.elements = M * K
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         self.fn = nq.library().nq_per_token_group_quant_fp8
         mode = nq.NQ_SCALE_UE8M0 if ue8m0 else nq.NQ_SCALE_FP32
@@ -147,6 +149,7 @@ class LayerNormCase(Case):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.layernorm_rows(M, d)
         self.bytes = traffic.total(traffic.layernorm_fp8(M, d, dynamic=dynamic))
+        self.elements = M * d
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         self.g = torch.from_numpy(w["gamma"]).cuda()
         self.b = torch.from_numpy(w["beta"]).cuda()
@@ -177,6 +180,7 @@ class Nvfp4Case(Case):
         w = W.nvfp4_slice(M) if sliced else W.nvfp4_7168(M)
         d, ld = w["d"], w["ld"]
         self.bytes = traffic.total(traffic.rmsnorm_nvfp4(M, d, residual=not sliced))
+        self.elements = M * d
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         r = None if sliced else torch.from_numpy(w["residual"]).view(torch.bfloat16).cuda()
         self.g = torch.from_numpy(w["gamma"]).cuda()
@@ -203,6 +207,7 @@ class RmsGroupCase(Case):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.rms_group_7168(M) if d == 7168 else W.rms_2816(M)
         self.bytes = traffic.total(traffic.fused_add_rmsnorm_fp8_group(M, d))
+        self.elements = M * d
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         r = torch.from_numpy(w["residual"]).view(torch.bfloat16).cuda()
         self.g = torch.from_numpy(w["gamma"]).cuda()
@@ -231,6 +236,7 @@ class UnfusedCase(Case):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.rms_2816(M)
         self.bytes = M * traffic.unfused_add_rmsnorm_fp8_per_row(d) + 4 * d
+        self.elements = M * d
         self.fused_bytes = traffic.total(traffic.fused_add_rmsnorm_fp8(M, d))
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         r = torch.from_numpy(w["residual"]).view(torch.bfloat16).cuda()
@@ -632,9 +638,65 @@ def summarize_counters(fetch_csv, write_csv, out_md, commands):
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+VALU_SUMMARY = os.path.join(ROOT, "profiles", "valu_counters.md")
+SIMDS = 256 * 4          # compute units x SIMDs per unit
+CYCLES_PER_VALU = 4      # a wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles
+CLOCK_GHZ = 2.4          # MI355X peak engine clock
+
+
+def summarize_valu(suite_log, csvs, out_md):
+    """VALU issue load of each profiled workload: SQ_INSTS_VALU (wavefront
+    instructions per dispatch) spread over the chip's SIMDs at 4 cycles each,
+    against the workload's measured time per call at the 2.4 GHz engine
+    clock."""
+    suite = {}
+    for line in open(suite_log):
+        if line.startswith('{"workload"'):
+            j = json.loads(line)
+            suite[j["workload"]] = j
+    rows = ["# rocprofv3 VALU counters per workload", "",
+            "Commands (repository root), one pass per workload W:", "",
+            "- `rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU GRBM_GUI_ACTIVE -d <dir>/valu_W -o valu --output-format csv "
+            "-- python3 bench.py --profile-workload W`",
+            f"- measured times: `python3 bench.py --suite --no-cpu-baseline` ({os.path.basename(suite_log)}, "
+            "each workload timed alone)", "",
+            "Per dispatch of the workload's kernel (averages over its 23 dispatches).  VALU issue time = "
+            f"SQ_INSTS_VALU x {CYCLES_PER_VALU} cycles / {SIMDS} SIMDs / {CLOCK_GHZ} GHz: how long every SIMD "
+            "would spend issuing vector instructions if the work were spread evenly (a lower bound: some "
+            "instructions take longer than 4 cycles).  GRBM_GUI_ACTIVE is collected but not used: under "
+            "counter collection it includes the profiler's own time and sums the 8 XCDs.", "",
+            "| workload | kernel | wavefronts | VALU instr / wavefront | VALU lane-ops / element | "
+            "VALU issue time (us) | measured us per call | issue / measured |",
+            "|---|---|---|---|---|---|---|---|"]
+    for path in csvs:
+        w = os.path.basename(os.path.dirname(os.path.abspath(path)))
+        w = w[len("valu_"):] if w.startswith("valu_") else w
+        vals = {}
+        for r in _csv(path):
+            name = r["Kernel_Name"]
+            if "nq::" not in name:
+                continue
+            vals.setdefault((name, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        for k in sorted({k for k, _ in vals}):
+            avg = {c: sum(v) / len(v) for (kk, c), v in vals.items() if kk == k}
+            waves, insts = avg.get("SQ_WAVES", 0), avg.get("SQ_INSTS_VALU", 0)
+            issue_us = insts * CYCLES_PER_VALU / SIMDS / (CLOCK_GHZ * 1e3)
+            el = suite.get(w, {})
+            per_el = f"{insts * 64 / el['elements']:.1f}" if el.get("elements") else ""
+            t = el.get("us_per_call_graph")
+            frac = f"{issue_us / t:.2f}" if t else ""
+            rows.append(f"| {w} | `{_short_name(k, 70)}` | {waves:.0f} | {insts / max(waves, 1):.0f} | {per_el} | "
+                        f"{issue_us:.2f} | {t if t else ''} | {frac} |")
+    rows += ["", "VALU lane-ops per element count every lane of every wavefront (64 per instruction) over the "
+             "workload's elements, idle lanes past a row's end included.  Where two kernels form one workload "
+             "(the unfused pair) the measured time is the pair's."]
+    open(out_md, "w").write("\n".join(rows) + "\n")
+
+
 # ------------------------------------------------------------------ main --
 
-def run_suite(torch, nq):
+def suite_cases(torch, nq):
+    """(name, factory) of every suite workload."""
     cases = [
         ("rms_small", lambda: RmsFp8Case(torch, nq, 64, 256)),
         ("rms_2816_m1", lambda: RmsFp8Case(torch, nq, 1, 2816, sets=64)),
@@ -664,11 +726,17 @@ def run_suite(torch, nq):
         ("copy_161MB", lambda: CopyCase(torch, nq, 161_524_736)),
         ("launch_floor_copy_32B", lambda: CopyCase(torch, nq, 32)),
     ]
+    return cases
+
+
+def run_suite(torch, nq):
+    cases = suite_cases(torch, nq)
     built, lines = [], []
     for name, make in cases:  # each workload alone: warm replays, then timed replays back to back
         case = make()
         us_graph = time_graph(torch, case) * 1e3
         lines.append({"workload": name, "label": case.label, "bytes_per_call": case.bytes,
+                      **({"elements": case.elements} if hasattr(case, "elements") else {}),
                       **({"fused_bytes_per_call": case.fused_bytes} if hasattr(case, "fused_bytes") else {}),
                       "us_per_call_graph": round(us_graph, 3),
                       "us_per_launch_events": round(time_launch_events(torch, case, 50) * 1e3, 3),
@@ -695,6 +763,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-mode", action="store_true",
                     help="short fixed run for rocprofv3: copy reference + main kernel steps")
+    ap.add_argument("--profile-workload", metavar="NAME",
+                    help="short fixed run of one suite workload (3 + 20 calls) for rocprofv3 --pmc")
+    ap.add_argument("--summarize-valu", nargs="+", metavar=("SUITE_LOG", "COUNTER_CSV"),
+                    help="write profiles/valu_counters.md from a suite log and rocprofv3 --pmc CSVs "
+                         "(one per workload, in directories named valu_<workload>)")
     ap.add_argument("--summarize-suite", metavar="STATS_CSV",
                     help="write profiles/suite_kernel_trace.md from a rocprofv3 --stats CSV of the suite")
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
@@ -703,6 +776,10 @@ def main():
 
     if args.summarize_suite:
         summarize_suite(args.summarize_suite, SUITE_TRACE_SUMMARY)
+        return
+
+    if args.summarize_valu:
+        summarize_valu(args.summarize_valu[0], args.summarize_valu[1:], VALU_SUMMARY)
         return
 
     if args.summarize:
@@ -728,6 +805,15 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     from fp4_quantization_amd import nq
+
+    if args.profile_workload:
+        case = dict(suite_cases(torch, nq))[args.profile_workload]()
+        h = torch.cuda.current_stream().cuda_stream
+        for i in range(23):
+            case.step(i, h)
+        torch.cuda.synchronize()
+        log(f"profile-workload {args.profile_workload} done")
+        return
 
     if args.profile_mode:
         # 10 copies of exactly 64 MiB read + 64 MiB written, then 20 main steps
