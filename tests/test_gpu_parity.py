@@ -1136,3 +1136,48 @@ def test_group_scales_of_tiny_groups(nq, orc, ue8m0):
     assert np.all((fo["scale"] == 0) | (fo["scale"] > 2.0 ** -128))
     assert_bits_equal(got["scale"].view(np.uint32), fo["scale"].view(np.uint32), "fused scales")
     assert_bits_equal(got["q"], fo["q"], "fused codes")
+
+
+def test_non_finite_inputs_stay_in_their_row(nq, orc):
+    """NaN and infinite inputs are outside the contract, but they must not
+    reach other rows (or other groups): every row without one equals the
+    oracle bit for bit, for each row entry point."""
+    note("non-finite inputs stay in their row")
+    M, d = 12, 2816
+    w = W.rms_2816(M, seed=60)
+    x = w["x"].copy()
+    x[3, 100] = 0x7FC0          # NaN
+    x[5, 7] = 0x7F80            # +inf
+    x[8, 2000] = 0xFF80         # -inf
+    bad = np.array([3, 5, 8])
+    good = np.setdiff1d(np.arange(M), bad)
+    w2 = dict(w, x=x)
+    got = run_rms_fp8(nq, w2)
+    o = orc.fused_add_rmsnorm_quant_fp8(x[good], w["residual"][good], w["gamma"], w["eps"])
+    assert_bits_equal(got["q"][good], o["q"], "rms codes of finite rows")
+    assert_bits_equal(got["scale"][good].view(np.uint32), o["scale"].view(np.uint32), "rms scales of finite rows")
+    got = run_rms_group(nq, w2)
+    og = orc.fused_add_rmsnorm_quant_fp8_group(x[good], w["residual"][good], w["gamma"], w["eps"])
+    assert_bits_equal(got["q"][good], og["q"], "fused group codes of finite rows")
+    q, s = run_group(nq, x, False)
+    gq = orc.per_token_group_quant_fp8(x, 128)
+    finite_groups = np.isfinite(W.bf16_bits_to_f32(x)).reshape(M, -1, 128).all(axis=2)
+    assert_bits_equal(s[finite_groups].view(np.uint32), gq["scale"][finite_groups].view(np.uint32),
+                      "group scales of finite groups")
+    wl = W.layernorm_rows(M=M, d=d, seed=61)
+    xl = wl["x"].copy()
+    xl[3, 100], xl[5, 7] = 0x7FC0, 0x7F80
+    ql = run_ln(nq, dict(wl, x=xl))
+    goodl = np.setdiff1d(np.arange(M), [3, 5])
+    ol = orc.layernorm_quant_fp8(xl[goodl], wl["gamma"], wl["beta"], wl["eps"], wl["scale"])
+    assert_bits_equal(ql[goodl], ol["q"], "layernorm codes of finite rows")
+    wn = dict(W.rms_rows(M, 7168, 0, 1.0, seed=62))
+    xn = wn["x"].copy()
+    xn[3, 100] = 0x7FC0
+    sg = calibrated_sg(orc, dict(wn, x=np.delete(xn, 3, axis=0), residual=np.delete(wn["residual"], 3, axis=0),
+                                 M=M - 1))
+    gotn = run_nvfp4(nq, dict(wn, x=xn), sg)
+    goodn = np.setdiff1d(np.arange(M), [3])
+    on = orc.rmsnorm_quant_nvfp4(xn[goodn], wn["residual"][goodn], wn["gamma"], wn["eps"], sg)
+    assert_bits_equal(gotn["sf"][goodn], on["sf"], "nvfp4 block scales of finite rows")
+    assert_bits_equal(gotn["q"][goodn], on["q"], "nvfp4 codes of finite rows")
