@@ -2,16 +2,17 @@
 // packed E2M1 elements, one e4m3 scale per 16 elements, a global fp32 scale.
 //
 // Pages: [NVFP4] "RMSNorm nvfp4 quant fusion for DS V3.2 / Kimi-K2.5"
-// ("Description": the norm is computed in registers and the packed E2M1 +
-// per-block e4m3 representation is emitted in the same pass; a residual-less
-// variant reads a row-strided column slice in place; commit notes: optional
-// bf16 norm output, a fresh residual buffer, hidden % 16 == 0, loop bounds
-// uniform across the lanes that shuffle together).
+// ("Description": one pass normalizes in registers and writes the 4-bit
+// codes with their 16-element e4m3 scales; the residual-less form takes a
+// column slice of wider rows through a row stride, without a copy; commit
+// notes: optional bf16 norm output, a fresh residual buffer, hidden % 16 ==
+// 0, loop bounds uniform across the lanes that shuffle together).
 //
 // With NQ_FLAG_BF16_SOURCE the values quantized are bf16(y), the rounding a
 // bf16 norm_out stores, so the codes and block scales equal the standalone
-// quantizer applied to norm_out ([NVFP4] commit notes: re-quantizing the
-// fused op's own norm_out reproduces its outputs bit for bit).
+// quantizer applied to norm_out ([NVFP4] commit notes: the fused op's codes
+// and scale factors match, bit for bit, what the standalone quantizer makes
+// of the norm_out it returns).
 //
 // The row is held in registers exactly as in the per-token FP8 kernel.  A
 // 16-element block is two adjacent chunks, owned by lanes t and t^1 of the

@@ -3,11 +3,11 @@
 // (2) FP8 quantization of bf16 rows with per-token (or static) scales.
 //
 // Pages: [FUSE] "Fusing RMSNorm and FP8 Quantization Under torch.compile"
-// ("TL;DR", "Where norm+quant sits": the norm writes a bf16 activation and a
-// second kernel reads it back, reduces it and quantizes it -- one extra HBM
-// round trip and one extra rounding); [LNQ] "feat: fused FP8 quantization
-// output for LayerNorm" ("Description": about 7 bytes of traffic per
-// element unfused against 3 fused).  Run back to back they give the codes of
+// ("TL;DR", "Where norm+quant sits": the norm stores a bf16 activation that
+// a separate quantization kernel loads again for its maximum and its codes --
+// one more HBM round trip and one more rounding); [LNQ] "feat: fused FP8
+// quantization output for LayerNorm" ("Description": roughly 7 bytes move
+// per element in two kernels, 3 in one).  Run back to back they give the codes of
 // the unfused reference and the time the fusion saves on this GPU.
 //
 // Both are row kernels on the same team layout as the fused ones: (1) is the

@@ -5,10 +5,10 @@ binding (``fp4_quantization_amd.nq``) on PyTorch's current stream; every step
 of the computation runs in the HIP kernels.  Outputs are fresh tensors, never
 views of or writes into the inputs, so the compiler sees no aliasing: the
 residual sum comes back as a new tensor rather than updating the residual in
-place ("RMSNorm nvfp4 quant fusion for DS V3.2 / Kimi-K2.5", commit notes:
-the fused add op returns the residual sum as a fresh tensor, and its fake
-implementation allocates with new_empty so the trace holds no layout-copying
-node).  Each op has a fake implementation (shapes and dtypes only) so it
+place ("RMSNorm nvfp4 quant fusion for DS V3.2 / Kimi-K2.5", commit notes: the
+fused add op hands back x + residual in a newly allocated tensor, and its
+fake implementation allocates with new_empty so the trace holds no
+layout-copying node).  Each op has a fake implementation (shapes and dtypes only) so it
 traces under FakeTensor / torch.compile without running.
 
 FP8 codes are returned as ``torch.float8_e4m3fn`` or, with ``e5m2=True``,

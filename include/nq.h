@@ -312,8 +312,8 @@ nq_status nq_rmsnorm_quant_nvfp4(
  * The same NVFP4 op with options: flags any of NQ_FLAG_BF16_SOURCE (the
  * values quantized are bf16(y_i), so the codes and block scales equal the
  * standalone quantizer applied to the bf16 norm_out -- [NVFP4] commit notes:
- * re-quantizing the fused op's own norm_out reproduces its outputs bit for
- * bit), NQ_FLAG_GAMMA_BF16 (gamma is bf16).  NQ_ERR_ARG for other bits.
+ * the fused op's outputs match, bit for bit, the standalone quantizer run on
+ * the norm_out it returns), NQ_FLAG_GAMMA_BF16 (gamma is bf16).  NQ_ERR_ARG for other bits.
  */
 nq_status nq_rmsnorm_quant_nvfp4_ex(
     const uint16_t* x, int64_t ld_x,

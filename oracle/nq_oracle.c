@@ -255,8 +255,8 @@ static void add_rmsnorm_row(const uint16_t *x, const uint16_t *r, uint16_t *r_ou
 /* Per-token dynamic FP8 of one fp32 row ([FUSE] "Where norm+quant sits";
  * the formula itself is not printed there, so this follows the plain
  * reading: scale = amax / 448, code = E4(y / scale), one division per
- * element ([GRP] "Details": per-token FP8 keeps exact per-element
- * division); for e5m2 the divisor is 57344.  An all-zero row stores scale
+ * element ([GRP] "Details": the per-token path was left dividing each
+ * element exactly); for e5m2 the divisor is 57344.  An all-zero row stores scale
  * 0 and codes 0. */
 static float quant_fp8_dynamic_row(const float *y, int64_t d, uint8_t *q, int32_t fmt)
 {

@@ -156,8 +156,8 @@ def test_rmsnorm_fp8_constant_row_and_zero_row(orc):
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 def test_per_token_quant_divides_per_element(orc, fmt):
-    """Per-token FP8 keeps one division per element ([GRP] "Details": per-token
-    FP8 keeps exact per-element division).  Rows are built from fp32 values
+    """Per-token FP8 keeps one division per element ([GRP] "Details": the
+    per-token path was left dividing each element exactly).  Rows are built from fp32 values
     for which RN(y/s) and RN(y * RN(1/s)) fall on different sides of an FP8
     rounding boundary; the oracle must give the division's code.  The same
     row step serves the RMSNorm and the dynamic LayerNorm ops."""
