@@ -312,3 +312,55 @@ def test_binding_constants_match_the_header():
     for k, v in defs.items():
         if hasattr(nq, k):
             assert getattr(nq, k) == v, k
+
+
+# ---------------------------------------------------- alias detection ------
+# The host rejects an output that overlaps an input or another output
+# (NQ_ERR_ALIAS), except residual_out == residual_in exactly.  Random
+# placements of every tensor of the per-token entry point in a small fake
+# address space are checked against an independent interval model: with
+# every other argument valid, the call must be refused as aliased exactly
+# when the model finds a forbidden overlap, and otherwise pass validation
+# (then the launch fails on a machine without a GPU: NQ_ERR_LAUNCH).
+
+NQ_ERR_LAUNCH = -5
+
+
+def _span(p, rows, ld, cols, esize):
+    return None if p is None else (p, p + ((rows - 1) * ld + cols) * esize)
+
+
+def _overlap(a, b):
+    return a is not None and b is not None and a[0] < b[1] and b[0] < a[1]
+
+
+def test_alias_detection_matches_an_interval_model(lib):
+    hyp = pytest.importorskip("hypothesis")
+    st = pytest.importorskip("hypothesis.strategies")
+    base = 0x200000
+
+    @hyp.settings(max_examples=1500, deadline=None, derandomize=True)
+    @hyp.given(M=st.integers(1, 3), d=st.integers(1, 40), pads=st.lists(st.integers(0, 6), min_size=5, max_size=5),
+               offs=st.lists(st.integers(0, 300), min_size=8, max_size=8), residual=st.sampled_from(["none", "fresh", "inplace"]),
+               static=st.booleans(), with_norm=st.booleans())
+    def check(M, d, pads, offs, residual, static, with_norm):
+        ldx, ldr, ldro, ldq, ldn = (d + p for p in pads)
+        x, r, ro, g, q, s, n, ss = (base + 2 * o for o in offs)
+        if residual == "none":
+            r = ro = None
+        elif residual == "inplace":
+            ro, ldro = r, ldr
+        if not static:
+            ss = None
+        if not with_norm:
+            n = None
+        ins = [_span(x, M, ldx, d, 2), _span(r, M, ldr, d, 2), _span(g, 1, d, d, 4), _span(ss, 1, 1, 1, 4)]
+        outs = [_span(ro, M, ldro, d, 2), _span(q, M, ldq, d, 1), None if static else _span(s, 1, M, M, 4),
+                _span(n, M, ldn, d, 2)]
+        bad = any(_overlap(o, i) and not (ii == 1 and oi == 0 and o == i)
+                  for oi, o in enumerate(outs) for ii, i in enumerate(ins))
+        bad = bad or any(_overlap(outs[a], outs[b]) for a in range(4) for b in range(a + 1, 4))
+        got = lib.nq_fused_add_rmsnorm_quant_fp8(x, ldx, r, ldr, ro, ldro, g, 1e-6, ss, q, ldq, s, n, ldn, M, d, None)
+        assert got == (NQ_ERR_ALIAS if bad else NQ_ERR_LAUNCH), (M, d, pads, offs, residual, static, with_norm, got)
+
+    check()
