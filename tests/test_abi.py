@@ -364,3 +364,75 @@ def test_alias_detection_matches_an_interval_model(lib):
         assert got == (NQ_ERR_ALIAS if bad else NQ_ERR_LAUNCH), (M, d, pads, offs, residual, static, with_norm, got)
 
     check()
+
+
+def _expect(ins, outs, exact=None):
+    """NQ_ERR_ALIAS when an output overlaps an input (other than the exact
+    pair `exact` = (input index, output index) coinciding) or another output."""
+    bad = any(_overlap(o, i) and not (exact == (ii, oi) and o == i)
+              for oi, o in enumerate(outs) for ii, i in enumerate(ins))
+    bad = bad or any(_overlap(outs[a], outs[b]) for a in range(len(outs)) for b in range(a + 1, len(outs)))
+    return NQ_ERR_ALIAS if bad else NQ_ERR_LAUNCH
+
+
+def test_alias_detection_other_entry_points(lib):
+    """The same interval model for the fused group, NVFP4 and LayerNorm entry
+    points (a column-slice input's unread columns count as part of its range)."""
+    hyp = pytest.importorskip("hypothesis")
+    st = pytest.importorskip("hypothesis.strategies")
+    base = 0x300000
+    offs_s = st.lists(st.integers(0, 400), min_size=8, max_size=8)
+    pads_s = st.lists(st.integers(0, 6), min_size=6, max_size=6)
+    res_s = st.sampled_from(["none", "fresh", "inplace"])
+
+    def residual_ptrs(mode, r, ro, ldr, ldro):
+        if mode == "none":
+            return None, None, ldr, ldro
+        if mode == "inplace":
+            return r, r, ldr, ldr
+        return r, ro, ldr, ldro
+
+    @hyp.settings(max_examples=600, deadline=None, derandomize=True)
+    @hyp.given(M=st.integers(1, 3), gsel=st.integers(1, 2), pads=pads_s, offs=offs_s, mode=res_s,
+               with_norm=st.booleans())
+    def group(M, gsel, pads, offs, mode, with_norm):
+        d, G = 128 * gsel, gsel
+        ldx, ldr, ldro, ldq, lds, ldn = d + pads[0], d + pads[1], d + pads[2], d + pads[3], G + pads[4], d + pads[5]
+        x, r, ro, g, q, s, n, _ = (base + 4 * o for o in offs)
+        r, ro, ldr, ldro = residual_ptrs(mode, r, ro, ldr, ldro)
+        n = n if with_norm else None
+        ins = [_span(x, M, ldx, d, 2), _span(r, M, ldr, d, 2), _span(g, 1, d, d, 4)]
+        outs = [_span(ro, M, ldro, d, 2), _span(q, M, ldq, d, 1), _span(s, M, lds, G, 4), _span(n, M, ldn, d, 2)]
+        got = lib.nq_fused_add_rmsnorm_quant_fp8_group(x, ldx, r, ldr, ro, ldro, g, 1e-6, 128, 0, 0, q, ldq, s,
+                                                       lds, n, ldn, M, d, None)
+        assert got == _expect(ins, outs, (1, 0)), ("group", M, d, pads, offs, mode, with_norm, got)
+
+    @hyp.settings(max_examples=600, deadline=None, derandomize=True)
+    @hyp.given(M=st.integers(1, 3), dsel=st.integers(1, 4), pads=pads_s, offs=offs_s, mode=res_s,
+               with_norm=st.booleans())
+    def nvfp4(M, dsel, pads, offs, mode, with_norm):
+        d = 16 * dsel
+        ldx, ldr, ldro, ldq, ldsf, ldn = d + pads[0], d + pads[1], d + pads[2], d // 2 + pads[3], d // 16 + pads[4], d + pads[5]
+        x, r, ro, g, gs, q, sf, n = (base + 2 * o for o in offs)
+        r, ro, ldr, ldro = residual_ptrs(mode, r, ro, ldr, ldro)
+        n = n if with_norm else None
+        ins = [_span(x, M, ldx, d, 2), _span(r, M, ldr, d, 2), _span(g, 1, d, d, 4), _span(gs, 1, 1, 1, 4)]
+        outs = [_span(ro, M, ldro, d, 2), _span(q, M, ldq, d // 2, 1), _span(sf, M, ldsf, d // 16, 1),
+                _span(n, M, ldn, d, 2)]
+        got = lib.nq_rmsnorm_quant_nvfp4(x, ldx, r, ldr, ro, ldro, g, 1e-6, gs, q, ldq, sf, ldsf, n, ldn, M, d, None)
+        assert got == _expect(ins, outs, (1, 0)), ("nvfp4", M, d, pads, offs, mode, with_norm, got)
+
+    @hyp.settings(max_examples=600, deadline=None, derandomize=True)
+    @hyp.given(M=st.integers(1, 3), d=st.integers(1, 40), pads=pads_s, offs=offs_s, static=st.booleans())
+    def layernorm(M, d, pads, offs, static):
+        ldx, ldq = d + pads[0], d + pads[1]
+        x, g, b, sc, q, so, _, _ = (base + 2 * o for o in offs)
+        sc = sc if static else None
+        ins = [_span(x, M, ldx, d, 2), _span(g, 1, d, d, 4), _span(b, 1, d, d, 4), _span(sc, 1, 1, 1, 4)]
+        outs = [_span(q, M, ldq, d, 1), None if static else _span(so, 1, M, M, 4)]
+        got = lib.nq_layernorm_quant_fp8_ex(x, ldx, g, b, 1e-5, sc, 0, q, ldq, so, M, d, None)
+        assert got == _expect(ins, outs), ("layernorm", M, d, pads, offs, static, got)
+
+    group()
+    nvfp4()
+    layernorm()
