@@ -1,0 +1,31 @@
+"""CPU checks of bench.py's host side: the one-GPU refusal, the byte model
+of the headline step, and that the committed HBM-counter summary was taken on
+the current kernel sources (so the bench line reports `roofline.traffic`)."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_headline_bytes_per_step():
+    # inputs x and residual, residual write, e4m3 codes, fp32 scales, gamma once
+    M, d = 8192, 2816
+    assert bench.case_bytes_8192() == M * (2 * d + 2 * d + 2 * d + d + 4) + 4 * d == 161_524_736
+
+
+def test_counter_summary_matches_the_kernel_sources():
+    t = bench.read_traffic()
+    assert t is not None, ("profiles/rmsnorm_fp8_m8192_d2816_hbm_counters.md was taken on other kernel "
+                           "sources: profile the current kernel again")
+    assert 0.99 < t / bench.case_bytes_8192() < 1.05
