@@ -656,6 +656,59 @@ def test_nvfp4_mode_b_quantizes_bf16_of_y(orc):
     assert np.array_equal(packed, b["q"])
 
 
+def test_nvfp4_sign_symmetry(orc):
+    """Negating x and the residual negates z and y exactly, so the block
+    scales are unchanged and every non-zero element code flips its sign bit
+    (zeros keep their code up to the sign of zero)."""
+    w = W.nvfp4_7168(M=6, seed=3)
+    sg = W.NVFP4_NOMINAL_GLOBAL_SCALE
+    a = orc.rmsnorm_quant_nvfp4(w["x"], w["residual"], w["gamma"], w["eps"], sg)
+    b = orc.rmsnorm_quant_nvfp4(w["x"] ^ np.uint16(0x8000), w["residual"] ^ np.uint16(0x8000), w["gamma"],
+                                w["eps"], sg)
+    assert np.array_equal(a["sf"], b["sf"])
+    ca, _ = unpack_e2m1(a["q"])
+    cb, _ = unpack_e2m1(b["q"])
+    nz = (ca & 7) != 0
+    assert np.array_equal(cb[nz], ca[nz] ^ 8)
+    assert np.array_equal(cb[~nz] & 7, ca[~nz] & 7)
+
+
+def test_nvfp4_global_scale_equivariance(orc):
+    """Halving the global scale doubles G: every block scale that stays a
+    normal, unsaturated e4m3 value moves up one binade (its code by +8),
+    while m_b = G / value(sf) and so every element code stay the same.  A
+    block-scale formula that used s_g the wrong way round, or applied it to
+    the elements, fails this."""
+    w = W.nvfp4_7168(M=6, seed=4)
+    sg = W.NVFP4_NOMINAL_GLOBAL_SCALE * 4   # block scales well inside the normal range
+    a = orc.rmsnorm_quant_nvfp4(w["x"], w["residual"], w["gamma"], w["eps"], sg)
+    b = orc.rmsnorm_quant_nvfp4(w["x"], w["residual"], w["gamma"], w["eps"], float(np.float32(sg) / 2))
+    ok = (a["sf"] >= 0x08) & (a["sf"] <= 0x7E - 8)   # normal before and after, no saturation
+    assert ok.mean() > 0.99
+    assert np.array_equal(b["sf"][ok], a["sf"][ok] + 8)
+    blocks_ok = np.repeat(ok, 8, axis=1)              # 8 packed bytes per 16-element block
+    assert np.array_equal(b["q"][blocks_ok], a["q"][blocks_ok])
+
+
+def test_nvfp4_permutation_within_blocks(orc):
+    """RMSNorm's statistic is a sum (exact in binary64), so permuting the
+    elements of every 16-element block (x, residual and gamma together)
+    permutes the element codes the same way and leaves the block scales
+    unchanged: each code belongs to its own element."""
+    w = W.nvfp4_7168(M=4, seed=5)
+    sg = W.NVFP4_NOMINAL_GLOBAL_SCALE
+    rng = np.random.default_rng(9)
+    perm = rng.permutation(16)
+    idx = (np.arange(7168).reshape(-1, 16)[:, perm]).ravel()
+    a = orc.rmsnorm_quant_nvfp4(w["x"], w["residual"], w["gamma"], w["eps"], sg)
+    b = orc.rmsnorm_quant_nvfp4(np.ascontiguousarray(w["x"][:, idx]), np.ascontiguousarray(w["residual"][:, idx]),
+                                np.ascontiguousarray(w["gamma"][idx]), w["eps"], sg)
+    assert np.array_equal(a["sf"], b["sf"])
+    ca, _ = unpack_e2m1(a["q"])
+    cb, _ = unpack_e2m1(b["q"])
+    assert np.array_equal(cb, ca[:, idx])
+
+
 # ------------------------------------------------ byte model pins ----------
 
 def test_byte_model_matches_page_figures():
