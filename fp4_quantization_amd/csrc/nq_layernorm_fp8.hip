@@ -29,6 +29,7 @@ struct LnFp8Args {
     int64_t M;
     int d;
     float eps;
+    double inv_d;           // RN(1 / d), formed on the host
     bool e5m2;              // output format (e4m3 otherwise)
     bool vec_bf16;          // gamma and beta are bf16
 };
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
     }
     gb.publish(lds_gb);
     acc = team_sum<TEAM>(acc, lds_mean);
-    const float mu = (float)(acc / (double)d);
+    const float mu = (float)div_by_len(acc, (double)d, a.inv_d);
     __builtin_amdgcn_sched_barrier(0);
 
     // c = x - mean (binary32), held in registers (at most 32 per lane);
@@ -95,8 +96,8 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
         acc2 += e < d ? part : 0.0;
     }
     acc2 = team_sum<TEAM>(acc2, lds_var);
-    const float var = (float)(acc2 / (double)d);
-    const float rstd = 1.0f / sqrtf(var + a.eps);
+    const float var = (float)div_by_len(acc2, (double)d, a.inv_d);
+    const float rstd = rsqrt_rn(var + a.eps);
     __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (!DYN) {
@@ -211,7 +212,7 @@ extern "C" nq_status nq_layernorm_quant_fp8_ex(
     LnFp8Args a;
     a.x = x; a.gamma = gamma; a.beta = beta; a.scale = scale; a.q = q_out;
     a.scale_out = scale ? nullptr : scale_out;
-    a.ld_x = ld_x; a.ld_q = ld_q; a.M = M; a.d = (int)d; a.eps = eps;
+    a.ld_x = ld_x; a.ld_q = ld_q; a.M = M; a.d = (int)d; a.eps = eps; a.inv_d = 1.0 / (double)d;
     a.e5m2 = (flags & NQ_FLAG_E5M2) != 0;
     a.vec_bf16 = (flags & NQ_FLAG_GAMMA_BF16) != 0;
     if (!launch_row_shape<LnFp8Kernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;

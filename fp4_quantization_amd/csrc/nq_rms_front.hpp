@@ -12,8 +12,9 @@
 //   z_i  = bf16(x_i + r_i), or x_i itself when residual-less (RES false: a
 //          separate instance with no add, repacking or write-back)
 //   rstd = 1 / sqrt(sum z_i^2 / d + eps), the sum in binary64 (every z_i^2 is
-//          exact there), rounded to binary32 once, so the result does not
-//          depend on the reduction tree.
+//          exact there), its quotient by d correctly rounded in binary64 and
+//          then to binary32, so the result does not depend on the reduction
+//          tree; the square root and the reciprocal are each correctly rounded.
 #pragma once
 
 #include "nq_device.hpp"
@@ -29,8 +30,9 @@ namespace nq {
 // published before the reduction's barrier.
 template <int TEAM, int CPL, bool VEC, bool RES, class SV>
 __device__ __forceinline__ float rms_front(const uint16_t* x, int64_t ld_x, const uint16_t* r, int64_t ld_r,
-                                           uint16_t* ro, int64_t ld_ro, const RowMap& m, int t, int d, float eps,
-                                           SV& vecs, typename SV::Lds& lds_vec, double* lds_sum, uint4 (&zw)[CPL])
+                                           uint16_t* ro, int64_t ld_ro, const RowMap& m, int t, int d,
+                                           double inv_d, float eps, SV& vecs, typename SV::Lds& lds_vec,
+                                           double* lds_sum, uint4 (&zw)[CPL])
 {
     const RowIO<VEC, kLoadStream, uint16_t> xio(x, ld_x, m, d);
     double acc = 0.0;
@@ -88,8 +90,8 @@ __device__ __forceinline__ float rms_front(const uint16_t* x, int64_t ld_x, cons
 
     vecs.publish(lds_vec);
     acc = team_sum<TEAM>(acc, lds_sum);
-    const float ms = (float)(acc / (double)d);
-    const float rstd = 1.0f / sqrtf(ms + eps);
+    const float ms = (float)div_by_len(acc, (double)d, inv_d);
+    const float rstd = rsqrt_rn(ms + eps);
     __builtin_amdgcn_sched_barrier(0);
     return rstd;
 }

@@ -38,6 +38,15 @@ struct RmsFp8Args {
     int64_t M;
     int d;
     float eps;
+    double inv_d;           // RN(1 / d), formed on the host
+};
+// Two 64-byte lines of the kernel-argument segment: a third line measured
+// about 70 ns (2 %) slower for a single-row call on MI355X.
+static_assert(sizeof(RmsFp8Args) <= 128, "kernel arguments fit two 64-byte lines");
+
+// Host-side launch request: the kernel arguments and the instance choices.
+struct RmsFp8Launch {
+    RmsFp8Args k;
     bool e5m2;              // output format (e4m3 otherwise)
     bool gamma_bf16;
 };
@@ -58,8 +67,8 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
     SV gamma({a.gamma}, d);
 
     uint4 zw[CPL];
-    const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
-                                                 lds_gamma, lds_sum, zw);
+    const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.inv_d,
+                                                      a.eps, gamma, lds_gamma, lds_sum, zw);
 
     // y = (z * rstd) * gamma, held in fp32 registers (at most 32 per lane),
     // its absolute maximum, and the optional bf16 copy of y.
@@ -125,20 +134,20 @@ struct RmsFp8Kernel {
     template <bool STAGE>
     static constexpr int block() { return row_block<TEAM, CPL, 1, VEC, STAGE>(); }
     template <bool STAGE>
-    static void launch(const RmsFp8Args& a, dim3 grid, dim3 block, hipStream_t s)
+    static void launch(const RmsFp8Launch& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        if (a.r != nullptr) go<STAGE, true>(a, grid, block, s);
+        if (a.k.r != nullptr) go<STAGE, true>(a, grid, block, s);
         else go<STAGE, false>(a, grid, block, s);
     }
     template <bool STAGE, bool RES>
-    static void go(const RmsFp8Args& a, dim3 grid, dim3 block, hipStream_t s)
+    static void go(const RmsFp8Launch& a, dim3 grid, dim3 block, hipStream_t s)
     {
         if (a.gamma_bf16) {
-            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2, true, RES>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3, true, RES>), grid, block, 0, s, a);
+            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2, true, RES>), grid, block, 0, s, a.k);
+            else hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3, true, RES>), grid, block, 0, s, a.k);
         } else {
-            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2, false, RES>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3, false, RES>), grid, block, 0, s, a);
+            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E5M2, false, RES>), grid, block, 0, s, a.k);
+            else hipLaunchKernelGGL((k_add_rmsnorm_fp8<TEAM, CPL, VEC, STAGE, Fp8::E4M3, false, RES>), grid, block, 0, s, a.k);
         }
     }
 };
@@ -188,14 +197,15 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_ex(
     const RowShape shape = pick_row_shape(M, d, vec);
     if (shape.team == 0) return NQ_ERR_SHAPE;
 
-    RmsFp8Args a;
+    RmsFp8Launch L;
+    RmsFp8Args& a = L.k;
     a.x = x; a.r = residual_in; a.ro = residual_out; a.gamma = gamma;
     a.static_scale = static_scale; a.q = q_out; a.scale_out = scale_out; a.norm_out = norm_out;
     a.ld_x = ld_x; a.ld_r = ld_r; a.ld_ro = ld_ro; a.ld_q = ld_q; a.ld_n = ld_n;
-    a.M = M; a.d = (int)d; a.eps = eps;
-    a.e5m2 = (flags & NQ_FLAG_E5M2) != 0;
-    a.gamma_bf16 = (flags & NQ_FLAG_GAMMA_BF16) != 0;
-    if (!launch_row_shape<RmsFp8Kernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
+    a.M = M; a.d = (int)d; a.eps = eps; a.inv_d = 1.0 / (double)d;
+    L.e5m2 = (flags & NQ_FLAG_E5M2) != 0;
+    L.gamma_bf16 = (flags & NQ_FLAG_GAMMA_BF16) != 0;
+    if (!launch_row_shape<RmsFp8Kernel>(shape, L, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
 }
 

@@ -36,6 +36,7 @@ struct RmsGroupArgs {
     int64_t M;
     int d;
     float eps;
+    double inv_d;           // RN(1 / d), formed on the host
     int ue8m0;              // scales rounded up to powers of two
     int bf16_source;        // quantize bf16(y) (the unfused pipeline's values)
     bool e5m2;              // output format (e4m3 otherwise)
@@ -58,8 +59,8 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8_group(RmsGroupArgs a)
     SV gamma({a.gamma}, d);
 
     uint4 zw[CPL];
-    const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
-                                                 lds_gamma, lds_sum, zw);
+    const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.inv_d,
+                                                      a.eps, gamma, lds_gamma, lds_sum, zw);
 
     const RowIO<VEC, kStoreRows, uint16_t> nio(a.norm_out, a.ld_n, m, d);
     const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d);
@@ -183,7 +184,7 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_group(
     a.x = x; a.r = residual_in; a.ro = residual_out; a.gamma = gamma;
     a.q = q_out; a.scale_out = scale_out; a.norm_out = norm_out;
     a.ld_x = ld_x; a.ld_r = ld_r; a.ld_ro = ld_ro; a.ld_q = ld_q; a.ld_s = ld_s; a.ld_n = ld_n;
-    a.M = M; a.d = (int)d; a.eps = eps;
+    a.M = M; a.d = (int)d; a.eps = eps; a.inv_d = 1.0 / (double)d;
     a.ue8m0 = scale_mode == NQ_SCALE_UE8M0;
     a.bf16_source = (flags & NQ_FLAG_BF16_SOURCE) != 0;
     a.e5m2 = (flags & NQ_FLAG_E5M2) != 0;

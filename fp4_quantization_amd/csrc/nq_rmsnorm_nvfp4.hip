@@ -39,6 +39,7 @@ struct RmsFp4Args {
     int64_t M;
     int d;
     float eps;
+    double inv_d;           // RN(1 / d), formed on the host
     bool bf16_source;  // quantize bf16(y): the standalone quantizer applied to norm_out
     bool gamma_bf16;
 };
@@ -63,8 +64,8 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
     const float sg = a.global_scale[0];  // issued early: read on the device at run time
 
     uint4 zw[CPL];
-    const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
-                                                 lds_gamma, lds_sum, zw);
+    const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.inv_d,
+                                                      a.eps, gamma, lds_gamma, lds_sum, zw);
     const float G = 1.0f / sg;  // encode scale
     // The element multiplier depends only on the block-scale code: one
     // correctly rounded quotient per code and block instead of one per chunk.
@@ -189,7 +190,7 @@ extern "C" nq_status nq_rmsnorm_quant_nvfp4_ex(
     a.x = x; a.r = residual_in; a.ro = residual_out; a.gamma = gamma;
     a.global_scale = global_scale; a.q = q_packed; a.sf = block_scale; a.norm_out = norm_out;
     a.ld_x = ld_x; a.ld_r = ld_r; a.ld_ro = ld_ro; a.ld_q = ld_q; a.ld_sf = ld_sf; a.ld_n = ld_n;
-    a.M = M; a.d = (int)d; a.eps = eps;
+    a.M = M; a.d = (int)d; a.eps = eps; a.inv_d = 1.0 / (double)d;
     a.bf16_source = (flags & NQ_FLAG_BF16_SOURCE) != 0;
     a.gamma_bf16 = (flags & NQ_FLAG_GAMMA_BF16) != 0;
     if (!launch_row_shape<RmsFp4Kernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;

@@ -31,6 +31,7 @@ struct RmsBf16Args {
     int64_t M;
     int d;
     float eps;
+    double inv_d;           // RN(1 / d), formed on the host
 };
 
 template <int TEAM, int CPL, bool VEC, bool STAGE, bool RES = true, int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
@@ -47,8 +48,8 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_bf16(RmsBf16Args a)
     SV gamma({a.gamma}, d);
 
     uint4 zw[CPL];
-    const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.eps, gamma,
-                                                 lds_gamma, lds_sum, zw);
+    const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.inv_d,
+                                                      a.eps, gamma, lds_gamma, lds_sum, zw);
 
     const RowIO<VEC, kStoreRows, uint16_t> oio(a.out, a.ld_o, m, d);
     const int t1 = opaque(t);
@@ -198,7 +199,7 @@ extern "C" nq_status nq_fused_add_rmsnorm_bf16(
     RmsBf16Args a;
     a.x = x; a.r = residual_in; a.ro = residual_out; a.gamma = gamma; a.out = out;
     a.ld_x = ld_x; a.ld_r = ld_r; a.ld_ro = ld_ro; a.ld_o = ld_o;
-    a.M = M; a.d = (int)d; a.eps = eps;
+    a.M = M; a.d = (int)d; a.eps = eps; a.inv_d = 1.0 / (double)d;
     if (!launch_row_shape<RmsBf16Kernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
 }
