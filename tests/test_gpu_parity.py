@@ -1181,3 +1181,60 @@ def test_non_finite_inputs_stay_in_their_row(nq, orc):
     on = orc.rmsnorm_quant_nvfp4(xn[goodn], wn["residual"][goodn], wn["gamma"], wn["eps"], sg)
     assert_bits_equal(gotn["sf"][goodn], on["sf"], "nvfp4 block scales of finite rows")
     assert_bits_equal(gotn["q"][goodn], on["q"], "nvfp4 codes of finite rows")
+
+
+def _scaled_rows(d, exps, seed):
+    """bf16 rows N(0,1) * 2^e for each e in `exps` (None: one row of the
+    constant 2^-63, whose mean square is exactly 2^-126)."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for e in exps:
+        if e is None:
+            rows.append(np.full(d, 2.0 ** -63, np.float32))
+        else:
+            rows.append((rng.standard_normal(d) * 2.0 ** e).astype(np.float32))
+    return W.to_bf16_bits(np.stack(rows))
+
+
+# mean squares around 1, binary32-subnormal (2^-132, 2^-140), exactly 2^-126,
+# near the top of the range (2^124) and beyond it (2^132: rstd is exactly 0)
+_RSTD_EXPS = [0, -66, -70, None, 62, 66]
+
+
+def test_rstd_extremes_rmsnorm_bit_exact(nq, orc):
+    """rstd = 1 / sqrt(mean + eps) with eps = 0 where the mean square is a
+    binary32 subnormal, the smallest normal, near the largest finite value,
+    or overflows (rstd = 0, so y = 0, scale 0): every byte and scale equals
+    the oracle's."""
+    note("rmsnorm fp8 rstd extremes, eps 0")
+    d = 2816
+    x = _scaled_rows(d, _RSTD_EXPS, seed=41)
+    M = x.shape[0]
+    r = np.zeros_like(x)
+    r[0] = W.to_bf16_bits(np.random.default_rng(42).standard_normal(d).astype(np.float32))
+    w = dict(M=M, d=d, x=x, residual=r, gamma=np.random.default_rng(43).uniform(0.5, 1.5, d).astype(np.float32),
+             eps=0.0)
+    got = run_rms_fp8(nq, w)
+    o = orc.fused_add_rmsnorm_quant_fp8(x, r, w["gamma"], 0.0, d=d)
+    assert_bits_equal(got["residual_out"], o["residual_out"], "residual_out")
+    assert_bits_equal(got["scale"].view(np.uint32), o["scale"].view(np.uint32), "scale")
+    assert_bits_equal(got["q"], o["q"], "q")
+    assert got["scale"][5] == 0 and np.all(got["q"][5] == 0)     # mean square beyond binary32
+    assert np.all(got["scale"][:5] > 0)
+
+
+def test_rstd_extremes_layernorm_bit_exact(nq, orc):
+    """The same extremes through LayerNorm's variance (beta = 0, eps = 0),
+    dynamic per-token scales."""
+    note("layernorm dynamic rstd extremes, eps 0")
+    d = 4096
+    x = _scaled_rows(d, [e for e in _RSTD_EXPS if e is not None], seed=44)
+    M = x.shape[0]
+    g = np.random.default_rng(45).uniform(0.5, 1.5, d).astype(np.float32)
+    w = dict(M=M, d=d, x=x, gamma=g, beta=np.zeros(d, np.float32), eps=0.0)
+    q, s = run_ln_ex(nq, w, 0)
+    o = orc.layernorm_quant_fp8(x, g, w["beta"], 0.0, None)
+    assert_bits_equal(s.view(np.uint32), o["scale"].view(np.uint32), "scale")
+    assert_bits_equal(q, o["q"], "q")
+    assert s[-1] == 0 and np.all(q[-1] == 0)
+    assert np.all(s[:-1] > 0)
