@@ -525,8 +525,10 @@ int or_fused_add_rmsnorm_quant_fp8_group(
 /* instead of y_i (the bf16-sourced epilogue the pull request checks        */
 /* against its standalone quantizer).                                        */
 /* PARITY UNPINNED: the block-scale operation order and the global-scale    */
-/* semantics above are printed on no page; they are the plain reading,      */
-/* checked only for self-consistency and the saturation invariants.         */
+/* semantics above are printed on no page; they are the plain reading.      */
+/* Tests pin the saturation invariants, sign symmetry, equivariance under   */
+/* halving s_g, permutation within blocks and the bf16-sourced mode, but a  */
+/* different rounding order of the block scale would pass them too.         */
 /* ------------------------------------------------------------------------ */
 int or_rmsnorm_quant_nvfp4(
     const uint16_t *x, int64_t ld_x,
