@@ -55,12 +55,20 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
     if constexpr (!DYN) scale = a.scale[0];  // issued early: read on the device at run time
 
     uint4 xw[CPL];
+    // The many-rows dynamic form (7 wavefronts per SIMD, vector-issue bound)
+    // issues its loads at raised wavefront priority, so a wavefront starting
+    // its row is not held behind others' arithmetic: 4.5 % faster on MI355X.
+    // The same hint slows the static form by 2 % and the RMSNorm kernels by
+    // 10 %.
+    constexpr bool kLoadPriority = DYN && STAGE;
+    if constexpr (kLoadPriority) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t) * 8;
         xw[j] = xio.load16(e, e < d);
     }
     gb.issue(t);
+    if constexpr (kLoadPriority) __builtin_amdgcn_s_setprio(0);
 
     // mean = sum(x) / d; every bf16 x is exact in binary64 (masked = 0).
     // The unpacked row is what c replaces below, so it stays unpacked.
