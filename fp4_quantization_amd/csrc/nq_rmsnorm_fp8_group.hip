@@ -34,11 +34,20 @@ struct RmsGroupArgs {
     uint16_t* norm_out;     // optional
     int64_t ld_x, ld_r, ld_ro, ld_q, ld_s, ld_n;
     int64_t M;
-    int d;
+    uint16_t d;             // row length, at most NQ_MAX_D
+    uint8_t ue8m0;          // scales rounded up to powers of two
+    uint8_t bf16_source;    // quantize bf16(y) (the unfused pipeline's values)
     float eps;
     double inv_d;           // RN(1 / d), formed on the host
-    int ue8m0;              // scales rounded up to powers of two
-    int bf16_source;        // quantize bf16(y) (the unfused pipeline's values)
+};
+// Two 64-byte lines of the kernel-argument segment (a third costs a
+// single-row call about 70 ns on MI355X), hence the 16-bit row length.
+static_assert(sizeof(RmsGroupArgs) <= 128, "kernel arguments fit two 64-byte lines");
+static_assert(NQ_MAX_D <= 0xFFFF, "the row length fits its 16-bit field");
+
+// Host-side launch request: the kernel arguments and the instance choices.
+struct RmsGroupLaunch {
+    RmsGroupArgs k;
     bool e5m2;              // output format (e4m3 otherwise)
     bool gamma_bf16;
 };
@@ -117,20 +126,20 @@ struct RmsGroupKernel {
     template <bool STAGE>
     static constexpr int block() { return row_block<TEAM, CPL, 1, VEC, STAGE>(); }
     template <bool STAGE>
-    static void launch(const RmsGroupArgs& a, dim3 grid, dim3 block, hipStream_t s)
+    static void launch(const RmsGroupLaunch& a, dim3 grid, dim3 block, hipStream_t s)
     {
-        if (a.r != nullptr) go<STAGE, true>(a, grid, block, s);
+        if (a.k.r != nullptr) go<STAGE, true>(a, grid, block, s);
         else go<STAGE, false>(a, grid, block, s);
     }
     template <bool STAGE, bool RES>
-    static void go(const RmsGroupArgs& a, dim3 grid, dim3 block, hipStream_t s)
+    static void go(const RmsGroupLaunch& a, dim3 grid, dim3 block, hipStream_t s)
     {
         if (a.gamma_bf16) {
-            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E5M2, true, RES>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E4M3, true, RES>), grid, block, 0, s, a);
+            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E5M2, true, RES>), grid, block, 0, s, a.k);
+            else hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E4M3, true, RES>), grid, block, 0, s, a.k);
         } else {
-            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E5M2, false, RES>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E4M3, false, RES>), grid, block, 0, s, a);
+            if (a.e5m2) hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E5M2, false, RES>), grid, block, 0, s, a.k);
+            else hipLaunchKernelGGL((k_add_rmsnorm_fp8_group<TEAM, CPL, VEC, STAGE, Fp8::E4M3, false, RES>), grid, block, 0, s, a.k);
         }
     }
 };
@@ -180,15 +189,16 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_group(
     const RowShape shape = pick_row_shape(M, d, vec);
     if (shape.team == 0) return NQ_ERR_SHAPE;
 
-    RmsGroupArgs a;
+    RmsGroupLaunch L;
+    RmsGroupArgs& a = L.k;
     a.x = x; a.r = residual_in; a.ro = residual_out; a.gamma = gamma;
     a.q = q_out; a.scale_out = scale_out; a.norm_out = norm_out;
     a.ld_x = ld_x; a.ld_r = ld_r; a.ld_ro = ld_ro; a.ld_q = ld_q; a.ld_s = ld_s; a.ld_n = ld_n;
-    a.M = M; a.d = (int)d; a.eps = eps; a.inv_d = 1.0 / (double)d;
-    a.ue8m0 = scale_mode == NQ_SCALE_UE8M0;
-    a.bf16_source = (flags & NQ_FLAG_BF16_SOURCE) != 0;
-    a.e5m2 = (flags & NQ_FLAG_E5M2) != 0;
-    a.gamma_bf16 = (flags & NQ_FLAG_GAMMA_BF16) != 0;
-    if (!launch_row_shape<RmsGroupKernel>(shape, a, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
+    a.M = M; a.d = (uint16_t)d; a.eps = eps; a.inv_d = 1.0 / (double)d;
+    a.ue8m0 = scale_mode == NQ_SCALE_UE8M0 ? 1 : 0;
+    a.bf16_source = (flags & NQ_FLAG_BF16_SOURCE) != 0 ? 1 : 0;
+    L.e5m2 = (flags & NQ_FLAG_E5M2) != 0;
+    L.gamma_bf16 = (flags & NQ_FLAG_GAMMA_BF16) != 0;
+    if (!launch_row_shape<RmsGroupKernel>(shape, L, M, (hipStream_t)stream)) return NQ_ERR_SHAPE;
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
 }
