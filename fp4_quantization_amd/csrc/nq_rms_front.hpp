@@ -12,9 +12,11 @@
 //   z_i  = bf16(x_i + r_i), or x_i itself when residual-less (RES false: a
 //          separate instance with no add, repacking or write-back)
 //   rstd = 1 / sqrt(sum z_i^2 / d + eps), the sum in binary64 (every z_i^2 is
-//          exact there), its quotient by d correctly rounded in binary64 and
-//          then to binary32, so the result does not depend on the reduction
-//          tree; the square root and the reciprocal are each correctly rounded.
+//          exact there; the sum rounds, if at all, only in its last bit), its
+//          quotient by d correctly rounded in binary64 and then to binary32,
+//          so the reduction order changes the result only if that sum lies
+//          within about 2^-52 of a binary32 rounding boundary; the square
+//          root and the reciprocal are each correctly rounded.
 #pragma once
 
 #include "nq_device.hpp"
