@@ -258,9 +258,14 @@ __device__ __forceinline__ float pow2_ceil(float t)
 // q0 = y * inv is within one ulp of y / s, the remainder y - s * q0 is
 // exact in one fused multiply-add, and q0 + r * inv rounded once is the
 // correctly rounded quotient (Markstein's theorem for round-to-nearest
-// binary floating point; it needs no overflow and a normal s, and a
-// quotient below 2^-126 only arises where every e4m3/E2M1 code is zero).
-// Three operations per element instead of a full division sequence.
+// binary floating point).  The remainder is a multiple of 2^(e_y - 46)
+// below 2^(e_y - 22), so it is exact for |y| >= 2^-103; the theorem also
+// needs a normal s, no overflow and a quotient of at least 2^-126.  For
+// smaller y the result is within one ulp; a kernel meets such y with a
+// quotient whose FP8 code can be non-zero only in rows whose maximum is
+// below 2^-84.  Three operations per element instead of a full division
+// sequence.  Checked on the device against correctly rounded division over
+// random and edge operands (test_div_by_matches_division).
 __device__ __forceinline__ float div_by(float y, float s, float inv)
 {
     const float q0 = y * inv;
@@ -276,6 +281,8 @@ __device__ __forceinline__ float div_by(float y, float s, float inv)
 // the final rounding agrees with the quotient's.  The sums divided here are
 // 0 or at least 2^-266 in magnitude (squares and values of bf16 numbers),
 // far from underflow.  Three binary64 operations instead of a division.
+// Checked for every d <= 2^15 on the host (tests/test_shortcut_proofs.py)
+// and on the device (test_div_by_len_every_row_length).
 __device__ __forceinline__ double div_by_len(double a, double d, double inv_d)
 {
     const double q0 = a * inv_d;
@@ -283,20 +290,53 @@ __device__ __forceinline__ double div_by_len(double a, double d, double inv_d)
     return __builtin_fma(r, inv_d, q0);
 }
 
-// 1 / sqrt(x) as two correctly rounded steps, x >= 0: s = sqrt(x), then
-// RN(1 / s) by one Newton step from the hardware reciprocal.  An exhaustive
-// run on MI355X found that step exact for every normal s up to 2^125; the
-// s of a positive binary32 x lie in [2^-75, 2^64].  s = 0 and s = infinity
-// take the division's results (infinity and 0) explicitly.
+// RN(1 / s) for a normal s in [2^-75, 2^64]: the hardware reciprocal
+// (v_rcp_f32, about one ulp) corrected by one Newton step with fused
+// multiply-adds.  One step from a one-ulp seed is not correctly rounded for
+// every significand in theory; on this hardware it is exact over that whole
+// range -- the device test test_rcp_rn_every_significand (tests/
+// test_gpu_arith.py, through nq_diag_arith) compares it with the correctly
+// rounded reciprocal for every binary32 s of those binades.
+__device__ __forceinline__ float rcp_rn(float s)
+{
+    const float y0 = __builtin_amdgcn_rcpf(s);
+    const float e = __builtin_fmaf(-s, y0, 1.0f);
+    return __builtin_fmaf(e, y0, y0);
+}
+
+// 1 / sqrt(x) as two correctly rounded steps, x >= 0: s = sqrt(x)
+// (correctly rounded), then RN(1 / s) by rcp_rn; the s of a positive
+// binary32 x lie in [2^-75, 2^64].  s = 0 and s = infinity take the
+// division's results (infinity and 0) explicitly.  Checked on the device for
+// every non-negative binary32 x (test_rsqrt_rn_every_binary32).
 __device__ __forceinline__ float rsqrt_rn(float x)
 {
     const float s = sqrtf(x);
-    const float y0 = __builtin_amdgcn_rcpf(s);
-    const float e = __builtin_fmaf(-s, y0, 1.0f);
-    float r = __builtin_fmaf(e, y0, y0);
+    float r = rcp_rn(s);
     r = s == 0.0f ? __builtin_inff() : r;
     r = s == __builtin_inff() ? 0.0f : r;
     return r;
+}
+
+// RN(amax / 6) for a block maximum amax >= 0 (the NVFP4 block scale's
+// first step).  Markstein's correction from RN(1/6) (div_by) is exact
+// whenever the quotient is normal (amax >= 2^-120 with margin) and gives 0
+// for 0; a wavefront holding a smaller non-zero maximum takes the
+// correctly rounded division instead, behind a ballot so that ordinary data
+// never runs it.  Checked on the device for every finite non-negative
+// binary32 (test_div6_every_binary32).
+__device__ __forceinline__ float div6_rn(float amax)
+{
+    float per = div_by(amax, kE2M1Max, kInvE2M1Max);
+    const bool tiny = amax > 0.0f && amax < kMinNormalE2M1Quotient;
+    if (__builtin_amdgcn_ballot_w64(tiny) != 0) {
+        // The empty volatile statement keeps this a branch: without it the
+        // compiler evaluates the full division for every block and selects
+        // (about 12 vector instructions per chunk).
+        __asm__ volatile("");
+        if (tiny) per = amax / kE2M1Max;
+    }
+    return per;
 }
 
 // ------------------------------------------------------- row access -------

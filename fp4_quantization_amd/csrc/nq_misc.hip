@@ -1,7 +1,8 @@
-// nq_misc.hip -- status strings, version, and the two diagnostic kernels:
-// the device conversion routines applied element-wise (so their rounding can
-// be compared with an independent host codec) and a 128-bit copy used as
-// the bandwidth reference for the same HBM.
+// nq_misc.hip -- status strings, version, and the diagnostic kernels: the
+// device conversion routines and the arithmetic shortcuts applied
+// element-wise (so their rounding can be compared with an independent host
+// computation) and a 128-bit copy used as the bandwidth reference for the
+// same HBM.
 #include "nq_device.hpp"
 #include "nq_host.hpp"
 
@@ -38,6 +39,46 @@ __global__ __launch_bounds__(256) void k_diag_codec(int kind, const float* in, v
             if (i0 + k < n) o[i0 + k] = (uint16_t)p;
             if (i0 + k + 1 < n) o[i0 + k + 1] = (uint16_t)(p >> 16);
         }
+    }
+}
+
+// One element per thread through the kernels' own arithmetic routines.
+// Operand and result types per kind are given in include/nq.h.
+__global__ __launch_bounds__(256) void k_diag_arith(int kind, const void* a, const void* b, void* out, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // Lanes past n compute on a harmless operand and store nothing, so the
+    // wavefront-wide ballot inside div6_rn sees every lane.
+    const bool live = i < n;
+    const int64_t k = live ? i : 0;
+    switch (kind) {
+    case NQ_ARITH_RCP: {
+        const float r = rcp_rn(static_cast<const float*>(a)[k]);
+        if (live) static_cast<float*>(out)[i] = r;
+        break;
+    }
+    case NQ_ARITH_RSQRT: {
+        const float r = rsqrt_rn(static_cast<const float*>(a)[k]);
+        if (live) static_cast<float*>(out)[i] = r;
+        break;
+    }
+    case NQ_ARITH_DIV: {
+        const float y = static_cast<const float*>(a)[k], s = static_cast<const float*>(b)[k];
+        const float r = div_by(y, s, 1.0f / s);
+        if (live) static_cast<float*>(out)[i] = r;
+        break;
+    }
+    case NQ_ARITH_DIV_LEN: {
+        const double d = (double)static_cast<const int32_t*>(b)[k];
+        const double r = div_by_len(static_cast<const double*>(a)[k], d, 1.0 / d);
+        if (live) static_cast<double*>(out)[i] = r;
+        break;
+    }
+    default: {  // NQ_ARITH_DIV6
+        const float r = div6_rn(static_cast<const float*>(a)[k]);
+        if (live) static_cast<float*>(out)[i] = r;
+        break;
+    }
     }
 }
 
@@ -84,6 +125,25 @@ extern "C" nq_status nq_diag_codec(int32_t kind, const float* in, void* out, int
     if (blocks > 0x7FFFFFFF) return NQ_ERR_SHAPE;
     hipLaunchKernelGGL(k_diag_codec, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                        (int)kind, in, out, n);
+    return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
+}
+
+extern "C" nq_status nq_diag_arith(int32_t kind, const void* a, const void* b, void* out, int64_t n,
+                                   void* stream)
+{
+    if (kind < NQ_ARITH_RCP || kind > NQ_ARITH_DIV6) return NQ_ERR_ARG;
+    if (n < 0 || n > (int64_t(1) << 36)) return NQ_ERR_SHAPE;
+    if (n == 0) return NQ_OK;
+    const bool two = kind == NQ_ARITH_DIV || kind == NQ_ARITH_DIV_LEN;
+    if (!a || !out || (two && !b)) return NQ_ERR_NULL;
+    const int64_t asz = kind == NQ_ARITH_DIV_LEN ? 8 : 4;
+    const Region rin[] = {region(a, 1, n, n, asz), region(two ? b : nullptr, 1, n, n, 4)};
+    const Region rout[] = {region(out, 1, n, n, asz)};
+    if (any_alias(rin, rout)) return NQ_ERR_ALIAS;
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return NQ_ERR_SHAPE;
+    hipLaunchKernelGGL(k_diag_arith, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, (int)kind, a,
+                       b, out, n);
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
 }
 

@@ -104,18 +104,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
         // Block of 16 = this chunk and the partner lane's (same load
         // instruction, lanes t and t^1: one DPP exchange inside a quad).
         amax = fmaxf(amax, dpp_f32<kDppXor1>(amax));
-        // per = RN(amax / 6): Markstein's correction is exact for a normal
-        // quotient (and gives 0 for 0); a wavefront holding a smaller
-        // non-zero maximum takes the division.
-        float per = div_by(amax, kE2M1Max, kInvE2M1Max);
-        const bool tiny = amax > 0.0f && amax < kMinNormalE2M1Quotient;
-        if (__builtin_amdgcn_ballot_w64(tiny) != 0) {
-            // The empty volatile statement keeps this a branch: without it
-            // the compiler evaluates the full division for every block and
-            // selects (about 12 vector instructions per chunk).
-            __asm__ volatile("");
-            if (tiny) per = amax / kE2M1Max;
-        }
+        const float per = div6_rn(amax);  // RN(amax / 6)
         const uint32_t sf = e4m3x4(per * G, 0.0f, 0.0f, 0.0f) & 0x7Fu;  // amax >= 0: codes 0 .. 0x7E
         const float mult = lds_mult[sf];
         float v[8];

@@ -50,6 +50,7 @@ _SIGS = {
     "nq_fused_add_rmsnorm_bf16": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _f32, _vp, _i64, _i64, _i64, _vp],
     "nq_per_token_quant_fp8": [_vp, _i64, _vp, _u32, _vp, _i64, _vp, _i64, _i64, _vp],
     "nq_diag_codec": [_i32, _vp, _vp, _i64, _vp],
+    "nq_diag_arith": [_i32, _vp, _vp, _vp, _i64, _vp],
     "nq_diag_copy": [_vp, _vp, _i64, _vp],
 }
 for _name, _args in _SIGS.items():
@@ -72,6 +73,11 @@ NQ_CODEC_E4M3 = 0
 NQ_CODEC_E2M1 = 1
 NQ_CODEC_BF16 = 2
 NQ_CODEC_E5M2 = 3
+NQ_ARITH_RCP = 0
+NQ_ARITH_RSQRT = 1
+NQ_ARITH_DIV = 2
+NQ_ARITH_DIV_LEN = 3
+NQ_ARITH_DIV6 = 4
 NQ_MAX_D = 32768  # widest row of the row kernels (include/nq.h)
 
 
@@ -366,6 +372,30 @@ def nq_diag_codec(kind: int, x: torch.Tensor, out: torch.Tensor, stream=None):
         pout = _vec(out, torch.uint8, "out", n)
     st = _lib.nq_diag_codec(int(kind), px, pout, n, _stream(stream))
     _check(st, "nq_diag_codec")
+
+
+_ARITH_TYPES = {  # kind -> (a dtype, b dtype or None); out has a's dtype
+    NQ_ARITH_RCP: (torch.float32, None),
+    NQ_ARITH_RSQRT: (torch.float32, None),
+    NQ_ARITH_DIV: (torch.float32, torch.float32),
+    NQ_ARITH_DIV_LEN: (torch.float64, torch.int32),
+    NQ_ARITH_DIV6: (torch.float32, None),
+}
+
+
+def nq_diag_arith(kind: int, a: torch.Tensor, b, out: torch.Tensor, stream=None):
+    """Apply one of the kernels' arithmetic shortcuts element-wise (include/nq.h)."""
+    if kind not in _ARITH_TYPES:
+        raise ValueError(f"nq_diag_arith: unknown kind {kind}")
+    ta, tb = _ARITH_TYPES[kind]
+    n = a.numel()
+    pa = _vec(a, ta, "a", n)
+    pb = _vec(b, tb, "b", n) if tb is not None else None
+    if tb is None and b is not None:
+        raise ValueError("nq_diag_arith: this kind takes one operand")
+    pout = _vec(out, ta, "out", n)
+    st = _lib.nq_diag_arith(int(kind), pa, pb, pout, n, _stream(stream))
+    _check(st, "nq_diag_arith")
 
 
 def nq_diag_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):

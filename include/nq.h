@@ -379,6 +379,26 @@ const char* nq_version(void);
  *   NQ_CODEC_E5M2: out[i] = e5m2 code of in[i]   (clamp to +-57344, nearest-even)
  * `out` is uint8_t for the 8-bit formats and uint16_t for bf16.
  *
+ * nq_diag_arith: applies, element by element on the device, the arithmetic
+ * shortcuts the kernels take in place of a correctly rounded operation, so
+ * that each can be compared with the correctly rounded result on the host
+ * ([GRP] "Details": one correctly rounded division per group, the exact
+ * reciprocal).  n elements; kind:
+ *   NQ_ARITH_RCP:     out[i] = RN(1 / a[i]) by the hardware reciprocal and one
+ *                     Newton step (the reciprocal inside 1/sqrt); fp32
+ *   NQ_ARITH_RSQRT:   out[i] = RN(1 / RN(sqrt(a[i]))), the kernels' rstd step
+ *                     on its argument mean + eps; fp32
+ *   NQ_ARITH_DIV:     out[i] = RN(a[i] / b[i]) by Markstein's correction of
+ *                     a[i] * RN(1 / b[i]) (the per-token FP8 quotient); fp32
+ *   NQ_ARITH_DIV_LEN: out[i] = RN(a[i] / b[i]) in binary64 for an integer row
+ *                     length b[i] in [1, 32768] (int32), from RN(1 / b[i]);
+ *                     a and out are double
+ *   NQ_ARITH_DIV6:    out[i] = RN(a[i] / 6) for a block maximum a[i] >= 0 (the
+ *                     NVFP4 block scale's first step); fp32
+ * b is NULL for the one-operand kinds.  Errors: NQ_ERR_ARG (unknown kind),
+ * NQ_ERR_NULL, NQ_ERR_SHAPE (n < 0 or n > 2^36), NQ_ERR_ALIAS (out overlaps
+ * an operand).
+ *
  * nq_diag_copy: copies `bytes` (a multiple of 16, both pointers 16-byte
  * aligned) with 128-bit loads and stores, a bandwidth reference for the same
  * HBM the quantization kernels stream through.
@@ -388,6 +408,12 @@ const char* nq_version(void);
 #define NQ_CODEC_BF16 2
 #define NQ_CODEC_E5M2 3
 nq_status nq_diag_codec(int32_t kind, const float* in, void* out, int64_t n, void* stream);
+#define NQ_ARITH_RCP 0
+#define NQ_ARITH_RSQRT 1
+#define NQ_ARITH_DIV 2
+#define NQ_ARITH_DIV_LEN 3
+#define NQ_ARITH_DIV6 4
+nq_status nq_diag_arith(int32_t kind, const void* a, const void* b, void* out, int64_t n, void* stream);
 nq_status nq_diag_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 #ifdef __cplusplus

@@ -6,11 +6,20 @@ Acceptance, stated once here and used by every parity test:
   * e4m3 and E2M1 codes: identical, except that at most 0.1% of the elements
     may differ by one code step (a reduction-order tie at a rounding
     midpoint); +0 and -0 count as the same code.
-The kernels accumulate row sums in binary64 like the oracle, so the expected
-outcome is bit-exact; the tolerance is the acceptance bound, not the
-expectation, and every test also reports the exact mismatch count.
+The tolerance is the acceptance bound.  Every comparison is also recorded
+(test, output, elements compared, codes one step apart, worst relative scale
+error), and the test session prints the records of the full-size outputs and
+the totals at its end (tests/conftest.py), so the exact agreement is visible
+in every run.
+
+`ParallelOracle` runs the oracle's row operations over blocks of rows on host
+threads (the oracle's C calls release the interpreter lock), so whole
+full-size outputs are compared, not samples.
 """
 from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -35,9 +44,19 @@ def host_u8(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.uint8).cpu().numpy()
 
 
+# (test id, output, kind, elements, differing, worst relative scale error)
+REPORT: list[tuple] = []
+
+
+def _record(what, kind, size, differing, worst=0.0):
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    REPORT.append((test, what, kind, int(size), int(differing), float(worst)))
+
+
 def assert_bits_equal(got: np.ndarray, want: np.ndarray, what: str):
     assert got.shape == want.shape, (what, got.shape, want.shape)
     bad = np.count_nonzero(got != want)
+    _record(what, "bits", want.size, bad)
     assert bad == 0, f"{what}: {bad} of {want.size} differ"
 
 
@@ -49,6 +68,7 @@ def assert_scales(got: np.ndarray, want: np.ndarray, what: str):
     assert np.all(got[zero] == 0), f"{what}: nonzero scale where the oracle has 0"
     rel = np.abs(got[~zero] - want[~zero]) / np.abs(want[~zero])
     worst = float(rel.max()) if rel.size else 0.0
+    _record(what, "scale", want.size, int(np.count_nonzero(got != want)), worst)
     assert worst <= SCALE_RTOL, f"{what}: worst relative scale error {worst:.3g}"
     return worst
 
@@ -69,13 +89,15 @@ def assert_codes(got: np.ndarray, want: np.ndarray, what: str, fmt: str = "e4m3"
     assert got.shape == want.shape, (what, got.shape, want.shape)
     # e4m3 and e5m2 codes both order magnitudes by their low 7 bits
     mag, sign = (0x7F, 0x80) if fmt in ("e4m3", "e5m2") else (0x7, 0x8)
-    same, adjacent = _code_steps(got, want, mag, sign)
+    idx = np.flatnonzero(got != want)  # classify only the differing bytes
+    same, adjacent = _code_steps(got.ravel()[idx], want.ravel()[idx], mag, sign)
     diff = ~same
-    n = diff.sum()
+    n = int(diff.sum())
     far = diff & ~adjacent
+    _record(what, fmt, got.size, n)
     assert not far.any(), f"{what}: {far.sum()} codes differ by more than one step"
     assert n <= CODE_FLIP_FRAC * got.size, f"{what}: {n} of {got.size} codes differ by one step"
-    return int(n)
+    return n
 
 
 def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
@@ -83,3 +105,56 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
     lo = packed & 0xF
     hi = packed >> 4
     return np.stack([lo, hi], axis=-1).reshape(packed.shape[0], -1)
+
+
+def host_threads() -> int:
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return max(1, min(16, cores))
+
+
+class ParallelOracle:
+    """The oracle module, with its row operations run over blocks of rows on
+    host threads.  Every row of every operation is computed independently by
+    the oracle (scales are per row or per group of a row; static and global
+    scales are scalars), so splitting the rows changes no result.  A 2-D
+    array argument with as many rows as the first argument is split; vectors
+    (gamma, beta) and scalars are passed whole; the outputs' rows are joined
+    in order."""
+
+    ROW_OPS = ("fused_add_rmsnorm_quant_fp8", "quant_fp8_rows", "unfused_rmsnorm_quant_fp8",
+               "layernorm_quant_fp8", "per_token_group_quant_fp8", "fused_add_rmsnorm_quant_fp8_group",
+               "rmsnorm_quant_nvfp4")
+    MIN_ROWS = 64
+
+    def __init__(self, module):
+        self._m = module
+
+    def __getattr__(self, name):
+        fn = getattr(self._m, name)
+        if name not in self.ROW_OPS:
+            return fn
+
+        def run(x, *args, **kw):
+            M = x.shape[0]
+            if M < 2 * self.MIN_ROWS:
+                return fn(x, *args, **kw)
+            parts = min(4 * host_threads(), M // self.MIN_ROWS)
+            bounds = np.linspace(0, M, parts + 1).astype(int)
+
+            def cut(v, lo, hi):
+                return v[lo:hi] if isinstance(v, np.ndarray) and v.ndim == 2 and v.shape[0] == M else v
+
+            def one(k):
+                lo, hi = bounds[k], bounds[k + 1]
+                return fn(cut(x, lo, hi), *(cut(a, lo, hi) for a in args),
+                          **{key: cut(v, lo, hi) for key, v in kw.items()})
+
+            with ThreadPoolExecutor(host_threads()) as ex:
+                outs = list(ex.map(one, range(parts)))
+            return {key: (None if outs[0][key] is None else np.concatenate([o[key] for o in outs], axis=0))
+                    for key in outs[0]}
+
+        return run

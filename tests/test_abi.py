@@ -57,6 +57,7 @@ def lib():
     L.nq_rmsnorm_quant_nvfp4.argtypes = [v, i64, v, i64, v, i64, v, f32, v, v, i64, v, i64, v, i64, i64, i64, v]
     L.nq_diag_codec.argtypes = [i32, v, v, i64, v]
     L.nq_diag_copy.argtypes = [v, v, i64, v]
+    L.nq_diag_arith.argtypes = [i32, v, v, v, i64, v]
     L.nq_status_string.restype = ctypes.c_char_p
     L.nq_version.restype = ctypes.c_char_p
     return L
@@ -291,6 +292,15 @@ def test_diag_validation(lib):
     assert lib.nq_diag_copy(X, Q, 15, None) == NQ_ERR_SHAPE
     assert lib.nq_diag_copy(X + 4, Q, 16, None) == NQ_ERR_ARG
     assert lib.nq_diag_copy(X, Q, 0, None) == NQ_OK
+    assert lib.nq_diag_arith(5, X, None, Q, 16, None) == NQ_ERR_ARG
+    assert lib.nq_diag_arith(-1, X, None, Q, 16, None) == NQ_ERR_ARG
+    assert lib.nq_diag_arith(0, X, None, Q, -1, None) == NQ_ERR_SHAPE
+    assert lib.nq_diag_arith(0, X, None, Q, 0, None) == NQ_OK
+    assert lib.nq_diag_arith(2, X, None, Q, 16, None) == NQ_ERR_NULL   # division needs b
+    assert lib.nq_diag_arith(0, None, None, Q, 16, None) == NQ_ERR_NULL
+    assert lib.nq_diag_arith(0, X, None, X + 60, 16, None) == NQ_ERR_ALIAS
+    assert lib.nq_diag_arith(3, X, Q, Q + 32, 16, None) == NQ_ERR_ALIAS  # int32 b [Q, Q+64), double out
+    assert lib.nq_diag_arith(3, X + 64, Q, X, 16, None) == NQ_ERR_ALIAS  # double a [X+64, X+192)
 
 
 def test_binding_imports_without_gpu():

@@ -53,6 +53,8 @@ def _calls(nq, t):
             lambda: nq.nq_diag_copy(t["q"].view(-1), t["n"].view(torch.uint8).view(-1)),
         "nq_diag_codec":
             lambda: nq.nq_diag_codec(nq.NQ_CODEC_E4M3, t["g"], t["q"].view(-1)[:D]),
+        "nq_diag_arith":
+            lambda: nq.nq_diag_arith(nq.NQ_ARITH_RCP, t["g"], None, t["b"]),
     }
 
 

@@ -1,0 +1,224 @@
+"""Device checks of the arithmetic shortcuts the kernels take in place of a
+correctly rounded operation, through nq_diag_arith (the C ABI), against
+correctly rounded results computed on the host with numpy:
+
+* rcp_rn (hardware reciprocal + one Newton step): every binary32 s in
+  [2^-75, 2^64), the range sqrt(mean + eps) can take;
+* rsqrt_rn (correctly rounded sqrt, then rcp_rn): every non-negative
+  binary32, 0 and infinity;
+* div_by (Markstein's correction of y * RN(1/s), the per-token quotient):
+  random and edge operands over the scales and quotients the kernels see;
+* div_by_len (binary64 quotient by the row length): every d <= 32768 with
+  random, near-midpoint and exact numerators;
+* div6_rn (RN(amax/6), with its ballot-guarded division for tiny maxima):
+  every finite non-negative binary32.
+
+Whole binades are checked through one table of the significands: for a
+normal result, RN(f(m * 2^k)) is RN(f(m)) with its exponent moved by the
+power of two, so each binade's expected bit patterns are the table's plus
+a constant.  Division and square root on the host are IEEE binary64 (or
+binary32 sqrt), and rounding a binary64 quotient or root of binary32
+operands to binary32 is correctly rounded (double rounding is innocuous
+there), so every expected value is the correctly rounded one.
+
+Page: "per_token_group_quant_8bit: multiply by reciprocal instead of
+dividing per element", "Details" (one correctly rounded division per group;
+the exact reciprocal).
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+N_SIG = 1 << 23
+
+
+@pytest.fixture(scope="module")
+def nq():
+    import fp4_quantization_amd.nq as m
+    return m
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _significands() -> np.ndarray:
+    """Every binary32 in [1, 2)."""
+    return ((np.arange(N_SIG, dtype=np.uint32)) | np.uint32(127 << 23)).view(np.float32)
+
+
+def _binade_dev(field: int, mant: torch.Tensor) -> torch.Tensor:
+    return (mant | (field << 23)).view(torch.float32)
+
+
+def _run(nq, kind, a, b=None):
+    out = torch.empty_like(a)
+    nq.nq_diag_arith(kind, a, b, out)
+    return out
+
+
+def _host_rcp(s32: np.ndarray) -> np.ndarray:
+    return (1.0 / s32.astype(np.float64)).astype(np.float32)
+
+
+def test_rcp_rn_every_significand(nq):
+    note("rcp_rn, binades 2^-75 .. 2^63")
+    table = torch.from_numpy(_host_rcp(_significands()).view(np.int32)).cuda()
+    mant = torch.arange(N_SIG, dtype=torch.int32, device="cuda")
+    bad = {}
+    for field in range(127 - 75, 127 + 64):
+        got = _run(nq, nq.NQ_ARITH_RCP, _binade_dev(field, mant)).view(torch.int32)
+        want = table - ((field - 127) << 23)  # RN(1/(m 2^k)) = RN(1/m) 2^-k
+        n = int((got != want).sum())
+        if n:
+            bad[field - 127] = n
+    torch.cuda.synchronize()
+    assert not bad, f"binades (exponent: mismatches) {bad}"
+
+
+def test_rsqrt_rn_every_binary32(nq):
+    note("rsqrt_rn, every non-negative binary32")
+    m = _significands()
+    # x = m 2^k: k even -> RN(1/RN(sqrt m)) 2^(-k/2); k odd -> with 2m, 2^(-(k-1)/2)
+    even = _host_rcp(np.sqrt(m)).view(np.int32)
+    odd = _host_rcp(np.sqrt(2.0 * m.astype(np.float32))).view(np.int32)
+    tables = [torch.from_numpy(even).cuda(), torch.from_numpy(odd).cuda()]
+    mant = torch.arange(N_SIG, dtype=torch.int32, device="cuda")
+    bad = {}
+    for field in range(1, 255):
+        k = field - 127
+        got = _run(nq, nq.NQ_ARITH_RSQRT, _binade_dev(field, mant)).view(torch.int32)
+        want = tables[k & 1] - ((k >> 1) << 23)
+        n = int((got != want).sum())
+        if n:
+            bad[k] = n
+    assert not bad, f"binades (exponent: mismatches) {bad}"
+    # subnormal x (and 0 -> infinity), +infinity -> 0
+    sub = np.arange(N_SIG, dtype=np.uint32).view(np.float32)
+    got = _run(nq, nq.NQ_ARITH_RSQRT, torch.from_numpy(sub).cuda()).cpu().numpy()
+    with np.errstate(divide="ignore"):
+        want = _host_rcp(np.sqrt(sub))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert got[0] == np.inf
+    inf = _run(nq, nq.NQ_ARITH_RSQRT, torch.tensor([np.inf], dtype=torch.float32, device="cuda"))
+    assert inf.item() == 0.0
+
+
+def test_div_by_matches_division(nq):
+    """y / s for s = RN(amax / fmax) over normal scales and |y| up to about
+    fmax * s (both FP8 formats), signs mixed, plus edges.  Markstein's
+    correction needs its remainder y - s * q0 to be exact: it is a multiple of
+    2^(e_y - 46) below 2^(e_y - 22), so exact for |y| >= 2^-103.  There, with a
+    quotient of at least 2^-126, the result must be the correctly rounded
+    quotient.  Below, it must be within one ulp of it (the kernels only meet
+    such y where the quotient's FP8 code is 0 either way unless the row's
+    maximum is under 2^-84)."""
+    rng = np.random.default_rng(5)
+    n = 1 << 24
+    checked = exact_checked = 0
+    for part in range(4):
+        note(f"div_by part {part}")
+        e = rng.integers(-126, 113, n)
+        s = np.ldexp(1.0 + rng.random(n), e).astype(np.float32)
+        if part == 0:  # quotients spread over the whole FP8 range, log-uniform
+            u = np.exp2(rng.uniform(-30.0, 16.0, n))
+        elif part == 1:  # uniform up to the e5m2 maximum
+            u = rng.uniform(0.0, 57344.0 * 1.001, n)
+        elif part == 2:  # uniform up to the e4m3 maximum
+            u = rng.uniform(0.0, 448.0 * 1.001, n)
+        else:  # y = the row maximum itself, s = RN(amax / 448) or RN(amax / 57344)
+            amax = np.ldexp(1.0 + rng.random(n), rng.integers(-110, 120, n)).astype(np.float32)
+            fmax = np.where(rng.random(n) < 0.5, 448.0, 57344.0)
+            s = (amax.astype(np.float64) / fmax).astype(np.float32)
+            u = amax.astype(np.float64) / s.astype(np.float64)
+        sign = np.where(rng.random(n) < 0.5, -1.0, 1.0)
+        y = (sign * u * s.astype(np.float64)).astype(np.float32) if part < 3 else (sign * amax).astype(np.float32)
+        keep = np.isfinite(y) & (s > 0)
+        y, s = y[keep], s[keep]
+        got = _run(nq, nq.NQ_ARITH_DIV, torch.from_numpy(y).cuda(), torch.from_numpy(s).cuda()).cpu().numpy()
+        exact = y.astype(np.float64) / s.astype(np.float64)
+        want = exact.astype(np.float32)
+        ok_range = (np.abs(exact) >= 2.0 ** -126) & (np.abs(y) >= 2.0 ** -103)
+        differ = got.view(np.uint32) != want.view(np.uint32)
+        mism = np.nonzero(ok_range & differ)[0]
+        assert mism.size == 0, (part, mism.size, y[mism[:3]], s[mism[:3]], got[mism[:3]], want[mism[:3]])
+        # outside that range: at most one ulp (adjacent bit patterns, same sign)
+        steps = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+        assert np.all(steps[~ok_range] <= 1)
+        checked += y.size
+        exact_checked += int(ok_range.sum())
+    # edges: power-of-two scales, quotients exactly 448 / 57344, y = 0
+    s = np.ldexp(np.ones(200), np.arange(-120, 80)).astype(np.float32)
+    y = np.concatenate([s * 448, -s * 57344, 0 * s]).astype(np.float32)
+    s3 = np.concatenate([s, s, s])
+    got = _run(nq, nq.NQ_ARITH_DIV, torch.from_numpy(y).cuda(), torch.from_numpy(s3).cuda()).cpu().numpy()
+    want = (y.astype(np.float64) / s3.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(got, want)
+    assert checked > 60_000_000 and exact_checked > 55_000_000
+
+
+def _near_midpoint_numerators(d: np.ndarray, rng) -> np.ndarray:
+    """For each d: the double nearest to d times a midpoint between two
+    consecutive doubles (exact integer arithmetic)."""
+    out = np.empty(d.size, np.float64)
+    Q = (rng.integers(0, 1 << 52, d.size, dtype=np.int64) | (1 << 52)).tolist()
+    E = rng.integers(-200, 200, d.size).tolist()
+    for i, (di, q, e) in enumerate(zip(d.tolist(), Q, E)):
+        n = di * (2 * q + 1)
+        shift = max(n.bit_length() - 53, 0)
+        a, rem = n >> shift, n & ((1 << shift) - 1)
+        half = (1 << (shift - 1)) if shift else 0
+        if shift and (rem > half or (rem == half and a & 1)):
+            a += 1
+        out[i] = np.ldexp(float(a), e - 53 + shift)
+    return out
+
+
+def test_div_by_len_every_row_length(nq):
+    note("div_by_len, d = 1 .. 32768")
+    rng = np.random.default_rng(6)
+    d_all = np.arange(1, 32769, dtype=np.int32)
+    parts = []
+    # random numerators over the range the kernels divide: 2^-266 .. 2^272
+    d_r = np.repeat(d_all, 24)
+    a_r = np.ldexp(1.0 + rng.random(d_r.size), rng.integers(-266, 272, d_r.size))
+    parts.append((a_r, d_r))
+    # near-midpoint quotients, and their neighbours
+    d_m = np.repeat(d_all, 4)
+    a_m = _near_midpoint_numerators(d_m, rng)
+    parts += [(a_m, d_m), (np.nextafter(a_m, 0.0), d_m), (np.nextafter(a_m, np.inf), d_m)]
+    # exact quotients
+    d_e = np.repeat(d_all, 4)
+    a_e = d_e.astype(np.float64) * rng.integers(1, 1 << 38, d_e.size).astype(np.float64)
+    parts.append((a_e, d_e))
+    a = np.concatenate([p[0] for p in parts])
+    d = np.concatenate([p[1] for p in parts])
+    a = np.where(rng.random(a.size) < 0.5, -a, a)
+    got = _run(nq, nq.NQ_ARITH_DIV_LEN, torch.from_numpy(a).cuda(), torch.from_numpy(d).cuda()).cpu().numpy()
+    want = a / d.astype(np.float64)
+    mism = np.nonzero(got.view(np.uint64) != want.view(np.uint64))[0]
+    assert mism.size == 0, (mism.size, a[mism[:3]], d[mism[:3]])
+    assert a.size == 32768 * 40
+
+
+def test_div6_every_binary32(nq):
+    note("div6_rn, every finite non-negative binary32")
+    m = _significands()
+    table = torch.from_numpy((m.astype(np.float64) / 6.0).astype(np.float32).view(np.int32)).cuda()
+    mant = torch.arange(N_SIG, dtype=torch.int32, device="cuda")
+    bad = {}
+    for field in range(0, 255):
+        a = _binade_dev(field, mant)
+        got = _run(nq, nq.NQ_ARITH_DIV6, a)
+        if field >= 8:  # quotient normal: the table, exponent moved
+            want = table + ((field - 127) << 23)
+            n = int((got.view(torch.int32) != want).sum())
+        else:  # tiny maxima (the ballot-guarded division) and subnormals: directly
+            ah = a.cpu().numpy()
+            w = (ah.astype(np.float64) / 6.0).astype(np.float32)
+            n = int(np.count_nonzero(got.cpu().numpy().view(np.uint32) != w.view(np.uint32)))
+        if n:
+            bad[field] = n
+    assert not bad, f"exponent fields (field: mismatches) {bad}"

@@ -1,8 +1,8 @@
 """GPU-vs-oracle parity of the four entry points, through the C ABI.
 
-Small shapes are compared element by element; the full workload sizes are
-run whole on the GPU (in the launch configuration the benchmark times) and
-compared on sampled rows that the oracle computes one by one.  Edge cases:
+Every output is compared element by element with the oracle, the full
+workload sizes included (run whole on the GPU in the launch configuration
+the benchmark times; the oracle runs row-parallel on host threads).  Edge cases:
 M = 0 and 1, ragged d (not a multiple of the 8-element chunk, or of the
 lane count), misaligned pointers (element-wise path), row-strided column
 slices, in-place residual, all-zero and constant rows, saturating NVFP4
@@ -58,11 +58,15 @@ def check_guard_u8(buf, n):
     assert np.all(tail == 0xA5), "write past the end of an output"
 
 
-def sample_rows(M, k=64, seed=0):
-    if M <= k:
-        return np.arange(M)
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, M - 1], rng.choice(M, k, replace=False)]))
+def check_guard_bf16(buf, n):
+    """The sentinel after n bf16 elements of a guarded_bf16 buffer (None: no buffer)."""
+    if buf is not None:
+        check_guard_u8(buf.view(torch.uint8), 2 * n)
+
+
+# Every output row is compared with the oracle (run row-parallel on host
+# threads), at every size including the full workloads.
+EVERY_ROW = slice(None)
 
 
 # ------------------------------------------------------- RMSNorm + FP8 ----
@@ -71,6 +75,7 @@ def run_rms_fp8(nq, w, static_scale=None, norm_out=False, in_place=False):
     M, d = w["M"], w["d"]
     x = to_dev_bf16(w["x"])
     r = to_dev_bf16(w["residual"]) if w["residual"] is not None else None
+    ro_buf = None
     if r is not None and in_place:
         ro = r
     elif r is not None:
@@ -86,6 +91,8 @@ def run_rms_fp8(nq, w, static_scale=None, norm_out=False, in_place=False):
                                       None if ss is not None else s, n)
     torch.cuda.synchronize()
     check_guard_u8(q_buf, M * d)
+    check_guard_bf16(ro_buf, M * d)
+    check_guard_bf16(n_buf, M * d)
     out = dict(q=host_u8(q), scale=None if ss is not None else s.cpu().numpy(),
                residual_out=host_u16(ro) if ro is not None else None,
                norm_out=host_u16(n) if n is not None else None)
@@ -121,7 +128,7 @@ def test_rms_fp8_2816(nq, orc, M):
     note(f"rms fp8 d=2816 M={M}")
     w = W.rms_2816(M)
     got = run_rms_fp8(nq, w)
-    compare_rms_fp8(orc, w, got, sample_rows(M, 96))
+    compare_rms_fp8(orc, w, got, EVERY_ROW)
 
 
 @pytest.mark.parametrize("scale", [0.01, 0.05, 1.0, 10.0])
@@ -138,7 +145,7 @@ def test_rms_fp8_ragged_d(nq, orc, d, M):
     note(f"rms fp8 ragged d={d} M={M}")
     w = W.rms_rows(M, d, 2 if d >= 16 else 0, 20.0, seed=d)
     got = run_rms_fp8(nq, w, norm_out=True)
-    compare_rms_fp8(orc, w, got, sample_rows(M, 24), norm_out=True)
+    compare_rms_fp8(orc, w, got, EVERY_ROW, norm_out=True)
 
 
 def test_rms_fp8_in_place_and_residual_less(nq, orc):
@@ -215,6 +222,7 @@ def run_rms_group(nq, w, ue8m0=False, bf16_source=False, norm_out=False, in_plac
     G = d // 128
     x = to_dev_bf16(w["x"])
     r = to_dev_bf16(w["residual"]) if w["residual"] is not None else None
+    ro_buf = None
     if r is not None and in_place:
         ro = r
     elif r is not None:
@@ -232,6 +240,8 @@ def run_rms_group(nq, w, ue8m0=False, bf16_source=False, norm_out=False, in_plac
         flags=nq.NQ_FLAG_BF16_SOURCE if bf16_source else 0, norm_out=n)
     torch.cuda.synchronize()
     check_guard_u8(q_buf, M * d)
+    check_guard_bf16(ro_buf, M * d)
+    check_guard_bf16(n_buf, M * d)
     sh = s_buf.cpu().numpy()
     assert np.all(np.isnan(sh[M * ld_s:])), "write past the end of scale_out"
     if ld_s > G:  # the padding columns of every scale row are untouched
@@ -262,7 +272,7 @@ def test_rms_group_7168(nq, orc, M, ue8m0):
     note(f"rms group fp8 d=7168 M={M} ue8m0={ue8m0}")
     w = W.rms_group_7168(M)
     got = run_rms_group(nq, w, ue8m0=ue8m0)
-    compare_rms_group(orc, w, got, sample_rows(M, 40), ue8m0=ue8m0)
+    compare_rms_group(orc, w, got, EVERY_ROW, ue8m0=ue8m0)
 
 
 @pytest.mark.parametrize("M", [1, 16, 1101, 8192])
@@ -270,7 +280,7 @@ def test_rms_group_2816(nq, orc, M):
     note(f"rms group fp8 d=2816 M={M}")
     w = W.rms_2816(M, seed=7)
     got = run_rms_group(nq, w, norm_out=(M == 16))
-    compare_rms_group(orc, w, got, sample_rows(M, 64), norm_out=(M == 16))
+    compare_rms_group(orc, w, got, EVERY_ROW, norm_out=(M == 16))
 
 
 @pytest.mark.parametrize("ue8m0", [False, True])
@@ -296,7 +306,7 @@ def test_rms_group_ragged_d(nq, orc, d, M):
     note(f"rms group fp8 d={d} M={M}")
     w = W.rms_rows(M, d, 2, 20.0, seed=d + 1)
     got = run_rms_group(nq, w, norm_out=True)
-    compare_rms_group(orc, w, got, sample_rows(M, 24), norm_out=True)
+    compare_rms_group(orc, w, got, EVERY_ROW, norm_out=True)
 
 
 def test_rms_group_in_place_residual_less_strided_scales(nq, orc):
@@ -371,11 +381,11 @@ def run_ln(nq, w, scale_t=None):
     return host_u8(q)
 
 
-def test_layernorm_full_config_sampled(nq, orc):
+def test_layernorm_full_config(nq, orc):
     note("layernorm M=16384 d=4096")
     w = W.layernorm_rows()
     q = run_ln(nq, w)
-    rows = sample_rows(w["M"], 96)
+    rows = EVERY_ROW
     o = orc.layernorm_quant_fp8(w["x"][rows], w["gamma"], w["beta"], w["eps"], w["scale"])
     assert_codes(q[rows], o["q"], "ln q")
 
@@ -386,7 +396,7 @@ def test_layernorm_shapes(nq, orc, d, M):
     note(f"layernorm d={d} M={M}")
     w = W.layernorm_rows(M=M, d=d, seed=d + M)
     q = run_ln(nq, w)
-    rows = sample_rows(M, 24)
+    rows = EVERY_ROW
     o = orc.layernorm_quant_fp8(w["x"][rows], w["gamma"], w["beta"], w["eps"], w["scale"])
     assert_codes(q[rows], o["q"], "ln q")
 
@@ -430,6 +440,38 @@ def test_layernorm_graph_replay_reads_scale_on_device(nq, orc):
         assert_codes(host_u8(q), o["q"], f"ln q under replay, scale {sc}")
 
 
+def test_layernorm_config_graph_replay_full_size(nq, orc):
+    """The LayerNorm workload as specified: M=16384, d=4096, static scale in a
+    one-element device tensor, the call captured once in a hipGraph, the
+    scale changed between replays, and every replay's whole output compared
+    with the oracle for the scale it held."""
+    note("layernorm M=16384 d=4096 graph replay, scale updated")
+    w = W.layernorm_rows()
+    M, d = w["M"], w["d"]
+    x = to_dev_bf16(w["x"])
+    g, b = to_dev_f32(w["gamma"]), to_dev_f32(w["beta"])
+    scale = to_dev_f32([w["scale"]])
+    q_buf, q = guarded_u8(M, d)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        nq.nq_layernorm_quant_fp8(x, g, b, w["eps"], scale, q, stream=s)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nq.nq_layernorm_quant_fp8(x, g, b, w["eps"], scale, q)
+    for sc in (w["scale"], 0.01, 1.0, 10.0, w["scale"]):
+        scale.fill_(sc)
+        q.fill_(0xA5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        check_guard_u8(q_buf, M * d)
+        o = orc.layernorm_quant_fp8(w["x"], w["gamma"], w["beta"], w["eps"], sc)
+        assert_codes(host_u8(q), o["q"], f"ln q, graph replay with scale {sc}")
+
+
 # ------------------------------------------------------- group FP8 --------
 
 def run_group(nq, x_bits, ue8m0, K=None):
@@ -451,7 +493,7 @@ def test_group_config(nq, orc, M, ue8m0):
     note(f"group M={M} K=4096 ue8m0={ue8m0}")
     w = W.group_t3(M)
     q, s = run_group(nq, w["x"], ue8m0)
-    rows = sample_rows(M, 128)
+    rows = EVERY_ROW
     o = orc.per_token_group_quant_fp8(w["x"][rows], 128, ue8m0=ue8m0)
     # scales and codes are bit-exact by construction (exact max, one
     # correctly rounded division and reciprocal per group)
@@ -496,14 +538,16 @@ def run_nvfp4(nq, w, sg, norm_out=False, slice_buf=False):
     x = to_dev_bf16(w["x"])
     xin = x[:, :d]
     r = to_dev_bf16(w["residual"]) if w["residual"] is not None else None
-    ro = torch.empty(M, d, dtype=torch.bfloat16, device="cuda") if r is not None else None
+    ro_buf, ro = guarded_bf16(M, d) if r is not None else (None, None)
     q_buf, q = guarded_u8(M, d // 2)
     sf_buf, sf = guarded_u8(M, d // 16)
-    n = torch.empty(M, d, dtype=torch.bfloat16, device="cuda") if norm_out else None
+    n_buf, n = guarded_bf16(M, d) if norm_out else (None, None)
     nq.nq_rmsnorm_quant_nvfp4(xin, r, ro, to_dev_f32(w["gamma"]), w["eps"], to_dev_f32([sg]), q, sf, n)
     torch.cuda.synchronize()
     check_guard_u8(q_buf, M * d // 2)
     check_guard_u8(sf_buf, M * d // 16)
+    check_guard_bf16(ro_buf, M * d)
+    check_guard_bf16(n_buf, M * d)
     if slice_buf:  # the unread columns of the strided input are untouched
         assert_bits_equal(host_u16(x), w["x"], "input buffer")
     return dict(q=host_u8(q), sf=host_u8(sf), residual_out=host_u16(ro) if ro is not None else None,
@@ -536,7 +580,7 @@ def test_nvfp4_7168(nq, orc, M, sg_mult):
     w = W.nvfp4_7168(M)
     sg = calibrated_sg(orc, w) * sg_mult
     got = run_nvfp4(nq, w, sg, norm_out=(M == 64))
-    compare_nvfp4(orc, w, got, sample_rows(M, 48), sg, norm_out=(M == 64))
+    compare_nvfp4(orc, w, got, EVERY_ROW, sg, norm_out=(M == 64))
 
 
 def test_nvfp4_schedules_bitwise_equal(nq, orc):
@@ -558,7 +602,7 @@ def test_nvfp4_column_slice(nq, orc, M):
     w = W.nvfp4_slice(M)
     sg = calibrated_sg(orc, w)
     got = run_nvfp4(nq, w, sg, slice_buf=True)
-    compare_nvfp4(orc, w, got, sample_rows(M, 48), sg)
+    compare_nvfp4(orc, w, got, EVERY_ROW, sg)
 
 
 @pytest.mark.parametrize("d", [16, 32, 128, 8208])
@@ -588,6 +632,7 @@ def run_rms_fp8_ex(nq, w, flags, static_scale=None):
                                          None if ss is not None else s)
     torch.cuda.synchronize()
     check_guard_u8(q_buf, M * d)
+    check_guard_bf16(ro_buf, M * d)
     if ss is None:
         assert np.all(np.isnan(s_buf[M:].cpu().numpy()))
     return dict(q=host_u8(q), scale=s.cpu().numpy(), residual_out=host_u16(ro))
@@ -600,7 +645,7 @@ def test_rms_fp8_e5m2(nq, orc, M, static):
     w = W.rms_2816(M, seed=12)
     sc = 0.02 if static else None
     got = run_rms_fp8_ex(nq, w, nq.NQ_FLAG_E5M2, sc)
-    rows = sample_rows(M, 64)
+    rows = EVERY_ROW
     o = orc.fused_add_rmsnorm_quant_fp8(w["x"][rows], w["residual"][rows], w["gamma"], w["eps"],
                                         static_scale=sc, fmt="e5m2")
     assert_bits_equal(got["residual_out"][rows], o["residual_out"], "residual_out")
@@ -630,11 +675,11 @@ def run_ln_ex(nq, w, flags, scale=None):
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
-def test_layernorm_dynamic_full_config_sampled(nq, orc, fmt):
+def test_layernorm_dynamic_full_config(nq, orc, fmt):
     note(f"layernorm dynamic M=16384 d=4096 {fmt}")
     w = W.layernorm_rows()
     q, s = run_ln_ex(nq, w, nq.NQ_FLAG_E5M2 if fmt == "e5m2" else 0)
-    rows = sample_rows(w["M"], 96)
+    rows = EVERY_ROW
     o = orc.layernorm_quant_fp8(w["x"][rows], w["gamma"], w["beta"], w["eps"], None, fmt=fmt)
     assert_scales(s[rows], o["scale"], "ln dynamic scale")
     assert_codes(q[rows], o["q"], "ln dynamic q", fmt=fmt)
@@ -649,7 +694,7 @@ def test_layernorm_dynamic_shapes(nq, orc, d, M, fmt):
     note(f"layernorm dynamic d={d} M={M} {fmt}")
     w = W.layernorm_rows(M=M, d=d, seed=3 * d + M)
     q, s = run_ln_ex(nq, w, nq.NQ_FLAG_E5M2 if fmt == "e5m2" else 0)
-    rows = sample_rows(M, 24)
+    rows = EVERY_ROW
     o = orc.layernorm_quant_fp8(w["x"][rows], w["gamma"], w["beta"], w["eps"], None, fmt=fmt)
     assert_scales(s[rows], o["scale"], "ln dynamic scale")
     assert_codes(q[rows], o["q"], "ln dynamic q", fmt=fmt)
@@ -663,7 +708,7 @@ def test_layernorm_static_e5m2(nq, orc, scale, d, M):
     note(f"layernorm static e5m2 d={d} M={M} scale={scale}")
     w = W.layernorm_rows(M=M, d=d, seed=d + 7 * M)
     q, _ = run_ln_ex(nq, w, nq.NQ_FLAG_E5M2, scale)
-    rows = sample_rows(M, 24)
+    rows = EVERY_ROW
     o = orc.layernorm_quant_fp8(w["x"][rows], w["gamma"], w["beta"], w["eps"], scale, fmt="e5m2")
     assert_codes(q[rows], o["q"], "ln static e5m2 q", fmt="e5m2")
 
@@ -704,7 +749,7 @@ def test_group_e5m2(nq, orc, M, ue8m0):
     check_guard_u8(q_buf, M * 4096)
     assert np.all(np.isnan(s_buf[M * 32:].cpu().numpy()))
     qh, sh = host_u8(q), s.cpu().numpy().reshape(M, 32)
-    rows = sample_rows(M, 128)
+    rows = EVERY_ROW
     o = orc.per_token_group_quant_fp8(w["x"][rows], 128, ue8m0=ue8m0, fmt="e5m2")
     assert_bits_equal(sh[rows].view(np.uint32), o["scale"].view(np.uint32), "e5m2 group scales")
     assert_bits_equal(qh[rows], o["q"], "e5m2 group codes")
@@ -722,7 +767,7 @@ def test_rms_group_e5m2(nq, orc, bf16_source):
     flags = nq.NQ_FLAG_E5M2 | (nq.NQ_FLAG_BF16_SOURCE if bf16_source else 0)
     nq.nq_fused_add_rmsnorm_quant_fp8_group(x, r, ro, to_dev_f32(w["gamma"]), w["eps"], q, s, flags=flags)
     torch.cuda.synchronize()
-    rows = sample_rows(M, 40)
+    rows = EVERY_ROW
     o = orc.fused_add_rmsnorm_quant_fp8_group(w["x"][rows], w["residual"][rows], w["gamma"], w["eps"],
                                               bf16_source=bf16_source, fmt="e5m2")
     assert_bits_equal(host_u16(ro)[rows], o["residual_out"], "residual_out")
@@ -749,7 +794,7 @@ def test_nvfp4_bf16_source(nq, orc, M):
     torch.cuda.synchronize()
     check_guard_u8(q_buf, M * 3584)
     check_guard_u8(sf_buf, M * 448)
-    rows = sample_rows(M, 48)
+    rows = EVERY_ROW
     o = orc.rmsnorm_quant_nvfp4(w["x"][rows], w["residual"][rows], w["gamma"], w["eps"], sg, want_norm_out=True,
                                 mode_b=True)
     assert_bits_equal(host_u16(n)[rows], o["norm_out"], "norm_out")
@@ -777,6 +822,8 @@ def run_unfused(nq, w, static_scale=None, flags=0):
     nq.nq_per_token_quant_fp8(n, ss, flags, q, None if ss is not None else s)
     torch.cuda.synchronize()
     check_guard_u8(q_buf, M * d)
+    check_guard_bf16(ro_buf, M * d)
+    check_guard_bf16(n_buf, M * d)
     assert np.all(np.isnan(s_buf[M:].cpu().numpy()))
     return dict(norm=host_u16(n), residual_out=host_u16(ro), q=host_u8(q), scale=s.cpu().numpy())
 
@@ -789,7 +836,7 @@ def test_unfused_pipeline(nq, orc, M):
     note(f"unfused pipeline d=2816 M={M}")
     w = W.rms_2816(M, seed=13)
     got = run_unfused(nq, w)
-    rows = sample_rows(M, 64)
+    rows = EVERY_ROW
     f = orc.fused_add_rmsnorm_quant_fp8(w["x"][rows], w["residual"][rows], w["gamma"], w["eps"], want_norm_out=True)
     assert_bits_equal(got["residual_out"][rows], f["residual_out"], "residual_out")
     assert_bits_equal(got["norm"][rows], f["norm_out"], "bf16 norm output")
@@ -861,7 +908,7 @@ def test_bf16_gamma_rmsnorm_fp8(nq, orc, M, d):
     s = torch.empty(M, dtype=torch.float32, device="cuda")
     nq.nq_fused_add_rmsnorm_quant_fp8_ex(x, r, ro, gdev, w["eps"], None, 0, q, s)
     torch.cuda.synchronize()
-    rows = sample_rows(M, 32)
+    rows = EVERY_ROW
     o = orc.fused_add_rmsnorm_quant_fp8(w["x"][rows], w["residual"][rows], g32, w["eps"])
     assert_bits_equal(host_u16(ro)[rows], o["residual_out"], "residual_out")
     assert_scales(s.cpu().numpy()[rows], o["scale"], "scale")
@@ -884,7 +931,7 @@ def test_bf16_gamma_group_and_nvfp4(nq, orc):
     s = torch.empty(M, d // 128, dtype=torch.float32, device="cuda")
     nq.nq_fused_add_rmsnorm_quant_fp8_group(x, r, torch.empty_like(r), gdev, w["eps"], q, s)
     torch.cuda.synchronize()
-    rows = sample_rows(M, 32)
+    rows = EVERY_ROW
     o = orc.fused_add_rmsnorm_quant_fp8_group(w["x"][rows], w["residual"][rows], g32, w["eps"])
     assert_scales(s.cpu().numpy()[rows], o["scale"], "group scale")
     assert_codes(host_u8(q)[rows], o["q"], "group q")
@@ -912,7 +959,7 @@ def test_bf16_gamma_beta_layernorm(nq, orc, d, M, dynamic):
     sc = None if dynamic else to_dev_f32([w["scale"]])
     nq.nq_layernorm_quant_fp8_ex(x, gdev, bdev, w["eps"], sc, 0, q, s if dynamic else None)
     torch.cuda.synchronize()
-    rows = sample_rows(M, 24)
+    rows = EVERY_ROW
     o = orc.layernorm_quant_fp8(w["x"][rows], g32, b32, w["eps"], None if dynamic else w["scale"])
     if dynamic:
         assert_scales(s.cpu().numpy()[rows], o["scale"], "ln scale")
@@ -930,7 +977,7 @@ def test_max_hidden_size_every_row_entry_point(nq, orc, M):
     note(f"d=NQ_MAX_D={d} M={M}: layernorm static / dynamic e4m3 / dynamic e5m2")
     w = W.layernorm_rows(M=M, d=d, seed=M + 31)
     q = run_ln(nq, w)
-    rows = sample_rows(M, 12)
+    rows = EVERY_ROW
     o = orc.layernorm_quant_fp8(w["x"][rows], w["gamma"], w["beta"], w["eps"], w["scale"])
     assert_codes(q[rows], o["q"], "ln q")
     for fmt, fl in (("e4m3", 0), ("e5m2", nq.NQ_FLAG_E5M2)):

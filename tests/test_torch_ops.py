@@ -2,7 +2,9 @@
 
 CPU: every op traces under FakeTensorMode with the right output shapes and
 dtypes and returns fresh tensors (no output aliases an input).
-GPU: each op equals the C entry point it wraps bit for bit;
+GPU: every one of the 13 ops matches the CPU oracle on the same inputs, at a
+small size and at its workload's full size, with each of its flags
+exercised; the ops equal the C entry points they wrap bit for bit;
 torch.library.opcheck passes; compiled code (torch.compile, full graph) gives
 the eager result; and a poisoned-kernel probe ("Fusing RMSNorm and FP8
 Quantization Under torch.compile", "Gating": replace the kernel with a
@@ -199,3 +201,155 @@ def test_inductor_compiled_norm_linear(ops):
     torch.cuda.synchronize()
     assert torch.equal(z2, z)
     torch.testing.assert_close(out, eager, rtol=1e-5, atol=1e-5)
+
+
+# ------------------------------------------------- every op vs the oracle --
+#
+# Each of the 13 ops against the CPU oracle on the same seeded inputs, at a
+# small size and at its workload's full size, with every flag the op takes
+# exercised at least once (a flag or argument mixed up in the wrapper --
+# ue8m0 for bf16_source, a static scale dropped, e5m2 ignored -- changes
+# codes or scales and fails).  The NVFP4 column-slice op reads a strided view
+# of wider rows.  Tolerances: tests/parity.py.
+
+def _dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).cuda()
+
+
+def _u8(t):
+    return t.contiguous().view(torch.uint8).cpu().numpy()
+
+
+def _u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _fmt(e5m2):
+    return "e5m2" if e5m2 else "e4m3"
+
+
+# (op, M, d, variant): variants are the op's keyword flags
+ORACLE_CASES = [
+    ("add_rmsnorm_fp8", 64, 2816, {}), ("add_rmsnorm_fp8", 8192, 2816, {}),
+    ("add_rmsnorm_fp8", 64, 2816, {"e5m2": True}),
+    ("rmsnorm_fp8", 64, 2816, {}), ("rmsnorm_fp8", 333, 7168, {"e5m2": True}),
+    ("add_rmsnorm_fp8_static", 64, 2816, {}), ("add_rmsnorm_fp8_static", 8192, 2816, {}),
+    ("add_rmsnorm_fp8_static", 64, 2816, {"e5m2": True}),
+    ("rmsnorm_fp8_static", 64, 2816, {}), ("rmsnorm_fp8_static", 77, 4096, {"e5m2": True}),
+    ("add_rmsnorm_fp8_group", 64, 7168, {}), ("add_rmsnorm_fp8_group", 8192, 7168, {}),
+    ("add_rmsnorm_fp8_group", 64, 7168, {"ue8m0": True}),
+    ("add_rmsnorm_fp8_group", 64, 7168, {"bf16_source": True}),
+    ("add_rmsnorm_fp8_group", 64, 7168, {"e5m2": True}),
+    ("rmsnorm_fp8_group", 64, 2816, {}), ("rmsnorm_fp8_group", 64, 2816, {"ue8m0": True, "bf16_source": True}),
+    ("rmsnorm_fp8_group", 64, 2816, {"e5m2": True}),
+    ("group_quant_fp8", 64, 4096, {}), ("group_quant_fp8", 32768, 4096, {}),
+    ("group_quant_fp8", 64, 4096, {"ue8m0": True}), ("group_quant_fp8", 64, 4096, {"e5m2": True}),
+    ("layernorm_fp8_static", 64, 4096, {}), ("layernorm_fp8_static", 16384, 4096, {}),
+    ("layernorm_fp8_static", 64, 4096, {"e5m2": True}),
+    ("layernorm_fp8", 64, 4096, {}), ("layernorm_fp8", 16384, 4096, {}),
+    ("layernorm_fp8", 64, 4096, {"e5m2": True}),
+    ("add_rmsnorm_nvfp4", 64, 7168, {}), ("add_rmsnorm_nvfp4", 8192, 7168, {}),
+    ("add_rmsnorm_nvfp4", 64, 7168, {"bf16_source": True}),
+    ("rmsnorm_nvfp4", 64, 1536, {}), ("rmsnorm_nvfp4", 8192, 1536, {}),
+    ("rmsnorm_nvfp4", 64, 1536, {"bf16_source": True}),
+    ("add_rmsnorm_bf16", 64, 2816, {}), ("add_rmsnorm_bf16", 8192, 2816, {}),
+    ("per_token_quant_fp8", 64, 2816, {}), ("per_token_quant_fp8", 8192, 2816, {}),
+    ("per_token_quant_fp8", 64, 2816, {"e5m2": True}),
+]
+
+
+def test_oracle_cases_cover_every_op(ops):
+    assert {c[0] for c in ORACLE_CASES} == set(ops.OPS)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,M,d,kw", ORACLE_CASES,
+                         ids=[f"{c[0]}-{c[1]}x{c[2]}-{'-'.join(c[3]) or 'default'}" for c in ORACLE_CASES])
+def test_every_op_against_the_oracle(ops, orc, name, M, d, kw):
+    from tests.parity import assert_bits_equal, assert_codes, assert_scales, unpack_nibbles
+    print(f"[case] torch op {name} M={M} d={d} {kw}", flush=True)
+    op = getattr(torch.ops.nq, name)
+    e5m2 = kw.get("e5m2", False)
+    fmt = _fmt(e5m2)
+    if name == "group_quant_fp8":
+        w = W.group_t3(M, d, seed=M + 1)
+        q, s = op(_dev_bf16(w["x"]), kw.get("ue8m0", False), e5m2)
+        o = orc.per_token_group_quant_fp8(w["x"], 128, ue8m0=kw.get("ue8m0", False), fmt=fmt)
+        assert_bits_equal(s.cpu().numpy().view(np.uint32), o["scale"].view(np.uint32), f"{name} scales")
+        assert_bits_equal(_u8(q), o["q"], f"{name} codes")
+        return
+    if name.startswith("layernorm"):
+        w = W.layernorm_rows(M, d, seed=M + 2)
+        x, g, b = _dev_bf16(w["x"]), torch.from_numpy(w["gamma"]).cuda(), torch.from_numpy(w["beta"]).cuda()
+        if name == "layernorm_fp8_static":
+            q = op(x, g, b, w["eps"], torch.tensor([w["scale"]], device="cuda"), e5m2)
+            o = orc.layernorm_quant_fp8(w["x"], w["gamma"], w["beta"], w["eps"], w["scale"], fmt=fmt)
+        else:
+            q, s = op(x, g, b, w["eps"], e5m2)
+            o = orc.layernorm_quant_fp8(w["x"], w["gamma"], w["beta"], w["eps"], None, fmt=fmt)
+            assert_scales(s.cpu().numpy(), o["scale"], f"{name} scales")
+        assert_codes(_u8(q), o["q"], f"{name} codes", fmt=fmt)
+        return
+    if name == "rmsnorm_nvfp4":  # a column slice of wider rows, read in place
+        w = W.nvfp4_slice(M, seed=M + 3)
+        buf = _dev_bf16(w["x"])
+        g = torch.from_numpy(w["gamma"]).cuda()
+        gs = W.NVFP4_NOMINAL_GLOBAL_SCALE
+        q, sf = op(buf[:, :d], g, w["eps"], torch.tensor([gs], device="cuda"), kw.get("bf16_source", False))
+        o = orc.rmsnorm_quant_nvfp4(w["x"], None, w["gamma"], w["eps"], gs, d=d,
+                                    mode_b=kw.get("bf16_source", False))
+        assert_codes(_u8(sf), o["sf"], f"{name} block scales")
+        assert_codes(unpack_nibbles(_u8(q)), unpack_nibbles(o["q"]), f"{name} codes", fmt="e2m1")
+        assert_bits_equal(_u16(buf), w["x"], "input buffer untouched")
+        return
+    w = W.rms_rows(M, d, max(1, d // 100), 50.0, seed=M + d)
+    x, r, g = _dev_bf16(w["x"]), _dev_bf16(w["residual"]), torch.from_numpy(w["gamma"]).cuda()
+    res = name.startswith("add_")
+    rh = w["residual"] if res else None
+    if name == "add_rmsnorm_nvfp4":
+        gs = W.NVFP4_NOMINAL_GLOBAL_SCALE
+        q, sf, ro = op(x, r, g, w["eps"], torch.tensor([gs], device="cuda"), kw.get("bf16_source", False))
+        o = orc.rmsnorm_quant_nvfp4(w["x"], rh, w["gamma"], w["eps"], gs, mode_b=kw.get("bf16_source", False))
+        assert_bits_equal(_u16(ro), o["residual_out"], f"{name} residual")
+        assert_codes(_u8(sf), o["sf"], f"{name} block scales")
+        assert_codes(unpack_nibbles(_u8(q)), unpack_nibbles(o["q"]), f"{name} codes", fmt="e2m1")
+        return
+    if name in ("add_rmsnorm_fp8_group", "rmsnorm_fp8_group"):
+        flags = (kw.get("ue8m0", False), kw.get("bf16_source", False), e5m2)
+        out = op(x, r, g, w["eps"], *flags) if res else op(x, g, w["eps"], *flags)
+        o = orc.fused_add_rmsnorm_quant_fp8_group(w["x"], rh, w["gamma"], w["eps"], ue8m0=flags[0],
+                                                  bf16_source=flags[1], fmt=fmt)
+        assert_scales(out[1].cpu().numpy(), o["scale"], f"{name} scales")
+        assert_codes(_u8(out[0]), o["q"], f"{name} codes", fmt=fmt)
+        if res:
+            assert_bits_equal(_u16(out[2]), o["residual_out"], f"{name} residual")
+        return
+    if name == "add_rmsnorm_bf16":
+        n, ro = op(x, r, g, w["eps"])
+        o = orc.fused_add_rmsnorm_quant_fp8(w["x"], rh, w["gamma"], w["eps"], want_norm_out=True)
+        assert_bits_equal(_u16(n), o["norm_out"], f"{name} norm")
+        assert_bits_equal(_u16(ro), o["residual_out"], f"{name} residual")
+        return
+    if name == "per_token_quant_fp8":
+        q, s = op(x, e5m2)
+        o = orc.quant_fp8_rows(W.bf16_bits_to_f32(w["x"]), fmt=fmt)
+        assert_scales(s.cpu().numpy(), o["scale"], f"{name} scales")
+        assert_codes(_u8(q), o["q"], f"{name} codes", fmt=fmt)
+        return
+    static = name.endswith("_static")
+    sc = torch.tensor([0.05], device="cuda")
+    if name == "add_rmsnorm_fp8":
+        q, s, ro = op(x, r, g, w["eps"], e5m2)
+    elif name == "rmsnorm_fp8":
+        q, s = op(x, g, w["eps"], e5m2)
+    elif name == "add_rmsnorm_fp8_static":
+        q, ro = op(x, r, g, w["eps"], sc, e5m2)
+    else:
+        q = op(x, g, w["eps"], sc, e5m2)
+    o = orc.fused_add_rmsnorm_quant_fp8(w["x"], rh, w["gamma"], w["eps"], static_scale=0.05 if static else None,
+                                        fmt=fmt)
+    if not static:
+        assert_scales(s.cpu().numpy(), o["scale"], f"{name} scales")
+    if res:
+        assert_bits_equal(_u16(ro), o["residual_out"], f"{name} residual")
+    assert_codes(_u8(q), o["q"], f"{name} codes", fmt=fmt)
