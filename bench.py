@@ -729,8 +729,13 @@ def suite_cases(torch, nq):
     return cases
 
 
-def run_suite(torch, nq):
+def run_suite(torch, nq, only=None):
     cases = suite_cases(torch, nq)
+    if only:
+        unknown = set(only) - {n for n, _ in cases}
+        if unknown:
+            raise SystemExit(f"bench.py: unknown suite workloads {sorted(unknown)}")
+        cases = [c for c in cases if c[0] in only]
     built, lines = [], []
     for name, make in cases:  # each workload alone: warm replays, then timed replays back to back
         case = make()
@@ -760,6 +765,8 @@ def main():
     ap.add_argument("--steps", type=int, default=DEFAULT_STEPS)
     ap.add_argument("--warmup", type=int, default=DEFAULT_WARMUP)
     ap.add_argument("--suite", action="store_true", help="also time all five workloads (stderr)")
+    ap.add_argument("--suite-cases", metavar="A,B,...",
+                    help="time only these suite workloads (comma-separated names), then exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-mode", action="store_true",
                     help="short fixed run for rocprofv3: copy reference + main kernel steps")
@@ -805,6 +812,10 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     from fp4_quantization_amd import nq
+
+    if args.suite_cases:
+        run_suite(torch, nq, args.suite_cases.split(","))
+        return
 
     if args.profile_workload:
         case = dict(suite_cases(torch, nq))[args.profile_workload]()

@@ -99,6 +99,41 @@ __device__ __forceinline__ uint2 fp8x8(const float v[8])
     return make_uint2(fp8x4<F>(v[0], v[1], v[2], v[3]), fp8x4<F>(v[4], v[5], v[6], v[7]));
 }
 
+// FP8 of values known to be at most fmax * (1 + 2^-21) in magnitude: the
+// native conversion alone, with no clamp.  It rounds to nearest even and
+// first leaves the finite range at 464 (e4m3) and 61440 (e5m2), so every
+// such value gets the code of its clamped value.  Quotients by a dynamic
+// scale s = RN(amax / fmax) that is a normal number are bounded so:
+// |y| / s <= amax / s <= fmax / (1 - 2^-24), and the quotient's rounding
+// adds one more unit in the last place.  Checked exhaustively against the
+// oracle's codec up to that bound (NQ_CODEC_*_BOUNDED).
+template <Fp8 F>
+__device__ __forceinline__ uint32_t fp8x4_bounded(float a, float b, float c, float d)
+{
+    if constexpr (F == Fp8::E5M2) {
+        int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+    } else {
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    }
+}
+
+template <Fp8 F>
+__device__ __forceinline__ uint2 fp8x8_bounded(const float v[8])
+{
+    return make_uint2(fp8x4_bounded<F>(v[0], v[1], v[2], v[3]), fp8x4_bounded<F>(v[4], v[5], v[6], v[7]));
+}
+
+// True when every lane of the wavefront holds a normal dynamic scale, so
+// its quotients are bounded as fp8x8_bounded needs (a zero, subnormal or
+// non-finite scale anywhere sends the whole wavefront through the clamped
+// conversion).
+__device__ __forceinline__ bool wave_scales_normal(float s)
+{
+    return __builtin_amdgcn_ballot_w64(!(s >= 0x1p-126f && s <= 0x1p127f)) == 0;
+}
+
 // Decode of an e4m3 code (used for the NVFP4 block scale): sign, 4-bit
 // exponent with bias 7, 3-bit mantissa, subnormals at exponent 0.  Codes
 // reaching here come from e4m3x4 of a non-negative clamped value, so never
@@ -140,17 +175,28 @@ __device__ __forceinline__ uint32_t e2m1x8(const float v[8])
 // Across the four rows of a wavefront the row results are read into scalar
 // registers and combined in a fixed order; across 32 lanes one cross-lane
 // exchange finishes the pair of rows.
+//
+// Every lane of the wavefront executes these exchanges (no reduction sits in
+// a divergent branch), and every pattern reads a lane of the same row, so
+// the moves are issued with bound_ctrl: no lane ever keeps its old value,
+// and the compiler needs no register initialised for it (and can fold a
+// move into the instruction that consumes it).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
 }
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v)
 {
     const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    const uint32_t lo = dpp_u32<CTRL>((uint32_t)u);
+    const uint32_t hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 __device__ __forceinline__ double readlane_f64(double v, int lane)
@@ -160,9 +206,9 @@ __device__ __forceinline__ double readlane_f64(double v, int lane)
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
-__device__ __forceinline__ float readlane_f32(float v, int lane)
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }
 
 constexpr int kDppXor1 = 0xB1;        // quad_perm 1,0,3,2
@@ -184,18 +230,33 @@ __device__ __forceinline__ double group_sum(double v)
     return v;
 }
 
+// Maxima here are maxima of absolute values: non-negative binary32 (or NaN
+// from a non-finite input) order exactly as their bit patterns do as
+// unsigned integers, so one integer max per step replaces the float max and
+// the quieting of its DPP operand (NaN, 0x7FC00000 and up, still wins).
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
 template <int W>
-__device__ __forceinline__ float group_max(float v)
+__device__ __forceinline__ float group_max(float x)
 {
     static_assert(W == 16 || W == 32 || W == 64, "group of 16, 32 or 64 lanes");
-    v = fmaxf(v, dpp_f32<kDppXor1>(v));
-    v = fmaxf(v, dpp_f32<kDppXor2>(v));
-    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
-    v = fmaxf(v, dpp_f32<kDppMirror>(v));
-    if constexpr (W == 32) v = fmaxf(v, __shfl_xor(v, 16, kWave));
+    uint32_t v = __builtin_bit_cast(uint32_t, x);
+    v = umax(v, dpp_u32<kDppXor1>(v));
+    v = umax(v, dpp_u32<kDppXor2>(v));
+    v = umax(v, dpp_u32<kDppHalfMirror>(v));
+    v = umax(v, dpp_u32<kDppMirror>(v));
+    if constexpr (W == 32) v = umax(v, (uint32_t)__shfl_xor((int)v, 16, kWave));
     if constexpr (W == 64)
-        v = fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
-    return v;
+        v = umax(umax(readlane_u32(v, 0), readlane_u32(v, 16)), umax(readlane_u32(v, 32), readlane_u32(v, 48)));
+    return __builtin_bit_cast(float, v);
+}
+
+// Maximum of a non-negative value (an absolute maximum) over lanes t and
+// t ^ 1: one DPP exchange inside each quad.
+__device__ __forceinline__ float pair_max(float x)
+{
+    const uint32_t v = __builtin_bit_cast(uint32_t, x);
+    return __builtin_bit_cast(float, umax(v, dpp_u32<kDppXor1>(v)));
 }
 
 // Max over each aligned group of 16 lanes (one DPP row).
@@ -235,10 +296,10 @@ __device__ __forceinline__ float team_max(float v, float* lds)
         if ((threadIdx.x & (kWave - 1)) == 0) lds[wave] = v;
         __syncthreads();
         const int first = wave / NW * NW;
-        float s = lds[first];
+        uint32_t s = __builtin_bit_cast(uint32_t, lds[first]);
 #pragma unroll
-        for (int i = 1; i < NW; ++i) s = fmaxf(s, lds[first + i]);
-        v = s;
+        for (int i = 1; i < NW; ++i) s = umax(s, __builtin_bit_cast(uint32_t, lds[first + i]));
+        v = __builtin_bit_cast(float, s);
     }
     return v;
 }
@@ -261,11 +322,12 @@ __device__ __forceinline__ float pow2_ceil(float t)
 // binary floating point).  The remainder is a multiple of 2^(e_y - 46)
 // below 2^(e_y - 22), so it is exact for |y| >= 2^-103; the theorem also
 // needs a normal s, no overflow and a quotient of at least 2^-126.  For
-// smaller y the result is within one ulp; a kernel meets such y with a
+// smaller y the quotient can be off, but a kernel meets such y with a
 // quotient whose FP8 code can be non-zero only in rows whose maximum is
 // below 2^-84.  Three operations per element instead of a full division
 // sequence.  Checked on the device against correctly rounded division over
-// random and edge operands (test_div_by_matches_division).
+// random and edge operands, codes included where the quotient is not
+// exact (test_div_by_matches_division).
 __device__ __forceinline__ float div_by(float y, float s, float inv)
 {
     const float q0 = y * inv;
@@ -546,6 +608,63 @@ __device__ __forceinline__ void unpack_bf16x8(uint4 w, float v[8])
     v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
     v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
 }
+
+// Sum of the squares of one chunk of 8 bf16 values (packed), in binary64.
+// Every square is exact in binary64, so the chunk sum rounds at most in its
+// last bit.
+__device__ __forceinline__ double sumsq_chunk(uint4 w)
+{
+    float z[8];
+    unpack_bf16x8(w, z);
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const double zd = (double)z[k];
+        acc = fma(zd, zd, acc);
+    }
+    return acc;
+}
+
+
+// Row sums in binary32 chunks with a binary64 safety net.  Each 8-element
+// chunk is summed in binary32 and the chunk sums are added in binary64.  A
+// chunk sum is trusted while it lies in a range where neither an overflow
+// nor flushed or subnormal products can have touched it; a lane holding a
+// chunk outside that range sums all its chunks exactly in binary64 instead
+// (a branch no wavefront takes on ordinary data).  Within the range the
+// binary32 sum is the exact one to within its few roundings (2^-24 relative
+// each; a sum of squares has no cancellation, and a plain sum of bf16
+// values only rounds when they span more than 2^16 in magnitude).
+
+// Sum of the 8 bf16 values of a packed chunk: four packed bf16 dot products
+// with (1, 1).
+__device__ __forceinline__ float sum_chunk_f32(uint4 w)
+{
+    const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+    float p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), one, 0.0f, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), one, p, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), one, p, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), one, p, false);
+}
+// Whether a chunk's binary32 plain sum can be trusted: tiny (or cancelled),
+// huge and non-finite sums are recomputed.
+__device__ __forceinline__ bool sum_ok(float p)
+{
+    const float a = __builtin_fabsf(p);
+    return a >= 0x1p-100f && a <= 0x1p100f;
+}
+
+// Sum of the squares of 8 binary32 values.
+__device__ __forceinline__ float sumsq_chunk_f32(const float c[8])
+{
+    float p = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p = __builtin_fmaf(c[k], c[k], p);
+    return p;
+}
+// Whether a chunk's binary32 sum of squares can be trusted (its squares
+// cannot have underflowed or overflowed).
+__device__ __forceinline__ bool sumsq_ok(float p) { return p >= 0x1p-60f && p <= 0x1p60f; }
 
 // 8 fp32 (two 16-byte loads) of a vector such as gamma.
 template <bool VEC, int POLICY>

@@ -9,9 +9,17 @@
 //
 // One HBM read of the bf16 row and one write of its codes (3 bytes per
 // element, [LNQ] "Description").  Both statistics come from the registers:
-// the mean (binary64 partial sums, rounded to binary32 once), then the
-// population variance of c = x - mean (c^2 is exact in binary64), so a
-// large mean costs no precision.
+// the mean, then the population variance of c = x - mean (two passes, so a
+// large mean costs no precision).  Each 8-element chunk is summed in
+// binary32 (sum_chunk / sumsq_chunk in nq_device.hpp: a packed bf16 dot
+// product for the mean, fused multiply-adds for c^2), the chunk sums are
+// added in binary64, and a chunk whose binary32 sum leaves a safe range is
+// summed exactly in binary64 instead.  The result is the binary64 row sum
+// to within a few binary32 roundings of the chunk sums -- a relative 2^-22 of
+// the variance at most -- so a row's rstd can differ from the exactly summed
+// one by one unit in the last place: within the reduction-order tolerance,
+// and the kernel's instruction count drops by a fifth (it is bound by vector
+// issue as much as by HBM).
 #include "nq_device.hpp"
 #include "nq_host.hpp"
 #include "nq_rows.hpp"
@@ -65,20 +73,32 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t) * 8;
-        xw[j] = xio.load16(e, e < d);
+        xw[j] = xio.load16(e, col_live<TEAM, VEC>(e, d));
     }
     gb.issue(t);
     if constexpr (kLoadPriority) __builtin_amdgcn_s_setprio(0);
 
-    // mean = sum(x) / d; every bf16 x is exact in binary64 (masked = 0).
-    // The unpacked row is what c replaces below, so it stays unpacked.
+    // mean = sum(x) / d (masked elements load as 0).  The unpacked row is
+    // what c replaces below, so it stays unpacked.
     float c[CPL][8];
     double acc = 0.0;
+    bool ok = true;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
+        const float p = sum_chunk_f32(xw[j]);
+        ok = ok && sum_ok(p);
+        acc += (double)p;
         unpack_bf16x8(xw[j], c[j]);
+    }
+    if (__builtin_amdgcn_ballot_w64(!ok) != 0) {
+        __asm__ volatile("");  // keep it a branch
+        if (!ok) {
+            acc = 0.0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc += (double)c[j][k];
+            for (int j = 0; j < CPL; ++j)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc += (double)c[j][k];
+        }
     }
     gb.publish(lds_gb);
     acc = team_sum<TEAM>(acc, lds_mean);
@@ -86,22 +106,41 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
     __builtin_amdgcn_sched_barrier(0);
 
     // c = x - mean (binary32), held in registers (at most 32 per lane);
-    // var = sum(c^2) / d over the d real elements (c^2 is exact in
-    // binary64).  A chunk past the row end contributes nothing.
+    // var = sum(c^2) / d over the d real elements.  A chunk past the row end
+    // contributes nothing; on the element-wise path the elements of the last
+    // chunk past the end are left out of its sum.
     double acc2 = 0.0;
+    bool ok2 = true;
     const int t1 = opaque(t);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t1) * 8;
-        double part = 0.0;
+        float sq[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             c[j][k] = c[j][k] - mu;
             const bool live = VEC || e + k < d;  // whole chunks on the 128-bit path
-            const double cd = live ? (double)c[j][k] : 0.0;
-            part = fma(cd, cd, part);
+            sq[k] = live ? c[j][k] : 0.0f;
         }
-        acc2 += e < d ? part : 0.0;
+        const float p = sumsq_chunk_f32(sq);
+        const bool in_row = e < d;
+        ok2 = ok2 && (sumsq_ok(p) || !in_row);
+        acc2 += in_row ? (double)p : 0.0;
+    }
+    if (__builtin_amdgcn_ballot_w64(!ok2) != 0) {
+        __asm__ volatile("");  // keep it a branch
+        if (!ok2) {
+            acc2 = 0.0;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int e = (j * TEAM + t1) * 8;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const double cd = (VEC ? e < d : e + k < d) ? (double)c[j][k] : 0.0;
+                    acc2 = fma(cd, cd, acc2);
+                }
+            }
+        }
     }
     acc2 = team_sum<TEAM>(acc2, lds_var);
     const float var = (float)div_by_len(acc2, (double)d, a.inv_d);
@@ -125,7 +164,7 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
                 const float y = gn + b[k];
                 v[k] = y * inv;
             }
-            qio.store8(e, e < d, fp8x8<F>(v));
+            qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8<F>(v));
         }
     } else {
         // Dynamic per-token: y replaces c in the registers, its absolute
@@ -157,7 +196,7 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
             float v[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) v[k] = div_by(c[j][k], s, inv);
-            qio.store8(e, e < d, fp8x8<F>(v));
+            qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8<F>(v));
         }
     }
 }

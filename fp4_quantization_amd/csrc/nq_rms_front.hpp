@@ -46,47 +46,34 @@ __device__ __forceinline__ float rms_front(const uint16_t* x, int64_t ld_x, cons
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int e = (j * TEAM + t) * 8;
-            xw[j] = xio.load16(e, e < d);
-            rw[j] = rio.load16(e, e < d);
+            xw[j] = xio.load16(e, col_live<TEAM, VEC>(e, d));
+            rw[j] = rio.load16(e, col_live<TEAM, VEC>(e, d));
         }
         vecs.issue(t);
         // z = bf16(x + r), kept packed; residual write-back; sum of z^2.
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int e = (j * TEAM + t) * 8;
-            float xv[8], rv[8], z[8];
+            float xv[8], rv[8];
             unpack_bf16x8(xw[j], xv);
             unpack_bf16x8(rw[j], rv);
             uint32_t p[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) p[k] = pack_bf16x2(xv[2 * k] + rv[2 * k], xv[2 * k + 1] + rv[2 * k + 1]);
             zw[j] = make_uint4(p[0], p[1], p[2], p[3]);
-            roio.store16(e, e < d, zw[j]);
-            unpack_bf16x8(zw[j], z);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const double zd = (double)z[k];
-                acc = fma(zd, zd, acc);  // z^2 is exact in binary64
-            }
+            roio.store16(e, col_live<TEAM, VEC>(e, d), zw[j]);
+            acc += sumsq_chunk(zw[j]);
         }
     } else {
         // Residual-less: z is x itself (a bf16 value).
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int e = (j * TEAM + t) * 8;
-            zw[j] = xio.load16(e, e < d);
+            zw[j] = xio.load16(e, col_live<TEAM, VEC>(e, d));
         }
         vecs.issue(t);
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            float z[8];
-            unpack_bf16x8(zw[j], z);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const double zd = (double)z[k];
-                acc = fma(zd, zd, acc);
-            }
-        }
+        for (int j = 0; j < CPL; ++j) acc += sumsq_chunk(zw[j]);
     }
     __builtin_amdgcn_sched_barrier(0);
 

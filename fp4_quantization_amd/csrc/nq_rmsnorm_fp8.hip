@@ -94,7 +94,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
         if (a.norm_out) {
             const uint4 nw = make_uint4(pack_bf16x2(y[j][0], y[j][1]), pack_bf16x2(y[j][2], y[j][3]),
                                         pack_bf16x2(y[j][4], y[j][5]), pack_bf16x2(y[j][6], y[j][7]));
-            nio.store16(e, e < d, nw);
+            nio.store16(e, col_live<TEAM, VEC>(e, d), nw);
         }
     }
 
@@ -108,13 +108,24 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
         const float s = amax / fp8_max<F>();
         if (t == 0 && m.ok) a.scale_out[m.row] = s;
         const float inv = s > 0.0f ? 1.0f / s : 0.0f;
+        if (wave_scales_normal(s)) {
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-            const int e = (j * TEAM + t1) * 8;
-            float v[8];
+            for (int j = 0; j < CPL; ++j) {
+                const int e = (j * TEAM + t1) * 8;
+                float v[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = div_by(y[j][k], s, inv);
-            qio.store8(e, e < d, fp8x8<F>(v));
+                for (int k = 0; k < 8; ++k) v[k] = div_by(y[j][k], s, inv);
+                qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8_bounded<F>(v));
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const int e = (j * TEAM + t1) * 8;
+                float v[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = div_by(y[j][k], s, inv);
+                qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8<F>(v));
+            }
         }
     } else {
         const float inv = 1.0f / a.static_scale[0];
@@ -124,7 +135,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
             float v[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) v[k] = y[j][k] * inv;
-            qio.store8(e, e < d, fp8x8<F>(v));
+            qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8<F>(v));
         }
     }
 }

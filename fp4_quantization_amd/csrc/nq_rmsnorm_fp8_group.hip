@@ -93,7 +93,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8_group(RmsGroupArgs a)
         if (a.bf16_source || a.norm_out) {
             const uint4 nw = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
                                         pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
-            nio.store16(e, e < d, nw);  // dropped when norm_out is NULL
+            nio.store16(e, col_live<TEAM, VEC>(e, d), nw);  // dropped when norm_out is NULL
             if (a.bf16_source) unpack_bf16x8(nw, y);
         }
         float amax = 0.0f;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8_group(RmsGroupArgs a)
         float v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = y[k] * inv;
-        qio.store8(e, e < d, fp8x8<F>(v));
+        qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8<F>(v));
         sc[j] = s;
     }
     // Every lane of a DPP row holds its group's scale for each chunk, so lane

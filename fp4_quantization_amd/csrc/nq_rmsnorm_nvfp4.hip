@@ -96,22 +96,22 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
         if (a.norm_out || a.bf16_source) {
             const uint4 nw = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
                                         pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
-            nio.store16(e, e < d, nw);  // dropped when norm_out is NULL
+            nio.store16(e, col_live<TEAM, VEC>(e, d), nw);  // dropped when norm_out is NULL
             if (a.bf16_source) unpack_bf16x8(nw, y);
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(y[k]));
         // Block of 16 = this chunk and the partner lane's (same load
         // instruction, lanes t and t^1: one DPP exchange inside a quad).
-        amax = fmaxf(amax, dpp_f32<kDppXor1>(amax));
+        amax = pair_max(amax);
         const float per = div6_rn(amax);  // RN(amax / 6)
         const uint32_t sf = e4m3x4(per * G, 0.0f, 0.0f, 0.0f) & 0x7Fu;  // amax >= 0: codes 0 .. 0x7E
         const float mult = lds_mult[sf];
         float v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = y[k] * mult;
-        qio.store4(e / 2, e < d, e2m1x8(v));
-        sfio.store1(e / 16, e < d && (t1 & 1) == 0, sf);
+        qio.store4(e / 2, col_live<TEAM, VEC>(e, d), e2m1x8(v));
+        sfio.store1(e / 16, col_live<TEAM, VEC>(e, d) && (t1 & 1) == 0, sf);
     }
 }
 

@@ -54,12 +54,11 @@ __device__ __forceinline__ int64_t logical_block()
 // Rows owned by this lane and its wavefront.  The wavefront-uniform parts
 // come from blockIdx and a readfirstlane'd wave index, so they sit in scalar
 // registers and the per-wavefront buffer resources need no waterfall.
-template <int TEAM, int BLOCK = default_block<TEAM>(), bool XCD = false>
-__device__ __forceinline__ RowMap row_map(int64_t M)
+template <int TEAM, int BLOCK = default_block<TEAM>()>
+__device__ __forceinline__ RowMap row_map_at(int64_t M, int64_t blk)
 {
     using S = TeamShape<TEAM, BLOCK>;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-    const int64_t blk = logical_block<XCD>();
     RowMap m;
     m.row = blk * S::kRows + threadIdx.x / TEAM;
     m.ok = m.row < M;
@@ -75,6 +74,25 @@ __device__ __forceinline__ RowMap row_map(int64_t M)
         m.rel = (int)(m.row - m.row0);
     }
     return m;
+}
+
+template <int TEAM, int BLOCK = default_block<TEAM>(), bool XCD = false>
+__device__ __forceinline__ RowMap row_map(int64_t M)
+{
+    return row_map_at<TEAM, BLOCK>(M, logical_block<XCD>());
+}
+
+// Whether an access at element e of a d-element row needs its explicit
+// mask.  A buffer resource that holds exactly one row -- a team of one or
+// more whole wavefronts owns one row per wavefront -- drops every access
+// past the row's end by itself (chunks are whole 16-byte pieces and d % 8 ==
+// 0 on this path, so a chunk is entirely inside or entirely past the end).
+// A resource shared by the rows of several narrower teams, and the
+// element-wise path, need the mask.
+template <int TEAM, bool VEC>
+__device__ __forceinline__ bool col_live(int e, int d)
+{
+    return (VEC && TEAM >= kWave) || e < d;
 }
 
 // A one-row view for vectors shared by every row (gamma, beta).
@@ -132,6 +150,8 @@ class SharedVectors {
 
     // The vectors are fp32 or (BF16) bf16; both are read through a
     // 2-byte-element view, so element e of an fp32 vector starts at 2e.
+    // On the 128-bit path each vector's resource holds exactly the vector,
+    // so reads past its end return zeros with no mask.
     __device__ __forceinline__ SharedVectors(const void* const (&p)[NV], int d) : d_(d)
     {
 #pragma unroll
@@ -151,10 +171,10 @@ class SharedVectors {
                 for (int j = 0; j < CPL; ++j) {
                     const int e = (j * TEAM + t) * 8;
                     if constexpr (BF16) {
-                        pre_[v][j][0] = io_[v].load16(e, e < d_);
+                        pre_[v][j][0] = io_[v].load16(e, VEC || e < d_);
                     } else {
-                        pre_[v][j][0] = io_[v].load16(2 * e, e < d_);
-                        pre_[v][j][1] = io_[v].load16(2 * e + 8, e < d_);
+                        pre_[v][j][0] = io_[v].load16(2 * e, VEC || e < d_);
+                        pre_[v][j][1] = io_[v].load16(2 * e + 8, VEC || e < d_);
                     }
                 }
         }
@@ -165,10 +185,10 @@ class SharedVectors {
                 for (int u = 0; u < kPer; ++u) {
                     const int i = u * S::kBlock + (int)threadIdx.x;
                     if constexpr (BF16) {
-                        const uint2 h = io_[v].load8(i * 4, i * 4 < d_);
+                        const uint2 h = io_[v].load8(i * 4, VEC || i * 4 < d_);
                         held_[v][u] = make_uint4(h.x, h.y, 0u, 0u);
                     } else {
-                        held_[v][u] = io_[v].load16(i * 8, i * 4 < d_);
+                        held_[v][u] = io_[v].load16(i * 8, VEC || i * 4 < d_);
                     }
                 }
         }
@@ -210,9 +230,9 @@ class SharedVectors {
             g[4] = __uint_as_float(b.x); g[5] = __uint_as_float(b.y);
             g[6] = __uint_as_float(b.z); g[7] = __uint_as_float(b.w);
         } else if constexpr (BF16) {
-            unpack_bf16x8(io_[v].load16(e, e < d_), g);
+            unpack_bf16x8(io_[v].load16(e, VEC || e < d_), g);
         } else {
-            const uint4 a = io_[v].load16(2 * e, e < d_), b = io_[v].load16(2 * e + 8, e < d_);
+            const uint4 a = io_[v].load16(2 * e, VEC || e < d_), b = io_[v].load16(2 * e + 8, VEC || e < d_);
             g[0] = __uint_as_float(a.x); g[1] = __uint_as_float(a.y);
             g[2] = __uint_as_float(a.z); g[3] = __uint_as_float(a.w);
             g[4] = __uint_as_float(b.x); g[5] = __uint_as_float(b.y);

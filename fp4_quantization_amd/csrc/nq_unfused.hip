@@ -66,7 +66,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_bf16(RmsBf16Args a)
             const float n = z[k] * rstd;
             y[k] = n * g[k];
         }
-        oio.store16(e, e < d, make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+        oio.store16(e, col_live<TEAM, VEC>(e, d), make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
                                          pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])));
     }
 }
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(default_block<TEAM>()) void k_quant_fp8_rows(QuantR
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t) * 8;
-        xw[j] = xio.load16(e, e < d);  // zeros past the row end
+        xw[j] = xio.load16(e, col_live<TEAM, VEC>(e, d));  // zeros past the row end
     }
 
     if (is_static) {
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(default_block<TEAM>()) void k_quant_fp8_rows(QuantR
             unpack_bf16x8(xw[j], v);
 #pragma unroll
             for (int k = 0; k < 8; ++k) v[k] = v[k] * inv;
-            qio.store8(e, e < d, fp8x8<F>(v));
+            qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8<F>(v));
         }
     } else {
         float amax = 0.0f;
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(default_block<TEAM>()) void k_quant_fp8_rows(QuantR
             unpack_bf16x8(xw[j], v);
 #pragma unroll
             for (int k = 0; k < 8; ++k) v[k] = div_by(v[k], s, inv);
-            qio.store8(e, e < d, fp8x8<F>(v));
+            qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8<F>(v));
         }
     }
 }

@@ -73,6 +73,8 @@ NQ_CODEC_E4M3 = 0
 NQ_CODEC_E2M1 = 1
 NQ_CODEC_BF16 = 2
 NQ_CODEC_E5M2 = 3
+NQ_CODEC_E4M3_BOUNDED = 4
+NQ_CODEC_E5M2_BOUNDED = 5
 NQ_ARITH_RCP = 0
 NQ_ARITH_RSQRT = 1
 NQ_ARITH_DIV = 2

@@ -377,6 +377,10 @@ const char* nq_version(void);
  *   NQ_CODEC_E2M1: out[i] = E2M1 code of in[i]   (clamp to +-6, nearest-even)
  *   NQ_CODEC_BF16: out16[i] = bf16 bits of in[i] (nearest-even)
  *   NQ_CODEC_E5M2: out[i] = e5m2 code of in[i]   (clamp to +-57344, nearest-even)
+ *   NQ_CODEC_E4M3_BOUNDED, NQ_CODEC_E5M2_BOUNDED: the conversion without the
+ *     clamp, which the dynamic-scale kernels use for quotients by a normal
+ *     scale (|in[i]| at most 448 resp. 57344 times 1 + 2^-21); defined, and
+ *     equal to the clamped code, only for inputs within that bound
  * `out` is uint8_t for the 8-bit formats and uint16_t for bf16.
  *
  * nq_diag_arith: applies, element by element on the device, the arithmetic
@@ -407,6 +411,8 @@ const char* nq_version(void);
 #define NQ_CODEC_E2M1 1
 #define NQ_CODEC_BF16 2
 #define NQ_CODEC_E5M2 3
+#define NQ_CODEC_E4M3_BOUNDED 4
+#define NQ_CODEC_E5M2_BOUNDED 5
 nq_status nq_diag_codec(int32_t kind, const float* in, void* out, int64_t n, void* stream);
 #define NQ_ARITH_RCP 0
 #define NQ_ARITH_RSQRT 1

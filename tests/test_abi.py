@@ -315,7 +315,8 @@ def test_binding_constants_match_the_header():
     import fp4_quantization_amd.nq as nq
     text = open(HEADER).read()
     defs = {k: int(v) for k, v in re.findall(r"^#define (NQ_[A-Z0-9_]+) \(?(-?\d+)u?\)?", text, re.M)}
-    needed = [k for k in defs if k.startswith(("NQ_SCALE_", "NQ_FLAG_", "NQ_CODEC_")) or k == "NQ_MAX_D"]
+    needed = [k for k in defs if k.startswith(("NQ_SCALE_", "NQ_FLAG_", "NQ_CODEC_", "NQ_ARITH_"))
+              or k == "NQ_MAX_D"]
     assert len(needed) >= 9
     for k in needed:
         assert getattr(nq, k) == defs[k], k

@@ -29,6 +29,8 @@ import numpy as np
 import pytest
 import torch
 
+from tests.parity import assert_codes
+
 pytestmark = pytest.mark.gpu
 
 N_SIG = 1 << 23
@@ -106,15 +108,15 @@ def test_rsqrt_rn_every_binary32(nq):
     assert inf.item() == 0.0
 
 
-def test_div_by_matches_division(nq):
+def test_div_by_matches_division(nq, orc):
     """y / s for s = RN(amax / fmax) over normal scales and |y| up to about
     fmax * s (both FP8 formats), signs mixed, plus edges.  Markstein's
     correction needs its remainder y - s * q0 to be exact: it is a multiple of
     2^(e_y - 46) below 2^(e_y - 22), so exact for |y| >= 2^-103.  There, with a
     quotient of at least 2^-126, the result must be the correctly rounded
-    quotient.  Below, it must be within one ulp of it (the kernels only meet
-    such y where the quotient's FP8 code is 0 either way unless the row's
-    maximum is under 2^-84)."""
+    quotient.  Elsewhere its e4m3 and e5m2 codes must meet the parity bound
+    against those of the correctly rounded quotient (the kernels quantize it
+    next)."""
     rng = np.random.default_rng(5)
     n = 1 << 24
     checked = exact_checked = 0
@@ -144,9 +146,12 @@ def test_div_by_matches_division(nq):
         differ = got.view(np.uint32) != want.view(np.uint32)
         mism = np.nonzero(ok_range & differ)[0]
         assert mism.size == 0, (part, mism.size, y[mism[:3]], s[mism[:3]], got[mism[:3]], want[mism[:3]])
-        # outside that range: at most one ulp (adjacent bit patterns, same sign)
-        steps = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
-        assert np.all(steps[~ok_range] <= 1)
+        # outside that range the quotient is not always the correctly
+        # rounded one; its FP8 codes (what the kernels make of it) must meet
+        # the parity bound against those of the correctly rounded quotient
+        out = ~ok_range
+        for fmt, enc in (("e4m3", orc.e4m3_encode), ("e5m2", orc.e5m2_encode)):
+            assert_codes(enc(got[out]), enc(want[out]), f"div_by codes outside the exact range ({fmt})", fmt=fmt)
         checked += y.size
         exact_checked += int(ok_range.sum())
     # edges: power-of-two scales, quotients exactly 448 / 57344, y = 0

@@ -109,3 +109,30 @@ def test_bf16_device_codec_exhaustive(nq, orc, exp_field):
     for sign in (0, 1):
         v = _binade(exp_field, sign)
         assert np.array_equal(_run(nq, nq.NQ_CODEC_BF16, v), orc.bf16_encode(v))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_bounded_fp8_device_codec_exhaustive(nq, orc, fmt):
+    """The clamp-free conversion the dynamic-scale kernels use when every
+    scale of the wavefront is normal: every binary32 of magnitude up to
+    fmax * (1 + 2^-21) that reaches the format (from half its smallest
+    subnormal), both signs, equals the clamped oracle code; this includes
+    the few values just above fmax that a quotient by a normal dynamic
+    scale can reach."""
+    kind = nq.NQ_CODEC_E4M3_BOUNDED if fmt == "e4m3" else nq.NQ_CODEC_E5M2_BOUNDED
+    enc = orc.e4m3_encode if fmt == "e4m3" else orc.e5m2_encode
+    fmax = 448.0 if fmt == "e4m3" else 57344.0
+    lo_field = 116 if fmt == "e4m3" else 109           # 2^-11 / 2^-18
+    top_field = 127 + int(np.log2(fmax))               # binade holding fmax
+    bound = np.float32(fmax * (1.0 + 2.0 ** -21))
+    for e in range(lo_field, top_field + 1):
+        for sign in (0, 1):
+            v = _binade(e, sign)
+            if e == top_field:
+                v = v[np.abs(v) <= bound]
+            got = _run(nq, kind, v)
+            want = enc(v)
+            bad = np.nonzero(got != want)[0]
+            assert bad.size == 0, (fmt, e, sign, bad.size, v[bad[:4]], got[bad[:4]], want[bad[:4]])
+    tiny = np.array([0.0, -0.0, 1e-40, -1e-40, 2.0 ** -30, -(2.0 ** -30)], np.float32)
+    assert np.array_equal(_run(nq, kind, tiny), enc(tiny))
