@@ -104,6 +104,7 @@ class RmsFp8Case(Case):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.rms_2816(M, seed) if d == 2816 else W.rms_small(seed, M)
         rd, wr = traffic.fused_add_rmsnorm_fp8(M, d, residual=True, static=static)
+        self.rw = (rd, wr)
         self.bytes = rd + wr
         self.elements = M * d
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
@@ -130,7 +131,8 @@ class GroupCase(Case):
     def __init__(self, torch, nq, M, K=4096, ue8m0=False):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.group_t3(M, K)
-        self.bytes = traffic.total(traffic.group_fp8(M, K))
+        self.rw = traffic.group_fp8(M, K)
+        self.bytes = traffic.total(self.rw)
         self.elements = M * K
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         self.fn = nq.library().nq_per_token_group_quant_fp8
@@ -148,7 +150,8 @@ class LayerNormCase(Case):
     def __init__(self, torch, nq, M=16384, d=4096, dynamic=False, e5m2=False):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.layernorm_rows(M, d)
-        self.bytes = traffic.total(traffic.layernorm_fp8(M, d, dynamic=dynamic))
+        self.rw = traffic.layernorm_fp8(M, d, dynamic=dynamic)
+        self.bytes = traffic.total(self.rw)
         self.elements = M * d
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         self.g = torch.from_numpy(w["gamma"]).cuda()
@@ -179,7 +182,8 @@ class Nvfp4Case(Case):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.nvfp4_slice(M) if sliced else W.nvfp4_7168(M)
         d, ld = w["d"], w["ld"]
-        self.bytes = traffic.total(traffic.rmsnorm_nvfp4(M, d, residual=not sliced))
+        self.rw = traffic.rmsnorm_nvfp4(M, d, residual=not sliced)
+        self.bytes = traffic.total(self.rw)
         self.elements = M * d
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         r = None if sliced else torch.from_numpy(w["residual"]).view(torch.bfloat16).cuda()
@@ -206,7 +210,8 @@ class RmsGroupCase(Case):
     def __init__(self, torch, nq, M, d=7168, ue8m0=False):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.rms_group_7168(M) if d == 7168 else W.rms_2816(M)
-        self.bytes = traffic.total(traffic.fused_add_rmsnorm_fp8_group(M, d))
+        self.rw = traffic.fused_add_rmsnorm_fp8_group(M, d)
+        self.bytes = traffic.total(self.rw)
         self.elements = M * d
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
         r = torch.from_numpy(w["residual"]).view(torch.bfloat16).cuda()
@@ -236,6 +241,8 @@ class UnfusedCase(Case):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.rms_2816(M)
         self.bytes = M * traffic.unfused_add_rmsnorm_fp8_per_row(d) + 4 * d
+        self.rw = (M * 6 * d + 4 * d, M * (5 * d + 4))  # norm: x, r in; residual, bf16 out; quant: bf16 in; codes, scale out
+        assert traffic.total(self.rw) == self.bytes
         self.elements = M * d
         self.fused_bytes = traffic.total(traffic.fused_add_rmsnorm_fp8(M, d))
         x = torch.from_numpy(w["x"]).view(torch.bfloat16).cuda()
@@ -274,6 +281,7 @@ class CopyCase(Case):
             dst = torch.empty(n, dtype=torch.uint8, device="cuda")
             self.bufs.append((src, dst))
             self.args.append((src.data_ptr(), dst.data_ptr(), n))
+        self.rw = (n, n)
         self.bytes = 2 * n
         self.label = f"128-bit copy, {n} bytes read + {n} written"
 
@@ -563,6 +571,38 @@ def summarize_trace(stats_csv, out_md, command):
 
 
 SUITE_TRACE_SUMMARY = os.path.join(ROOT, "profiles", "suite_kernel_trace.md")
+M1_SUMMARY = os.path.join(ROOT, "profiles", "m1_kernel_durations.md")
+M1_WORKLOADS = ["rms_2816_m1", "rms_2816_m16", "rms_small", "group_m1", "rms_group_7168_m1",
+                "layernorm_dynamic_m1", "nvfp4_7168_m1", "nvfp4_7168_m64", "nvfp4_slice_m1", "nvfp4_slice_m64"]
+
+
+def summarize_m1(stats_csv, out_md):
+    """Kernel durations of the single-row and few-row workloads, each called
+    eagerly (one launch per host call, so the host's enqueue gap separates
+    the dispatches and a recorded duration is the kernel's own)."""
+    command = (f"rocprofv3 --kernel-trace --stats -d {_profile_dir(stats_csv)} -o m1 --output-format csv -- "
+               f"python3 bench.py --profile-workload {','.join(M1_WORKLOADS)}")
+    trace = os.path.join(os.path.dirname(stats_csv),
+                         os.path.basename(stats_csv).replace("kernel_stats", "kernel_trace"))
+    groups = {}
+    for r in _csv(trace):
+        if "nq::" not in r["Kernel_Name"] or r["Kernel_Name"].startswith(COPY_KERNEL_PREFIX):
+            continue
+        grid = int(r.get("Grid_Size") or r["Grid_Size_X"])
+        groups.setdefault((r["Kernel_Name"], grid), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# rocprofv3 kernel durations: single-row and few-row calls", "",
+             f"Command (repository root): `{command}`", "",
+             "Workloads, in order: " + ", ".join(M1_WORKLOADS) + ".  Each is called 23 times, eagerly; "
+             "the first 3 calls (cold instruction cache, first touch of the buffers) are left out of the "
+             "median.  The graph-amortized per-call time of the same workloads (bench.py `configs`, "
+             "`m1_us_per_call`) adds the dispatch of each launch.", "",
+             "| kernel | grid (lanes) | calls | median us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (name, grid), d in groups.items():  # dispatch order
+        warm = d[3:] if len(d) > 3 else d
+        med = sorted(warm)[len(warm) // 2]
+        lines.append(f"| `{_short_name(name)}` | {grid} | {len(d)} | {med:.2f} | {min(d):.2f} | {max(d):.2f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
 
 
 def _profile_dir(csv_path):
@@ -581,20 +621,46 @@ def _short_name(name, width=160):
 def summarize_suite(stats_csv, out_md):
     """Text summary of a rocprofv3 --kernel-trace --stats run of the suite:
     every kernel instance (template arguments name the row shape, team x
-    chunks, staging, output format), its calls and average duration."""
-    rows = sorted(_csv(stats_csv), key=lambda r: -float(r["TotalDurationNs"]))
+    chunks, staging, output format) split by launch size (the grid tells a
+    single-row call from a full workload even where both use one kernel
+    instance), with its calls and durations from the per-dispatch trace
+    written next to the statistics; then the single-block (one-row and
+    few-row) calls alone."""
     command = (f"rocprofv3 --kernel-trace --stats -d {_profile_dir(stats_csv)} -o suite --output-format csv -- "
-               "python3 bench.py --suite --no-cpu-baseline")
+               "python3 bench.py --suite --no-cpu-baseline --no-configs")
+    trace = os.path.join(os.path.dirname(stats_csv),
+                         os.path.basename(stats_csv).replace("kernel_stats", "kernel_trace"))
+    groups = {}
+    for r in _csv(trace):
+        grid = int(r.get("Grid_Size") or r["Grid_Size_X"])
+        wg = int(r.get("Workgroup_Size") or r["Workgroup_Size_X"])
+        key = (r["Kernel_Name"], grid, wg)
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
     lines = ["# rocprofv3 kernel trace: every workload of `bench.py --suite`", "",
              f"Command (repository root): `{command}`", "",
              "Kernel template arguments: team lanes, chunks per lane, 128-bit path, staged shared "
              "vectors, then (where present) output format (0 e4m3, 1 e5m2), dynamic scale, bf16 gamma, "
-             "and lanes per block.  The suite's own per-call figures (graph-replayed, events) are in "
-             "its stderr lines; these durations come from the profiler, with its overhead.", "",
-             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
-    for r in rows:
-        lines.append(f"| `{_short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+             "and lanes per block.  Durations are per dispatch from the profiler's trace (start to end of "
+             "the kernel), averaged over every dispatch of that kernel instance at that launch size, warm-up "
+             "replays included; the suite's own per-call figures (graph-replayed, events) are in its "
+             "stderr lines.", "",
+             "| kernel | grid (lanes) | block | calls | average us | min us | max us |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, grid, wg), d in rows:
+        lines.append(f"| `{_short_name(name)}` | {grid} | {wg} | {len(d)} | {sum(d) / len(d):.2f} | "
+                     f"{min(d):.2f} | {max(d):.2f} |")
+    small = [(k, d) for k, d in rows if "nq::" in k[0] and k[1] <= k[2] and not k[0].startswith(COPY_KERNEL_PREFIX)]
+    lines += ["", "## Single-block calls (M = 1 and the few-row workloads)", "",
+              "Per-dispatch durations from the trace.  Inside a replayed graph the calls run back to back and "
+              "a dispatch's recorded start can include the wait behind its predecessor, so the average runs "
+              "close to the graph-amortized per-call time; the median and the minimum are nearer the "
+              "kernel's own duration.",
+              "", "| kernel | grid (lanes) | calls | median us | average us | min us |", "|---|---|---|---|---|---|"]
+    for (name, grid, wg), d in sorted(small, key=lambda kv: kv[0][0]):
+        med = sorted(d)[len(d) // 2]
+        lines.append(f"| `{_short_name(name)}` | {grid} | {len(d)} | {med:.2f} | {sum(d) / len(d):.2f} | "
+                     f"{min(d):.2f} |")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -610,7 +676,8 @@ def summarize_counters(fetch_csv, write_csv, out_md, commands):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            key = "main" if name.startswith(MAIN_KERNEL_PREFIX) else "copy" if name.startswith(COPY_KERNEL_PREFIX) else None
+            key = ("main" if name.startswith(MAIN_KERNEL_PREFIX) and "128, 3" in name
+                   else "copy" if name.startswith(COPY_KERNEL_PREFIX) else None)
             if key:
                 vals.setdefault(key, []).append(float(r["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in vals.items()}
@@ -636,6 +703,92 @@ def summarize_counters(fetch_csv, write_csv, out_md, commands):
              "", "(bench.py reports `roofline.traffic` from these two lines while the kernel sources "
              "still hash to the value above.)"]
     open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+HBM_SUMMARY = os.path.join(ROOT, "profiles", "hbm_counters_all_workloads.md")
+# the full-size workloads whose HBM traffic is measured
+HBM_WORKLOADS = ["rms_2816_m8192", "rms_2816_m8192_static", "rms_2816_m8192_e5m2", "group_m32768_fp32",
+                 "group_m32768_ue8m0", "rms_group_7168_m8192", "rms_group_7168_m8192_ue8m0",
+                 "rms_group_2816_m8192", "layernorm_m16384", "layernorm_m16384_e5m2",
+                 "layernorm_dynamic_m16384", "nvfp4_7168_m8192", "nvfp4_slice_m8192", "unfused_2816_m8192"]
+
+
+def _counter_per_dispatch(path, counter):
+    """Average counter value per call of the profiled workload (its nq
+    kernels summed per call, the two of the unfused pair included) and of
+    the calibration copy, from a rocprofv3 --pmc CSV of
+    `bench.py --profile-workload W`."""
+    per = {}
+    for r in _csv(path):
+        if r["Counter_Name"] != counter or "nq::" not in r["Kernel_Name"]:
+            continue
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    copy = [v for k, v in per.items() if k.startswith(COPY_KERNEL_PREFIX)]
+    work = {k: v for k, v in per.items() if not k.startswith(COPY_KERNEL_PREFIX)}
+    if not copy or not work:
+        raise ValueError(f"{path}: no calibration copy or no workload kernel")
+    return (sum(copy[0]) / len(copy[0]), {k: sum(v) / len(v) for k, v in work.items()})
+
+
+def summarize_hbm(top):
+    """profiles/hbm_counters_all_workloads.md from the FETCH_SIZE and
+    WRITE_SIZE passes of every workload in HBM_WORKLOADS (directories
+    <top>/<workload>_fetch and <top>/<workload>_write), each scaled by the
+    calibration copy of its own run; and the headline kernel's summary
+    (COUNTER_SUMMARY) that roofline.traffic reads."""
+    kib = PROFILE_COPY_BYTES / 1024
+    rel = os.path.relpath(os.path.abspath(top), ROOT)
+    lines = ["# rocprofv3 HBM counters: every full-size workload", "",
+             "Commands (repository root), two passes per workload W:", "",
+             f"- `rocprofv3 --pmc FETCH_SIZE -d {rel}/W_fetch -o c --output-format csv -- "
+             "python3 bench.py --profile-workload W`",
+             f"- `rocprofv3 --pmc WRITE_SIZE -d {rel}/W_write -o c --output-format csv -- "
+             "python3 bench.py --profile-workload W`", "",
+             "Each run first copies exactly 64 MiB ten times with the 128-bit copy kernel; a counter is "
+             "scaled by what it reads for that copy in the same run (FETCH_SIZE counts about half the "
+             "bytes read on gfx950, WRITE_SIZE all bytes written).  Per call of the workload (its 23 "
+             "calls averaged; the unfused pair's two kernels summed).", "",
+             "| workload | kernel | read: scaled bytes | algorithmic | ratio | written: scaled bytes | "
+             "algorithmic | ratio | FETCH scale | WRITE scale |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    headline = None
+    for w in HBM_WORKLOADS:
+        fetch = _find_csv(os.path.join(top, f"{w}_fetch"))
+        write = _find_csv(os.path.join(top, f"{w}_write"))
+        if not fetch or not write:
+            lines.append(f"| {w} | (not profiled) | | | | | | | | |")
+            continue
+        fc, fk = _counter_per_dispatch(fetch, "FETCH_SIZE")
+        wc, wk = _counter_per_dispatch(write, "WRITE_SIZE")
+        fs, ws = kib / fc, kib / wc
+        rd, wr = sum(fk.values()) * fs * 1024, sum(wk.values()) * ws * 1024
+        ard, awr = workload_rw(w)
+        names = " + ".join(f"`{_short_name(k, 60)}`" for k in sorted(fk))
+        lines.append(f"| {w} | {names} | {rd:.0f} | {ard} | {rd / ard:.4f} | {wr:.0f} | {awr} | {wr / awr:.4f} | "
+                     f"{fs:.4f} | {ws:.4f} |")
+        if w == "rms_2816_m8192":
+            headline = (fetch, write)
+    lines += ["", "A ratio near 1 means the kernel moves its algorithmic bytes and nothing else (no "
+              "re-reads of inputs, no partial-line writes); the shared vectors (gamma, beta) are counted "
+              "once per call in the algorithmic bytes and are mostly served from the caches."]
+    open(HBM_SUMMARY, "w").write("\n".join(lines) + "\n")
+    if headline:
+        summarize_counters(headline[0], headline[1], COUNTER_SUMMARY,
+                           [f"rocprofv3 --pmc FETCH_SIZE -d {rel}/rms_2816_m8192_fetch -o c --output-format csv "
+                            "-- python3 bench.py --profile-workload rms_2816_m8192",
+                            f"rocprofv3 --pmc WRITE_SIZE -d {rel}/rms_2816_m8192_write -o c --output-format csv "
+                            "-- python3 bench.py --profile-workload rms_2816_m8192"])
+
+
+def _find_csv(d):
+    """The counter-collection CSV rocprofv3 wrote under directory d."""
+    if not os.path.isdir(d):
+        return None
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                return os.path.join(root, f)
+    return None
 
 
 VALU_SUMMARY = os.path.join(ROOT, "profiles", "valu_counters.md")
@@ -674,7 +827,7 @@ def summarize_valu(suite_log, csvs, out_md):
         vals = {}
         for r in _csv(path):
             name = r["Kernel_Name"]
-            if "nq::" not in name:
+            if "nq::" not in name or name.startswith(COPY_KERNEL_PREFIX):
                 continue
             vals.setdefault((name, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
         for k in sorted({k for k, _ in vals}):
@@ -729,6 +882,67 @@ def suite_cases(torch, nq):
     return cases
 
 
+def workload_rw(name):
+    """(bytes read, bytes written) of one call of a suite workload, from the
+    byte model alone (no GPU needed)."""
+    from fp4_quantization_amd import traffic
+    m = re.match(r"rms_2816_m(\d+)(_static)?", name)
+    if m:
+        return traffic.fused_add_rmsnorm_fp8(int(m.group(1)), 2816, static=bool(m.group(2)))
+    if name == "rms_small":
+        return traffic.fused_add_rmsnorm_fp8(64, 256)
+    m = re.match(r"group_m(\d+)", name)
+    if m:
+        return traffic.group_fp8(int(m.group(1)), 4096)
+    m = re.match(r"rms_group_(\d+)_m(\d+)", name)
+    if m:
+        return traffic.fused_add_rmsnorm_fp8_group(int(m.group(2)), int(m.group(1)))
+    m = re.match(r"layernorm(_dynamic)?_m(\d+)", name)
+    if m:
+        return traffic.layernorm_fp8(int(m.group(2)), 4096, dynamic=bool(m.group(1)))
+    m = re.match(r"nvfp4_(7168|slice)_m(\d+)", name)
+    if m:
+        sliced = m.group(1) == "slice"
+        return traffic.rmsnorm_nvfp4(int(m.group(2)), 1536 if sliced else 7168, residual=not sliced)
+    m = re.match(r"unfused_2816_m(\d+)", name)
+    if m:
+        M, d = int(m.group(1)), 2816
+        return (M * 6 * d + 4 * d, M * (5 * d + 4))
+    raise KeyError(name)
+
+
+# The five workload configurations the metric is quoted with, and the suite
+# workloads that time each of them (M = 1 calls included).
+CONFIG_WORKLOADS = {
+    "1": ["rms_small"],
+    "2": ["rms_2816_m8192", "rms_2816_m256", "rms_2816_m16", "rms_2816_m1"],
+    "3": ["group_m32768_fp32", "group_m32768_ue8m0", "group_m1"],
+    "4": ["layernorm_m16384"],
+    "5": ["nvfp4_7168_m8192", "nvfp4_7168_m64", "nvfp4_7168_m1", "nvfp4_slice_m8192", "nvfp4_slice_m64",
+          "nvfp4_slice_m1"],
+}
+
+
+def time_configs(torch, nq):
+    """Every configuration's workloads timed together, round-robin (one
+    20-call graph per workload replayed once per round, median of 100
+    rounds): per workload the per-call time, GB/s of algorithmic bytes and %
+    of the 8 TB/s peak."""
+    factories = dict(suite_cases(torch, nq))
+    names = [(cfg, w) for cfg, ws in CONFIG_WORKLOADS.items() for w in ws]
+    cases = [factories[w]() for _, w in names]
+    ms = time_graphs_interleaved(torch, cases)
+    out = {}
+    for (cfg, w), case, t in zip(names, cases, ms):
+        us = t * 1e3
+        gbps = case.bytes / (us * 1e-6) / 1e9
+        out[w] = {"config": int(cfg), "us_per_call": round(us, 3), "GBps": round(gbps, 1),
+                  "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 1), "bytes_per_call": case.bytes}
+    del cases
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_suite(torch, nq, only=None):
     cases = suite_cases(torch, nq)
     if only:
@@ -748,6 +962,7 @@ def run_suite(torch, nq, only=None):
                       "GBps_graph": round(case.bytes / (us_graph * 1e-6) / 1e9, 1),
                       "pct_hbm_peak_graph": round(100 * case.bytes / (us_graph * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)})
         built.append(case)
+        log(f"suite: {name} timed alone")
     # all workloads together, round-robin (every case keeps its buffer sets resident)
     inter = time_graphs_interleaved(torch, built)
     for line, case, ms in zip(lines, built, inter):
@@ -768,10 +983,13 @@ def main():
     ap.add_argument("--suite-cases", metavar="A,B,...",
                     help="time only these suite workloads (comma-separated names), then exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="leave out the per-configuration timings (the `configs` object)")
     ap.add_argument("--profile-mode", action="store_true",
                     help="short fixed run for rocprofv3: copy reference + main kernel steps")
-    ap.add_argument("--profile-workload", metavar="NAME",
-                    help="short fixed run of one suite workload (3 + 20 calls) for rocprofv3 --pmc")
+    ap.add_argument("--profile-workload", metavar="NAME[,NAME...]",
+                    help="short fixed run for rocprofv3: ten 64 MiB copies (counter calibration), then "
+                         "each named suite workload in turn (3 + 20 calls)")
     ap.add_argument("--summarize-valu", nargs="+", metavar=("SUITE_LOG", "COUNTER_CSV"),
                     help="write profiles/valu_counters.md from a suite log and rocprofv3 --pmc CSVs "
                          "(one per workload, in directories named valu_<workload>)")
@@ -779,7 +997,21 @@ def main():
                     help="write profiles/suite_kernel_trace.md from a rocprofv3 --stats CSV of the suite")
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
                     help="write the profiles/ summaries from rocprofv3 output and exit")
+    ap.add_argument("--summarize-m1", metavar="STATS_CSV",
+                    help="write profiles/m1_kernel_durations.md from a rocprofv3 --kernel-trace --stats run of "
+                         "--profile-workload over the single-row and few-row workloads")
+    ap.add_argument("--summarize-hbm", metavar="DIR",
+                    help="write profiles/hbm_counters_all_workloads.md (and the headline counter summary) "
+                         "from per-workload FETCH_SIZE / WRITE_SIZE runs under DIR")
     args = ap.parse_args()
+
+    if args.summarize_m1:
+        summarize_m1(args.summarize_m1, M1_SUMMARY)
+        return
+
+    if args.summarize_hbm:
+        summarize_hbm(args.summarize_hbm)
+        return
 
     if args.summarize_suite:
         summarize_suite(args.summarize_suite, SUITE_TRACE_SUMMARY)
@@ -818,12 +1050,22 @@ def main():
         return
 
     if args.profile_workload:
-        case = dict(suite_cases(torch, nq))[args.profile_workload]()
-        h = torch.cuda.current_stream().cuda_stream
-        for i in range(23):
-            case.step(i, h)
+        # the counter calibration first: 10 copies of exactly 64 MiB read + 64 MiB written
+        src = torch.empty(PROFILE_COPY_BYTES, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            nq.nq_diag_copy(src, dst)
         torch.cuda.synchronize()
-        log(f"profile-workload {args.profile_workload} done")
+        del src, dst
+        factories = dict(suite_cases(torch, nq))
+        h = torch.cuda.current_stream().cuda_stream
+        for name in args.profile_workload.split(","):
+            case = factories[name]()
+            for i in range(23):
+                case.step(i, h)
+            torch.cuda.synchronize()
+            del case
+            log(f"profile-workload {name} done")
         return
 
     if args.profile_mode:
@@ -865,6 +1107,8 @@ def main():
     del cp
     torch.cuda.empty_cache()
 
+    configs = None if args.no_configs else time_configs(torch, nq)
+
     if args.suite:
         run_suite(torch, nq)
 
@@ -887,6 +1131,8 @@ def main():
         "copy_reference": {"us_per_call": round(copy_us, 3), "GBps": round(copy_gbps, 1),
                            "value_over_copy": round(value / copy_gbps, 4)},
     }
+    if configs is not None:
+        out["configs"] = configs
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

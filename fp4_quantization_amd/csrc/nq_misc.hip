@@ -86,11 +86,28 @@ __global__ __launch_bounds__(256) void k_diag_arith(int kind, const void* a, con
     }
 }
 
-__global__ __launch_bounds__(256) void k_diag_copy(const uint4* src, uint4* dst, int64_t n16)
+// One pass over the data: each lane moves kCopyUnroll 16-byte pieces, a
+// wavefront's pieces contiguous per step (1 KB per load instruction), every
+// load issued before the first store, both non-temporal (the data is used
+// once).  Measured on MI355X over 161.5 MB: 2 pieces per lane 27.8 us, 4
+// pieces 28.8, 8 pieces 30.0, and a grid-stride loop of one piece 29.3.
+constexpr int kCopyBlock = 256;
+constexpr int kCopyUnroll = 2;
+
+__global__ __launch_bounds__(kCopyBlock) void k_diag_copy(const uint4* src, uint4* dst, int64_t n16)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
-        dst[i] = src[i];
+    const int64_t base = (int64_t)blockIdx.x * kCopyBlock * kCopyUnroll + threadIdx.x;
+    u32x4_t v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const int64_t i = base + (int64_t)u * kCopyBlock;
+        v[u] = i < n16 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src) + i) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const int64_t i = base + (int64_t)u * kCopyBlock;
+        if (i < n16) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4_t*>(dst) + i);
+    }
 }
 
 } // namespace nq
@@ -160,10 +177,10 @@ extern "C" nq_status nq_diag_copy(const void* src, void* dst, int64_t bytes, voi
     const Region rout[] = {region(dst, 1, bytes, bytes, 1)};
     if (any_alias(rin, rout)) return NQ_ERR_ALIAS;
     const int64_t n16 = bytes / 16;
-    // enough blocks to fill every CU several times over; grid-stride beyond
-    int64_t blocks = (n16 + 255) / 256;
-    if (blocks > 256 * 64) blocks = 256 * 64;
-    hipLaunchKernelGGL(k_diag_copy, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+    const int64_t per_block = (int64_t)kCopyBlock * kCopyUnroll;
+    const int64_t blocks = (n16 + per_block - 1) / per_block;
+    if (blocks > 0x7FFFFFFF) return NQ_ERR_SHAPE;
+    hipLaunchKernelGGL(k_diag_copy, dim3((unsigned)blocks), dim3(kCopyBlock), 0, (hipStream_t)stream,
                        (const uint4*)src, (uint4*)dst, n16);
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
 }

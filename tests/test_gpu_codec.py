@@ -136,3 +136,16 @@ def test_bounded_fp8_device_codec_exhaustive(nq, orc, fmt):
             assert bad.size == 0, (fmt, e, sign, bad.size, v[bad[:4]], got[bad[:4]], want[bad[:4]])
     tiny = np.array([0.0, -0.0, 1e-40, -1e-40, 2.0 ** -30, -(2.0 ** -30)], np.float32)
     assert np.array_equal(_run(nq, kind, tiny), enc(tiny))
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, 3 * 4096 * 16 + 48, 33 << 20])
+def test_diag_copy_moves_every_byte(nq, nbytes):
+    """The bandwidth-reference copy: every byte copied, nothing written past
+    the end (ragged last block included)."""
+    g = torch.Generator(device="cuda").manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    dst = torch.full((nbytes + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    nq.nq_diag_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert bool((dst[nbytes:] == 0xA5).all())
