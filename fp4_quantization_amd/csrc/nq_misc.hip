@@ -89,10 +89,11 @@ __global__ __launch_bounds__(256) void k_diag_arith(int kind, const void* a, con
 // One pass over the data: each lane moves kCopyUnroll 16-byte pieces, a
 // wavefront's pieces contiguous per step (1 KB per load instruction), every
 // load issued before the first store, both non-temporal (the data is used
-// once).  Measured on MI355X over 161.5 MB: 2 pieces per lane 27.8 us, 4
-// pieces 28.8, 8 pieces 30.0, and a grid-stride loop of one piece 29.3.
+// once).  Measured on MI355X over 161.5 MB (half read, half written), same
+// box: one piece per lane 27.2 us, two 27.7, four 28.8, eight 30.0; blocks of
+// 128 or 1024 lanes no faster; a grid-stride loop of one piece 29.3.
 constexpr int kCopyBlock = 256;
-constexpr int kCopyUnroll = 2;
+constexpr int kCopyUnroll = 1;
 
 __global__ __launch_bounds__(kCopyBlock) void k_diag_copy(const uint4* src, uint4* dst, int64_t n16)
 {
