@@ -997,6 +997,9 @@ def main():
                     help="write profiles/suite_kernel_trace.md from a rocprofv3 --stats CSV of the suite")
     ap.add_argument("--summarize", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
                     help="write the profiles/ summaries from rocprofv3 output and exit")
+    ap.add_argument("--summarize-trace", metavar="STATS_CSV",
+                    help="write profiles/rmsnorm_fp8_m8192_d2816_kernel_trace.md from a rocprofv3 --kernel-trace "
+                         "--stats run of `bench.py --no-cpu-baseline --no-configs`")
     ap.add_argument("--summarize-m1", metavar="STATS_CSV",
                     help="write profiles/m1_kernel_durations.md from a rocprofv3 --kernel-trace --stats run of "
                          "--profile-workload over the single-row and few-row workloads")
@@ -1004,6 +1007,12 @@ def main():
                     help="write profiles/hbm_counters_all_workloads.md (and the headline counter summary) "
                          "from per-workload FETCH_SIZE / WRITE_SIZE runs under DIR")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, os.path.join(ROOT, "profiles", "rmsnorm_fp8_m8192_d2816_kernel_trace.md"),
+                        f"rocprofv3 --kernel-trace --stats -d {_profile_dir(args.summarize_trace)} -o kt "
+                        "--output-format csv -- python3 bench.py --no-cpu-baseline --no-configs")
+        return
 
     if args.summarize_m1:
         summarize_m1(args.summarize_m1, M1_SUMMARY)

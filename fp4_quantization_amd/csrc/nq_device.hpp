@@ -53,9 +53,16 @@ __device__ __forceinline__ float clamp_e4m3(float v)
     return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max);
 }
 
+// The packed conversions write one half (FP8) or one byte (E2M1) of their
+// destination and keep the rest; every part is written before the word is
+// used, so the first conversion of a word starts from whatever its first
+// operand's register holds (no register to zero first).
+__device__ __forceinline__ int any_bits(float v) { return __builtin_bit_cast(int, v); }
+
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
 {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(a), clamp_e4m3(b), 0, false);
+    const float ca = clamp_e4m3(a);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(ca, clamp_e4m3(b), any_bits(ca), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(c), clamp_e4m3(d), w, true);
     return (uint32_t)w;
 }
@@ -73,7 +80,8 @@ __device__ __forceinline__ float clamp_e5m2(float v)
 
 __device__ __forceinline__ uint32_t e5m2x4(float a, float b, float c, float d)
 {
-    int w = __builtin_amdgcn_cvt_pk_bf8_f32(clamp_e5m2(a), clamp_e5m2(b), 0, false);
+    const float ca = clamp_e5m2(a);
+    int w = __builtin_amdgcn_cvt_pk_bf8_f32(ca, clamp_e5m2(b), any_bits(ca), false);
     w = __builtin_amdgcn_cvt_pk_bf8_f32(clamp_e5m2(c), clamp_e5m2(d), w, true);
     return (uint32_t)w;
 }
@@ -111,10 +119,10 @@ template <Fp8 F>
 __device__ __forceinline__ uint32_t fp8x4_bounded(float a, float b, float c, float d)
 {
     if constexpr (F == Fp8::E5M2) {
-        int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+        int w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, any_bits(a), false);
         return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
     } else {
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, any_bits(a), false);
         return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     }
 }
@@ -159,7 +167,7 @@ __device__ __forceinline__ float e4m3_value(uint32_t c)
 // code of the value clamped to [-6, 6] for every non-NaN input.
 __device__ __forceinline__ uint32_t e2m1x8(const float v[8])
 {
-    uint32_t w = 0;
+    uint32_t w = (uint32_t)any_bits(v[0]);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
@@ -612,10 +620,8 @@ __device__ __forceinline__ void unpack_bf16x8(uint4 w, float v[8])
 // Sum of the squares of one chunk of 8 bf16 values (packed), in binary64.
 // Every square is exact in binary64, so the chunk sum rounds at most in its
 // last bit.
-__device__ __forceinline__ double sumsq_chunk(uint4 w)
+__device__ __forceinline__ double sumsq_chunk_unpacked(const float z[8])
 {
-    float z[8];
-    unpack_bf16x8(w, z);
     double acc = 0.0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -623,6 +629,12 @@ __device__ __forceinline__ double sumsq_chunk(uint4 w)
         acc = fma(zd, zd, acc);
     }
     return acc;
+}
+__device__ __forceinline__ double sumsq_chunk(uint4 w)
+{
+    float z[8];
+    unpack_bf16x8(w, z);
+    return sumsq_chunk_unpacked(z);
 }
 
 

@@ -27,14 +27,16 @@ namespace nq {
 // Returns rstd; zw[j] holds chunk j of z as packed bf16 (it is exactly a
 // bf16 value, so nothing is lost).  Callers launder zw (opaque) before
 // unpacking it again, so the unpacked copy from the sum is not kept alive
-// across the reduction.  `vecs` are the block's shared vectors:
+// across the reduction -- except with KEEP, where the residual-less path
+// also leaves z unpacked in zf (for kernels with registers to spare, which
+// then skip the second unpacking).  `vecs` are the block's shared vectors:
 // their cooperative loads are issued with the row loads and they are
 // published before the reduction's barrier.
-template <int TEAM, int CPL, bool VEC, bool RES, class SV>
+template <int TEAM, int CPL, bool VEC, bool RES, class SV, bool KEEP = false>
 __device__ __forceinline__ float rms_front(const uint16_t* x, int64_t ld_x, const uint16_t* r, int64_t ld_r,
                                            uint16_t* ro, int64_t ld_ro, const RowMap& m, int t, int d,
                                            double inv_d, float eps, SV& vecs, typename SV::Lds& lds_vec,
-                                           double* lds_sum, uint4 (&zw)[CPL])
+                                           double* lds_sum, uint4 (&zw)[CPL], float (*zf)[8] = nullptr)
 {
     const RowIO<VEC, kLoadStream, uint16_t> xio(x, ld_x, m, d);
     double acc = 0.0;
@@ -72,8 +74,16 @@ __device__ __forceinline__ float rms_front(const uint16_t* x, int64_t ld_x, cons
             zw[j] = xio.load16(e, col_live<TEAM, VEC>(e, d));
         }
         vecs.issue(t);
+        if constexpr (KEEP) {
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) acc += sumsq_chunk(zw[j]);
+            for (int j = 0; j < CPL; ++j) {
+                unpack_bf16x8(zw[j], zf[j]);
+                acc += sumsq_chunk_unpacked(zf[j]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) acc += sumsq_chunk(zw[j]);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 

@@ -63,9 +63,14 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
 
     const float sg = a.global_scale[0];  // issued early: read on the device at run time
 
+    // Residual-less rows keep z unpacked from the sum of squares (these
+    // instances have registers to spare); the others unpack it again below.
+    constexpr bool KEEP = !RES;
     uint4 zw[CPL];
-    const float rstd = rms_front<TEAM, CPL, VEC, RES>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d, a.inv_d,
-                                                      a.eps, gamma, lds_gamma, lds_sum, zw);
+    float zf[KEEP ? CPL : 1][8];
+    const float rstd = rms_front<TEAM, CPL, VEC, RES, SV, KEEP>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d,
+                                                               a.inv_d, a.eps, gamma, lds_gamma, lds_sum, zw,
+                                                               KEEP ? zf : nullptr);
     const float G = 1.0f / sg;  // encode scale
     // The element multiplier depends only on the block-scale code: one
     // correctly rounded quotient per code and block instead of one per chunk.
@@ -79,14 +84,21 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
     const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d / 2);
     const RowIO<VEC, kStoreScales, uint8_t> sfio(a.sf, a.ld_sf, m, d / 16);
     const int t1 = opaque(t);
+    if constexpr (!KEEP) {
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) opaque(zw[j]);
+        for (int j = 0; j < CPL; ++j) opaque(zw[j]);
+    }
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t1) * 8;
         float g[8], z[8], y[8];
         gamma.chunk(lds_gamma, 0, j, e, g);
-        unpack_bf16x8(zw[j], z);
+        if constexpr (KEEP) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) z[k] = zf[j][k];
+        } else {
+            unpack_bf16x8(zw[j], z);
+        }
         float amax = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
