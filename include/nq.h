@@ -153,6 +153,11 @@ nq_status nq_fused_add_rmsnorm_quant_fp8_ex(
  *   rstd = 1 / sqrt(sum_i c_i^2 / d + eps)      (population variance)
  *   y_i  = ((c_i * rstd) * gamma_i) + beta_i    (no fused multiply-add)
  *   q_i  = e4m3(y_i * (1 / scale[0]))
+ * The two row sums are taken over 8-element chunks in binary32 and added in
+ * binary64 (a chunk whose binary32 sum leaves a safe range is summed exactly
+ * instead), so mu and the variance are within a few binary32 roundings of
+ * the exactly summed values; rstd can differ from theirs by one unit in the
+ * last place.
  *
  *   x      [M, d] bf16, row stride ld_x
  *   gamma, beta [d] fp32
