@@ -308,23 +308,38 @@ def time_steps(torch, case, steps, warmup):
     return t0.elapsed_time(t1), time.perf_counter() - w0
 
 
+def _hip_runtime():
+    """The HIP runtime library this process already uses (PyTorch's)."""
+    import ctypes
+    with open("/proc/self/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64.so" in line}
+    lib = ctypes.CDLL(sorted(paths)[0] if paths else "libamdhip64.so")
+    lib.hipGraphUpload.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipGraphUpload.restype = ctypes.c_int
+    return lib
+
+
 def time_steps_graph(torch, case, steps, warmup):
-    """Exactly `steps` launches captured in one graph, then `warmup` untimed
-    eager launches, then the graph replayed once, bracketed by
-    synchronizations and by HIP events on the replay stream (the first
-    replay, so its one-time upload is inside the timed region).  Capturing
-    first keeps the GPU busy from the warmup straight into the timed steps:
-    measured on MI355X, after an idle gap the first ~100 launches of this
-    kernel run at ~27 us, the next ~100 at ~31 us, and it settles back near
-    27 us over a few hundred more, so a gap before the timed region (such as
-    a capture) lands the timed steps on that transient.  Returns stream
-    milliseconds."""
+    """Exactly `steps` launches captured in one graph and uploaded to the
+    device (hipGraphUpload: the graph's one-time setup, which a first replay
+    would otherwise do inside the timed region), then `warmup` untimed eager
+    launches, then the graph replayed once, bracketed by synchronizations and
+    by HIP events on the replay stream.  Capturing first keeps the GPU busy
+    from the warmup straight into the timed steps: measured on MI355X, after
+    an idle gap the first ~100 launches of this kernel run at ~27 us, the
+    next ~100 at ~31 us, and it settles back near 27 us over a few hundred
+    more, so a gap before the timed region (such as a capture) lands the
+    timed steps on that transient.  Returns stream milliseconds."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         hh = torch.cuda.current_stream().cuda_stream
         for i in range(steps):
             case.step(warmup + i, hh)
     h = torch.cuda.current_stream().cuda_stream
+    rc = _hip_runtime().hipGraphUpload(g.raw_cuda_graph_exec(), h)
+    if rc != 0:
+        raise RuntimeError(f"hipGraphUpload failed ({rc})")
+    torch.cuda.synchronize()
     for i in range(warmup):
         case.step(i, h)
     t0 = torch.cuda.Event(enable_timing=True)
