@@ -1285,3 +1285,61 @@ def test_rstd_extremes_layernorm_bit_exact(nq, orc):
     assert_bits_equal(q, o["q"], "q")
     assert s[-1] == 0 and np.all(q[-1] == 0)
     assert np.all(s[:-1] > 0)
+
+
+def _ln_hard_rows(d, seed):
+    """Rows that stress LayerNorm's binary32 chunk sums: a large mean against
+    a small spread, magnitudes 2^24 apart inside one chunk, cancelling pairs,
+    rows far below and far above the binary32 range of a square, constant and
+    zero rows, bf16 subnormals mixed with normal values, and plain rows."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    n = rng.standard_normal
+    rows.append(1000.0 + 8.0 * n(d))                          # mean >> spread
+    rows.append(2.0 ** 20 + 2.0 ** 13 * n(d))
+    mixed = 2.0 ** -4 * n(d)
+    mixed[::8] = 2.0 ** 20 * n(len(mixed[::8]))                # 2^24 apart in one chunk
+    rows.append(mixed)
+    pairs = np.empty(d)
+    h = 2.0 ** 30 * (1.0 + rng.random((d + 1) // 2))
+    pairs[0::2] = h[: len(pairs[0::2])]
+    pairs[1::2] = -h[: len(pairs[1::2])] * (1.0 + 2.0 ** -7 * rng.integers(-3, 4, len(pairs[1::2])))
+    rows.append(pairs)                                          # cancelling pairs
+    rows.append(2.0 ** -100 * n(d))                             # squares below binary32
+    rows.append(2.0 ** 100 * n(d))                              # squares above binary32
+    rows.append(np.zeros(d))
+    rows.append(np.full(d, 5.0))
+    spike = np.full(d, -3.0)
+    spike[d // 2] = 1e4
+    rows.append(spike)
+    sub = n(d)
+    sub[1::3] = 2.0 ** -130 * rng.integers(1, 100, len(sub[1::3]))  # bf16 subnormals
+    rows.append(sub)
+    near = np.ones(d)
+    near[rng.choice(d, max(1, d // 64), replace=False)] += 2.0 ** -7
+    rows.append(near)
+    rows.append(0.5 + n(d))
+    return W.to_bf16_bits(np.stack(rows).astype(np.float32))
+
+
+@pytest.mark.parametrize("d", [4096, 111])
+@pytest.mark.parametrize("dynamic", [False, True])
+def test_layernorm_chunk_sums_on_hard_rows(nq, orc, d, dynamic):
+    """LayerNorm's binary32 chunk sums against the oracle's binary64 sums on
+    rows built to break them, many rows per kind (the many-rows schedule) and
+    the element-wise path (d = 111): every output within the tolerance."""
+    note(f"layernorm hard rows d={d} dynamic={dynamic}")
+    x = np.concatenate([_ln_hard_rows(d, seed) for seed in range(8)])
+    M = x.shape[0]
+    rng = np.random.default_rng(99)
+    g = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(d)).astype(np.float32)
+    w = dict(M=M, d=d, x=x, gamma=g, beta=b, eps=1e-5)
+    big = np.concatenate([x] * 128)   # enough rows for the staged many-rows shape
+    wb = dict(w, M=big.shape[0], x=big)
+    for ww in (w, wb):
+        q, s = run_ln_ex(nq, ww, 0, None if dynamic else 0.05)
+        o = orc.layernorm_quant_fp8(ww["x"], g, b, 1e-5, None if dynamic else 0.05)
+        if dynamic:
+            assert_scales(s, o["scale"], "scale (hard rows)")
+        assert_codes(q, o["q"], "q (hard rows)")
