@@ -32,11 +32,25 @@ namespace nq {
 // then skip the second unpacking).  `vecs` are the block's shared vectors:
 // their cooperative loads are issued with the row loads and they are
 // published before the reduction's barrier.
-template <int TEAM, int CPL, bool VEC, bool RES, class SV, bool KEEP = false>
+struct NoBlockWork {
+    __device__ __forceinline__ void operator()() const {}
+};
+
+// Whether rms_front passes a block barrier after it has run `before_barrier`
+// (the staged vectors' barrier, or the cross-wavefront reduction's).
+template <int TEAM, class SV>
+constexpr bool rms_front_syncs() { return SV::kStaged || TEAM > kWave; }
+
+// `before_barrier` runs once the row loads are issued and before the block's
+// first barrier, so block-wide LDS a kernel fills there (a table) is
+// visible to every lane after rms_front without a barrier of its own when
+// rms_front_syncs() holds.
+template <int TEAM, int CPL, bool VEC, bool RES, class SV, bool KEEP = false, class Pre = NoBlockWork>
 __device__ __forceinline__ float rms_front(const uint16_t* x, int64_t ld_x, const uint16_t* r, int64_t ld_r,
                                            uint16_t* ro, int64_t ld_ro, const RowMap& m, int t, int d,
                                            double inv_d, float eps, SV& vecs, typename SV::Lds& lds_vec,
-                                           double* lds_sum, uint4 (&zw)[CPL], float (*zf)[8] = nullptr)
+                                           double* lds_sum, uint4 (&zw)[CPL], float (*zf)[8] = nullptr,
+                                           const Pre& before_barrier = Pre())
 {
     const RowIO<VEC, kLoadStream, uint16_t> xio(x, ld_x, m, d);
     double acc = 0.0;
@@ -87,6 +101,7 @@ __device__ __forceinline__ float rms_front(const uint16_t* x, int64_t ld_x, cons
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    before_barrier();
     vecs.publish(lds_vec);
     acc = team_sum<TEAM>(acc, lds_sum);
     const float ms = (float)div_by_len(acc, (double)d, inv_d);

@@ -62,7 +62,18 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
     SV gamma({a.gamma}, d);
 
     const float sg = a.global_scale[0];  // issued early: read on the device at run time
+    const float G = 1.0f / sg;            // encode scale
 
+    // The element multiplier depends only on the block-scale code: one
+    // correctly rounded quotient per code and block instead of one per chunk.
+    // The table is filled while the row loads are in flight, before the
+    // front half's first barrier, which then also publishes it.
+    const auto fill_table = [&]() {
+        if (threadIdx.x < 128) {
+            const float sfd = e4m3_value(threadIdx.x);
+            lds_mult[threadIdx.x] = sfd > 0.0f ? G / sfd : 0.0f;
+        }
+    };
     // Residual-less rows keep z unpacked from the sum of squares (these
     // instances have registers to spare); the others unpack it again below.
     constexpr bool KEEP = !RES;
@@ -70,15 +81,8 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
     float zf[KEEP ? CPL : 1][8];
     const float rstd = rms_front<TEAM, CPL, VEC, RES, SV, KEEP>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d,
                                                                a.inv_d, a.eps, gamma, lds_gamma, lds_sum, zw,
-                                                               KEEP ? zf : nullptr);
-    const float G = 1.0f / sg;  // encode scale
-    // The element multiplier depends only on the block-scale code: one
-    // correctly rounded quotient per code and block instead of one per chunk.
-    if (threadIdx.x < 128) {
-        const float sfd = e4m3_value(threadIdx.x);
-        lds_mult[threadIdx.x] = sfd > 0.0f ? G / sfd : 0.0f;
-    }
-    __syncthreads();
+                                                               KEEP ? zf : nullptr, fill_table);
+    if constexpr (!rms_front_syncs<TEAM, SV>()) __syncthreads();
 
     const RowIO<VEC, kStoreRows, uint16_t> nio(a.norm_out, a.ld_n, m, d);
     const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d / 2);
