@@ -94,6 +94,13 @@ template <Fp8 F>
 constexpr float fp8_max() { return F == Fp8::E5M2 ? kE5M2Max : kE4M3Max; }
 
 template <Fp8 F>
+__device__ __forceinline__ float fp8_clamp(float v)
+{
+    if constexpr (F == Fp8::E5M2) return clamp_e5m2(v);
+    else return clamp_e4m3(v);
+}
+
+template <Fp8 F>
 __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d)
 {
     if constexpr (F == Fp8::E5M2) return e5m2x4(a, b, c, d);

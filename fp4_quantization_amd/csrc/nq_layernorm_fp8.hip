@@ -63,20 +63,12 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
     if constexpr (!DYN) scale = a.scale[0];  // issued early: read on the device at run time
 
     uint4 xw[CPL];
-    // The many-rows dynamic form (7 wavefronts per SIMD, vector-issue bound)
-    // issues its loads at raised wavefront priority, so a wavefront starting
-    // its row is not held behind others' arithmetic: 4.5 % faster on MI355X.
-    // The same hint slows the static form by 2 % and the RMSNorm kernels by
-    // 10 %.
-    constexpr bool kLoadPriority = DYN && STAGE;
-    if constexpr (kLoadPriority) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int e = (j * TEAM + t) * 8;
         xw[j] = xio.load16(e, col_live<TEAM, VEC>(e, d));
     }
     gb.issue(t);
-    if constexpr (kLoadPriority) __builtin_amdgcn_s_setprio(0);
 
     // mean = sum(x) / d (masked elements load as 0).  The unpacked row is
     // what c replaces below, so it stays unpacked.
@@ -175,28 +167,57 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int e = (j * TEAM + t1) * 8;
-            float g[8], b[8];
-            gb.chunk(lds_gb, 0, j, e, g);
-            gb.chunk(lds_gb, 1, j, e, b);
+            if constexpr (SV::kStaged) {
+                // half a chunk of gamma and beta at a time: 8 registers fewer
+                // at the kernel's peak, which sets its occupancy
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float n = c[j][k] * rstd;
-                const float gn = n * g[k];
-                c[j][k] = gn + b[k];
-                amax = fmaxf(amax, fabsf(c[j][k]));
+                for (int h = 0; h < 2; ++h) {
+                    float g[4], b[4];
+                    gb.half(lds_gb, 0, e, h, g);
+                    gb.half(lds_gb, 1, e, h, b);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float n = c[j][4 * h + k] * rstd;
+                        const float gn = n * g[k];
+                        c[j][4 * h + k] = gn + b[k];
+                        amax = fmaxf(amax, fabsf(c[j][4 * h + k]));
+                    }
+                }
+            } else {
+                float g[8], b[8];
+                gb.chunk(lds_gb, 0, j, e, g);
+                gb.chunk(lds_gb, 1, j, e, b);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float n = c[j][k] * rstd;
+                    const float gn = n * g[k];
+                    c[j][k] = gn + b[k];
+                    amax = fmaxf(amax, fabsf(c[j][k]));
+                }
             }
         }
         amax = team_max<TEAM>(amax, lds_max);
         const float s = amax / fp8_max<F>();
         if (t == 0 && m.ok) a.scale_out[m.row] = s;
         const float inv = s > 0.0f ? 1.0f / s : 0.0f;
+        // The quotients replace y in place.  With a normal scale in every
+        // lane they are bounded as the clamp-free conversion needs; otherwise
+        // the wavefront clamps them first (the same codes either way).
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) c[j][k] = div_by(c[j][k], s, inv);
+        if (!wave_scales_normal(s)) {
+            __asm__ volatile("");  // keep it a branch
+#pragma unroll
+            for (int j = 0; j < CPL; ++j)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) c[j][k] = fp8_clamp<F>(c[j][k]);
+        }
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int e = (j * TEAM + t1) * 8;
-            float v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = div_by(c[j][k], s, inv);
-            qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8<F>(v));
+            qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8_bounded<F>(c[j]));
         }
     }
 }

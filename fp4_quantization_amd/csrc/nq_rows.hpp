@@ -240,6 +240,16 @@ class SharedVectors {
         }
     }
 
+    // Elements 4h .. 4h+3 of the chunk at e (staged only: one LDS read, so a
+    // loop over the chunk's halves holds 4 registers per vector, not 8).
+    __device__ __forceinline__ void half(const Lds& lds, int v, int e, int h, float g[4]) const
+    {
+        static_assert(kStaged, "half chunks come from the staged copy");
+        const uint4 a = lds[v][e / 4 + h];
+        g[0] = __uint_as_float(a.x); g[1] = __uint_as_float(a.y);
+        g[2] = __uint_as_float(a.z); g[3] = __uint_as_float(a.w);
+    }
+
   private:
     RowIO<VEC, kKeep, uint16_t> io_[NV];
     uint4 held_[kStaged ? NV : 1][kPer];

@@ -713,6 +713,31 @@ def test_layernorm_static_e5m2(nq, orc, scale, d, M):
     assert_codes(q[rows], o["q"], "ln static e5m2 q", fmt="e5m2")
 
 
+@pytest.mark.parametrize("fmt,scale", [("e4m3", 0.05), ("e5m2", 2e-4)])
+@pytest.mark.parametrize("M", [8, 2048])
+def test_layernorm_static_saturating_rows(nq, orc, fmt, scale, M):
+    """Static scales that leave most rows in range while every 37th row holds
+    one outlier whose scaled value saturates: the whole output must match the
+    oracle, the outliers must take the largest finite code and no other row
+    may reach it."""
+    note(f"layernorm static saturating rows {fmt} M={M}")
+    d = 4096
+    w = W.layernorm_rows(M=M, d=d, seed=71 + M)
+    x = w["x"].copy()
+    big = np.arange(0, M, 37)
+    x[big, 1000] = W.to_bf16_bits(np.full(len(big), 60.5, np.float32))
+    w = dict(w, x=x)
+    flags = nq.NQ_FLAG_E5M2 if fmt == "e5m2" else 0
+    q, _ = run_ln_ex(nq, w, flags, scale)
+    o = orc.layernorm_quant_fp8(x, w["gamma"], w["beta"], w["eps"], scale, fmt=fmt)
+    assert_codes(q, o["q"], f"ln static {fmt} q with saturating rows", fmt=fmt)
+    sat = 0x7E if fmt == "e4m3" else 0x7B  # largest finite magnitude
+    assert np.all((o["q"][big, 1000] & 0x7F) == sat), "the outliers saturate"
+    rest = np.setdiff1d(np.arange(M), big)
+    if len(rest):
+        assert not np.any((o["q"][rest] & 0x7F) == sat), "the other rows stay in range"
+
+
 def test_layernorm_dynamic_schedules_and_zero_rows(nq, orc):
     """Many rows (gamma and beta staged) and few rows give identical bits; a
     constant row gives y = beta, an all-zero row (beta = 0) scale 0."""
