@@ -79,7 +79,7 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
     constexpr bool KEEP = !RES;
     uint4 zw[CPL];
     float zf[KEEP ? CPL : 1][8];
-    const float rstd = rms_front<TEAM, CPL, VEC, RES, SV, KEEP>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d,
+    const float rstd = rms_front<TEAM, CPL, VEC, RES, SV, KEEP, true>(a.x, a.ld_x, a.r, a.ld_r, a.ro, a.ld_ro, m, t, d,
                                                                a.inv_d, a.eps, gamma, lds_gamma, lds_sum, zw,
                                                                KEEP ? zf : nullptr, fill_table);
     if constexpr (!rms_front_syncs<TEAM, SV>()) __syncthreads();

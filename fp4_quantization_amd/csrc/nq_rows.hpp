@@ -106,13 +106,14 @@ __device__ __forceinline__ RowMap vector_map()
 // Vectors shared by every row (gamma, beta).  Loading them per row doubles
 // the load traffic that reaches the caches (measured on MI355X at d = 2816:
 // ~1.3 us of a 28 us call).  Where a block holds several rows, the block
-// loads each vector once, cooperatively, right after the first row loads,
-// writes it to LDS before the first reduction (whose barrier, or one of its
-// own for teams within a wavefront, orders the writes before every read),
-// and the lanes read their chunks from LDS.  Staged only while the LDS of
-// the blocks that fill a compute unit (32 wavefronts) stays within its
-// 160 KB; otherwise, and on the element-wise path, each lane loads its
-// chunks from memory.
+// loads each vector once, cooperatively, right after the first row loads
+// (or, where a kernel asks, right before them, writing LDS as soon as they
+// arrive), writes it to LDS before the first reduction (whose barrier, or
+// one of its own for teams within a wavefront, orders the writes before
+// every read), and the lanes read their chunks from LDS.  Staged only while
+// the LDS of the blocks that fill a compute unit (32 wavefronts) stays
+// within its 160 KB; otherwise, and on the element-wise path, each lane
+// loads its chunks from memory.
 constexpr int kLanesPerCU = 2048;        // 8 wavefronts per SIMD x 4 SIMDs x 64
 constexpr int kLdsPerCU = 160 * 1024;
 
