@@ -340,14 +340,18 @@ __device__ __forceinline__ float pow2_ceil(float t)
 // smaller y the quotient can be off, but a kernel meets such y with a
 // quotient whose FP8 code can be non-zero only in rows whose maximum is
 // below 2^-84.  Three operations per element instead of a full division
-// sequence.  Checked on the device against correctly rounded division over
-// random and edge operands, codes included where the quotient is not
-// exact (test_div_by_matches_division).
+// sequence.  The remainder is formed as -(q0 * s - y): the same value, but
+// for y = -0 it is -0 rather than y + (+0) = +0, so the sum keeps the sign
+// of a zero quotient (-0 / s = -0, as correctly rounded division gives);
+// both negations are source modifiers, so this costs nothing.  Checked on
+// the device against correctly rounded division over random and edge
+// operands, signed zeros included, codes included where the quotient is
+// not exact (test_div_by_matches_division).
 __device__ __forceinline__ float div_by(float y, float s, float inv)
 {
     const float q0 = y * inv;
-    const float r = __builtin_fmaf(-q0, s, y);
-    return __builtin_fmaf(r, inv, q0);
+    const float t = __builtin_fmaf(q0, s, -y);  // -(remainder)
+    return __builtin_fmaf(-t, inv, q0);
 }
 
 // Correctly rounded binary64 a / d for a row length 1 <= d <= 2^15, from

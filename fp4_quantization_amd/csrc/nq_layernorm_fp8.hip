@@ -202,7 +202,8 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
         const float inv = s > 0.0f ? 1.0f / s : 0.0f;
         // The quotients replace y in place.  With a normal scale in every
         // lane they are bounded as the clamp-free conversion needs; otherwise
-        // the wavefront clamps them first (the same codes either way).
+        // the wavefront clamps them first (the same codes either way), and a
+        // zero scale stores +0 codes whatever the signs of y.
 #pragma unroll
         for (int j = 0; j < CPL; ++j)
 #pragma unroll
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
 #pragma unroll
             for (int j = 0; j < CPL; ++j)
 #pragma unroll
-                for (int k = 0; k < 8; ++k) c[j][k] = fp8_clamp<F>(c[j][k]);
+                for (int k = 0; k < 8; ++k) c[j][k] = s > 0.0f ? fp8_clamp<F>(c[j][k]) : 0.0f;
         }
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {

@@ -118,12 +118,14 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
                 qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8_bounded<F>(v));
             }
         } else {
+            // A zero scale (an all-zero row, or amax / fmax below the
+            // smallest subnormal) stores +0 codes whatever the signs of y.
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const int e = (j * TEAM + t1) * 8;
                 float v[8];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) v[k] = div_by(y[j][k], s, inv);
+                for (int k = 0; k < 8; ++k) v[k] = s > 0.0f ? div_by(y[j][k], s, inv) : 0.0f;
                 qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8<F>(v));
             }
         }

@@ -139,6 +139,9 @@ __global__ __launch_bounds__(default_block<TEAM>()) void k_quant_fp8_rows(QuantR
         const float s = amax / fp8_max<F>();
         if (t == 0 && m.ok) a.scale_out[m.row] = s;
         const float inv = s > 0.0f ? 1.0f / s : 0.0f;
+        // A zero scale (an all-zero row) stores +0 codes, -0 inputs included;
+        // the select runs only in a wavefront that holds such a row.
+        const bool zero_scales = __builtin_amdgcn_ballot_w64(!(s > 0.0f)) != 0;
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int e = (j * TEAM + t) * 8;
@@ -146,6 +149,11 @@ __global__ __launch_bounds__(default_block<TEAM>()) void k_quant_fp8_rows(QuantR
             unpack_bf16x8(xw[j], v);
 #pragma unroll
             for (int k = 0; k < 8; ++k) v[k] = div_by(v[k], s, inv);
+            if (zero_scales) {
+                __asm__ volatile("");  // keep it a branch
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = s > 0.0f ? v[k] : 0.0f;
+            }
             qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8<F>(v));
         }
     }

@@ -5,7 +5,8 @@ Acceptance, stated once here and used by every parity test:
   * scales (fp32 per token / per group): within 1e-6 relative;
   * e4m3 and E2M1 codes: identical, except that at most 0.1% of the elements
     may differ by one code step (a reduction-order tie at a rounding
-    midpoint); +0 and -0 count as the same code.
+    midpoint); +0 against -0 is such a step, so it is counted as a
+    difference, not hidden.
 The tolerance is the acceptance bound.  Every comparison is also recorded
 (test, output, elements compared, codes one step apart, worst relative scale
 error), and the test session prints the records of the full-size outputs and
@@ -77,10 +78,12 @@ def _code_steps(a: np.ndarray, b: np.ndarray, mag_mask: int, sign_bit: int):
     a = a.astype(np.int32)
     b = b.astype(np.int32)
     am, bm = a & mag_mask, b & mag_mask
-    same = (a == b) | ((am == 0) & (bm == 0))
-    # one step: same sign and adjacent magnitudes, or zero against the
-    # smallest magnitude of either sign
-    adjacent = (np.abs(am - bm) == 1) & (((a & sign_bit) == (b & sign_bit)) | (np.minimum(am, bm) == 0))
+    same = a == b
+    # one step: same sign and adjacent magnitudes, zero against the smallest
+    # magnitude of either sign, or +0 against -0 (a sign-only difference of
+    # zero counts as a differing code, so the exact-agreement counts see it)
+    adjacent = (((np.abs(am - bm) == 1) & (((a & sign_bit) == (b & sign_bit)) | (np.minimum(am, bm) == 0)))
+                | ((am == 0) & (bm == 0)))
     return same, adjacent
 
 

@@ -154,13 +154,19 @@ def test_div_by_matches_division(nq, orc):
             assert_codes(enc(got[out]), enc(want[out]), f"div_by codes outside the exact range ({fmt})", fmt=fmt)
         checked += y.size
         exact_checked += int(ok_range.sum())
-    # edges: power-of-two scales, quotients exactly 448 / 57344, y = 0
+    # edges: power-of-two scales, quotients exactly 448 / 57344, y = +0 and
+    # -0 (the sign of a zero quotient is kept: -0 / s = -0), and tiny y of
+    # both signs whose quotient underflows to a signed zero; compared bit
+    # for bit
     s = np.ldexp(np.ones(200), np.arange(-120, 80)).astype(np.float32)
-    y = np.concatenate([s * 448, -s * 57344, 0 * s]).astype(np.float32)
-    s3 = np.concatenate([s, s, s])
+    tiny = np.float32(2.0 ** -149)
+    y = np.concatenate([s * 448, -s * 57344, 0 * s, np.full(200, -0.0), np.full(200, tiny),
+                        np.full(200, -tiny)]).astype(np.float32)
+    s3 = np.concatenate([s] * 6)
     got = _run(nq, nq.NQ_ARITH_DIV, torch.from_numpy(y).cuda(), torch.from_numpy(s3).cuda()).cpu().numpy()
     want = (y.astype(np.float64) / s3.astype(np.float64)).astype(np.float32)
-    assert np.array_equal(got, want)
+    assert np.signbit(want[600:800]).all() and np.signbit(want[1000:]).all()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
     assert checked > 60_000_000 and exact_checked > 55_000_000
 
 

@@ -738,6 +738,41 @@ def test_layernorm_static_saturating_rows(nq, orc, fmt, scale, M):
         assert not np.any((o["q"][rest] & 0x7F) == sat), "the other rows stay in range"
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("f", [1.0, 1.37])
+@pytest.mark.parametrize("d,M", [(4096, 2048), (256, 96)])
+def test_layernorm_dynamic_subnormal_scales(nq, orc, fmt, f, d, M):
+    """Constant rows give y = beta.  Here beta's largest magnitude is
+    fmax * 2^-127 * f, so those rows' scales amax / fmax are subnormal
+    (2^-127 exactly for f = 1, a rounded subnormal for f = 1.37) but inside
+    the documented range (a scale of at least 2^-128); the other rows keep
+    normal scales, in the same wavefront where rows are narrower than one.
+    Whole output; the constant rows' scales and codes bit for bit (y is beta
+    exactly there, so the chunk sums play no part)."""
+    note(f"layernorm dynamic subnormal scales {fmt} f={f} d={d} M={M}")
+    fmax = 448.0 if fmt == "e4m3" else 57344.0
+    w = W.layernorm_rows(M=M, d=d, seed=90 + M)
+    rng = np.random.default_rng(91)
+    u = rng.uniform(-1.0, 1.0, d)
+    u[7] = -1.0
+    beta = (u * (fmax * 2.0 ** -127 * f)).astype(np.float32)
+    x = w["x"].copy()
+    const = np.arange(0, M, 3)
+    x[const] = W.to_bf16_bits(np.full(d, 0.75, np.float32))
+    w = dict(w, x=x, beta=beta)
+    flags = nq.NQ_FLAG_E5M2 if fmt == "e5m2" else 0
+    q, s = run_ln_ex(nq, w, flags)
+    o = orc.layernorm_quant_fp8(x, w["gamma"], beta, w["eps"], None, fmt=fmt)
+    assert_scales(s, o["scale"], "ln dynamic scales")
+    assert_bits_equal(s[const].view(np.uint32), o["scale"][const].view(np.uint32), "subnormal scales")
+    assert_bits_equal(q[const], o["q"][const], "ln dynamic codes of the subnormal-scale rows")
+    assert_codes(q, o["q"], f"ln dynamic {fmt} q with subnormal scales", fmt=fmt)
+    sc = o["scale"][const]
+    assert np.all((sc >= np.float32(2.0 ** -128)) & (sc < np.float32(2.0 ** -126))), "subnormal, in range"
+    top = 0x7E if fmt == "e4m3" else 0x7B
+    assert np.any((o["q"][const] & 0x7F) == top), "the largest element takes the top code"
+
+
 def test_layernorm_dynamic_schedules_and_zero_rows(nq, orc):
     """Many rows (gamma and beta staged) and few rows give identical bits; a
     constant row gives y = beta, an all-zero row (beta = 0) scale 0."""
@@ -890,6 +925,69 @@ def test_per_token_quant_static_e5m2_and_shapes(nq, orc):
             assert_bits_equal(host_u8(q), o["q"], f"quant d={d} scale={sc} {fmt}")
             if sc is None:
                 assert_bits_equal(s.cpu().numpy().view(np.uint32), o["scale"].view(np.uint32), "scale")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("M", [8, 2048])
+def test_zero_scale_rows_store_plus_zero_codes(nq, orc, fmt, M):
+    """A per-token scale of 0 (an all-zero row: padding tokens) stores code
+    0x00 for every element, as the oracle does, even where y is -0: here the
+    zero rows are -0 + -0 (z = -0) and gamma has both signs, so y holds both
+    zeros.  Every per-token entry point: the fused RMSNorm kernel (both row
+    schedules), the unfused pair, the quantizer alone on rows of +0 and -0,
+    and dynamic LayerNorm (constant rows with beta made of +0 and -0).  The
+    zero rows are compared bit for bit, the others within the tolerance."""
+    note(f"zero-scale rows {fmt} M={M}")
+    flags = nq.NQ_FLAG_E5M2 if fmt == "e5m2" else 0
+    d = 2816
+    rng = np.random.default_rng(101)
+    w = W.rms_2816(M, seed=100)
+    zero = np.array([0, 5]) if M > 5 else np.array([0])
+    x, r = w["x"].copy(), w["residual"].copy()
+    x[zero], r[zero] = 0x8000, 0x8000
+    gamma = rng.standard_normal(d).astype(np.float32)
+    w = dict(w, x=x, residual=r, gamma=gamma)
+    got = run_rms_fp8_ex(nq, w, flags)
+    o = orc.fused_add_rmsnorm_quant_fp8(x, r, gamma, w["eps"], fmt=fmt, want_y=True)
+    assert np.any(np.signbit(o["y"][zero])) and not np.all(np.signbit(o["y"][zero])), "y holds +0 and -0"
+    assert np.all(o["q"][zero] == 0) and np.all(o["scale"][zero] == 0)
+    assert_bits_equal(got["q"][zero], o["q"][zero], "fused zero-row codes")
+    assert_bits_equal(got["scale"].view(np.uint32), o["scale"].view(np.uint32), "fused scales")
+    assert_bits_equal(got["residual_out"], o["residual_out"], "residual_out (-0 kept)")
+    assert_codes(got["q"], o["q"], "fused codes", fmt=fmt)
+
+    u = run_unfused(nq, w, flags=flags)
+    # the unfused reference: the oracle's bf16 norm output, then its quantizer
+    on = orc.fused_add_rmsnorm_quant_fp8(x, r, gamma, w["eps"], want_norm_out=True)["norm_out"]
+    ou = orc.quant_fp8_rows(W.bf16_bits_to_f32(on), fmt=fmt)
+    assert_bits_equal(u["q"][zero], ou["q"][zero], "unfused zero-row codes")
+    assert_codes(u["q"], ou["q"], "unfused codes", fmt=fmt)
+
+    rows = np.zeros((M, d), np.uint16)
+    rows[1::2] = 0x8000  # rows of -0 alternate with rows of +0
+    xq = to_dev_bf16(rows)
+    q = torch.empty(M, d, dtype=torch.uint8, device="cuda")
+    s = torch.empty(M, dtype=torch.float32, device="cuda")
+    nq.nq_per_token_quant_fp8(xq, None, flags, q, s)
+    torch.cuda.synchronize()
+    oq = orc.quant_fp8_rows(W.bf16_bits_to_f32(rows), fmt=fmt)
+    assert np.all(oq["q"] == 0)
+    assert_bits_equal(host_u8(q), oq["q"], "quantizer codes of zero rows")
+    assert_bits_equal(s.cpu().numpy().view(np.uint32), oq["scale"].view(np.uint32), "quantizer zero scales")
+
+    wl = W.layernorm_rows(M=M, d=4096, seed=102)
+    beta = np.where(rng.random(4096) < 0.5, -0.0, 0.0).astype(np.float32)
+    gl = rng.standard_normal(4096).astype(np.float32)
+    xl = wl["x"].copy()
+    xl[zero] = W.to_bf16_bits(np.full(4096, 1.25, np.float32))  # constant rows: y = 0 * gamma + beta
+    wl = dict(wl, x=xl, gamma=gl, beta=beta)
+    ql, sl = run_ln_ex(nq, wl, flags)
+    ol = orc.layernorm_quant_fp8(xl, gl, beta, wl["eps"], None, fmt=fmt, want_y=True)
+    assert np.any(np.signbit(ol["y"][zero])), "y holds -0"
+    assert np.all(ol["q"][zero] == 0) and np.all(ol["scale"][zero] == 0)
+    assert_bits_equal(ql[zero], ol["q"][zero], "layernorm zero-row codes")
+    assert_bits_equal(sl[zero].view(np.uint32), ol["scale"][zero].view(np.uint32), "layernorm zero scales")
+    assert_codes(ql, ol["q"], "layernorm codes", fmt=fmt)
 
 
 def test_fused_vs_unfused_on_gpu(nq, orc):
