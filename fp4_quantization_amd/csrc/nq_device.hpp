@@ -437,13 +437,16 @@ __device__ __forceinline__ float div6_rn(float amax)
 // inputs read once are non-temporal, bf16 row outputs (residual, norm_out)
 // are written with sc1, quantized codes non-temporal, per-group and NVFP4
 // block scale rows (small pieces per row) with sc0 -- 0.3 to 1 % faster than
-// non-temporal; gamma / beta use the default policy.
+// non-temporal; gamma / beta use the default policy.  LayerNorm, whose codes
+// are its only output, writes them with sc1: 3 % faster than non-temporal
+// there, while sc1 codes slowed the RMSNorm kernels by 1-11 %.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kLoadStream = 2;              // nt
 constexpr int kStoreRows = 16;              // sc1
 constexpr int kStoreCodes = 2;              // nt
+constexpr int kStoreCodesOnly = 16;         // sc1: codes that are a kernel's only output (LayerNorm)
 constexpr int kStoreScales = 1;             // sc0: small scale rows, written in pieces
 constexpr int kKeep = 0;                    // default
 constexpr uint32_t kOOB = 0x80000000u;      // beyond any resource size used here

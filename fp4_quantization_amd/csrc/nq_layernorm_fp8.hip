@@ -58,7 +58,7 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
     using SV = SharedVectors<TEAM, CPL, VEC, 2, BLOCK, STAGE, GB>;
     __shared__ typename SV::Lds lds_gb;
     SV gb({a.gamma, a.beta}, d);
-    const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d);
+    const RowIO<VEC, kStoreCodesOnly, uint8_t> qio(a.q, a.ld_q, m, d);
     float scale = 1.0f;
     if constexpr (!DYN) scale = a.scale[0];  // issued early: read on the device at run time
 
