@@ -492,6 +492,14 @@ struct RowIO<true, POLICY, T> {
         const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off(i, live), 0, POLICY);
         return make_uint4(v.x, v.y, v.z, v.w);
     }
+    // 16 bytes starting at element i, written by the load itself to LDS at
+    // `lds` + 16 * (lane within the wavefront) (zeros when masked or out of
+    // range); `lds` must be the same for every lane of the wavefront.
+    __device__ __forceinline__ void load16_lds(int i, bool live, void* lds) const
+    {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
+                                                 (int)off(i, live), 0, 0, POLICY);
+    }
     // 8 bytes starting at element i
     __device__ __forceinline__ uint2 load8(int i, bool live) const
     {

@@ -67,7 +67,7 @@ __device__ __forceinline__ float rms_front(const uint16_t* x, int64_t ld_x, cons
         const RowIO<VEC, kLoadStream, uint16_t> rio(r, ld_r, m, d);
         const RowIO<VEC, kStoreRows, uint16_t> roio(ro, ld_ro, m, d);
         // Issue every load of the row before the first use.
-        if constexpr (kEarly) vecs.issue(t);
+        if constexpr (kEarly) vecs.issue(t, lds_vec);
         uint4 xw[CPL], rw[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
@@ -79,7 +79,7 @@ __device__ __forceinline__ float rms_front(const uint16_t* x, int64_t ld_x, cons
             before_barrier();
             vecs.publish(lds_vec);
         } else {
-            vecs.issue(t);
+            vecs.issue(t, lds_vec);
         }
         // z = bf16(x + r), kept packed; residual write-back; sum of z^2.
 #pragma unroll
@@ -102,7 +102,7 @@ __device__ __forceinline__ float rms_front(const uint16_t* x, int64_t ld_x, cons
             const int e = (j * TEAM + t) * 8;
             zw[j] = xio.load16(e, col_live<TEAM, VEC>(e, d));
         }
-        vecs.issue(t);
+        vecs.issue(t, lds_vec);
         if constexpr (KEEP) {
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {

@@ -110,10 +110,11 @@ __device__ __forceinline__ RowMap vector_map()
 // (or, where a kernel asks, right before them, writing LDS as soon as they
 // arrive), writes it to LDS before the first reduction (whose barrier, or
 // one of its own for teams within a wavefront, orders the writes before
-// every read), and the lanes read their chunks from LDS.  Staged only while
-// the LDS of the blocks that fill a compute unit (32 wavefronts) stays
-// within its 160 KB; otherwise, and on the element-wise path, each lane
-// loads its chunks from memory.
+// every read), and the lanes read their chunks from LDS (LayerNorm's fp32
+// vectors are loaded straight into LDS, buffer_load ... lds, see kDma).
+// Staged only while the LDS of the blocks that fill a compute unit (32
+// wavefronts) stays within its 160 KB; otherwise, and on the element-wise
+// path, each lane loads its chunks from memory.
 constexpr int kLanesPerCU = 2048;        // 8 wavefronts per SIMD x 4 SIMDs x 64
 constexpr int kLdsPerCU = 160 * 1024;
 
@@ -134,7 +135,7 @@ constexpr int row_block()
     return default_block<TEAM>();
 }
 
-template <int TEAM, int CPL, bool VEC, int NV, int BLOCK, bool STAGE, bool BF16 = false>
+template <int TEAM, int CPL, bool VEC, int NV, int BLOCK, bool STAGE, bool BF16 = false, bool DMA = false>
 class SharedVectors {
   public:
     using S = TeamShape<TEAM, BLOCK>;
@@ -146,6 +147,12 @@ class SharedVectors {
     // loads instead of after the first reduction, taking one memory round
     // trip off the critical path for at most 16 more registers per vector.
     static constexpr bool kPrefetch = !kStaged && CPL <= 2;
+    // DMA: staged fp32 vectors are loaded straight into LDS (bf16 ones are
+    // widened on the way, through registers).  Measured on MI355X against
+    // the register path: the dynamic LayerNorm 1.5 % faster, the static one
+    // the same, the RMSNorm kernels 0.3-1.8 % slower (so only LayerNorm
+    // asks for it).
+    static constexpr bool kDma = DMA && kStaged && !BF16;
     typedef uint4 Lds[kStaged ? NV : 1][kStaged ? kSlots : 1];
     static_assert(!kStaged || kSlots * 16 * NV <= 64 * 1024, "staged vectors fit one block's LDS");
 
@@ -163,7 +170,7 @@ class SharedVectors {
     // Issue the loads: staged, the block's cooperative loads (fp32 slot i
     // holds elements 4i .. 4i+3, loaded as 16 bytes, or as 8 bytes of bf16
     // widened at publish); prefetching, lane t's own chunks.
-    __device__ __forceinline__ void issue(int t)
+    __device__ __forceinline__ void issue(int t, Lds& lds)
     {
         if constexpr (kPrefetch) {
 #pragma unroll
@@ -179,7 +186,21 @@ class SharedVectors {
                     }
                 }
         }
-        if constexpr (kStaged) {
+        if constexpr (kDma) {
+            // fp32 vectors go straight to LDS: each wavefront's 64 lanes
+            // fill 64 consecutive slots, with no registers held and no LDS
+            // writes of their own (the barrier that publishes them waits for
+            // the loads)
+            const int wave_first = (int)(threadIdx.x & ~(kWave - 1));
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int u = 0; u < kPer; ++u) {
+                    const int i = u * S::kBlock + (int)threadIdx.x;
+                    if (u * S::kBlock + wave_first < kSlots && i < kSlots)
+                        io_[v].load16_lds(i * 8, VEC || i * 4 < d_, &lds[v][u * S::kBlock + wave_first]);
+                }
+        } else if constexpr (kStaged) {
 #pragma unroll
             for (int v = 0; v < NV; ++v)
 #pragma unroll
@@ -198,7 +219,9 @@ class SharedVectors {
     // reduction, which every lane of the block reaches).
     __device__ __forceinline__ void publish(Lds& lds)
     {
-        if constexpr (kStaged) {
+        if constexpr (kDma) {
+            if constexpr (TEAM <= kWave) __syncthreads();
+        } else if constexpr (kStaged) {
 #pragma unroll
             for (int v = 0; v < NV; ++v)
 #pragma unroll
@@ -253,7 +276,7 @@ class SharedVectors {
 
   private:
     RowIO<VEC, kKeep, uint16_t> io_[NV];
-    uint4 held_[kStaged ? NV : 1][kPer];
+    uint4 held_[kStaged && !kDma ? NV : 1][kStaged && !kDma ? kPer : 1];
     uint4 pre_[kPrefetch ? NV : 1][kPrefetch ? CPL : 1][BF16 ? 1 : 2];
     int d_;
 };
