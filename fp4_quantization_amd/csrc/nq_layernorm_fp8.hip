@@ -55,7 +55,7 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
     const RowMap m = row_map<TEAM, BLOCK>(a.M);
     const int d = a.d;
     const RowIO<VEC, kLoadStream, uint16_t> xio(a.x, a.ld_x, m, d);
-    using SV = SharedVectors<TEAM, CPL, VEC, 2, BLOCK, STAGE, GB, /*DMA=*/true>;
+    using SV = SharedVectors<TEAM, CPL, VEC, 2, BLOCK, STAGE, GB, /*DMA=*/DYN>;
     __shared__ typename SV::Lds lds_gb;
     SV gb({a.gamma, a.beta}, d);
     const RowIO<VEC, kStoreCodesOnly, uint8_t> qio(a.q, a.ld_q, m, d);

@@ -110,8 +110,9 @@ __device__ __forceinline__ RowMap vector_map()
 // (or, where a kernel asks, right before them, writing LDS as soon as they
 // arrive), writes it to LDS before the first reduction (whose barrier, or
 // one of its own for teams within a wavefront, orders the writes before
-// every read), and the lanes read their chunks from LDS (LayerNorm's fp32
-// vectors are loaded straight into LDS, buffer_load ... lds, see kDma).
+// every read), and the lanes read their chunks from LDS (the dynamic
+// LayerNorm's fp32 vectors are loaded straight into LDS, buffer_load ...
+// lds, see kDma).
 // Staged only while the LDS of the blocks that fill a compute unit (32
 // wavefronts) stays within its 160 KB; otherwise, and on the element-wise
 // path, each lane loads its chunks from memory.
@@ -150,8 +151,9 @@ class SharedVectors {
     // DMA: staged fp32 vectors are loaded straight into LDS (bf16 ones are
     // widened on the way, through registers).  Measured on MI355X against
     // the register path: the dynamic LayerNorm 1.5 % faster, the static one
-    // the same, the RMSNorm kernels 0.3-1.8 % slower (so only LayerNorm
-    // asks for it).
+    // within noise (and 12 more vector instructions per wavefront), the
+    // RMSNorm kernels 0.3-1.8 % slower, so only the dynamic LayerNorm asks
+    // for it.
     static constexpr bool kDma = DMA && kStaged && !BF16;
     typedef uint4 Lds[kStaged ? NV : 1][kStaged ? kSlots : 1];
     static_assert(!kStaged || kSlots * 16 * NV <= 64 * 1024, "staged vectors fit one block's LDS");
