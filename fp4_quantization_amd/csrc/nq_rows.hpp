@@ -222,6 +222,10 @@ class SharedVectors {
     __device__ __forceinline__ void publish(Lds& lds)
     {
         if constexpr (kDma) {
+            // This wavefront's loads into LDS have landed before it reaches
+            // the barrier that publishes them (s_waitcnt vmcnt(0); the row
+            // loads, issued first, are already in use here).
+            __builtin_amdgcn_s_waitcnt(0x0F70);
             if constexpr (TEAM <= kWave) __syncthreads();
         } else if constexpr (kStaged) {
 #pragma unroll
