@@ -685,12 +685,16 @@ def test_layernorm_dynamic_full_config(nq, orc, fmt):
     assert_codes(q[rows], o["q"], "ln dynamic q", fmt=fmt)
 
 
-@pytest.mark.parametrize("d", [1, 3, 111, 256, 768, 4096, 16384])
+@pytest.mark.parametrize("d", [1, 3, 111, 256, 768, 2304, 4096, 16384])
 @pytest.mark.parametrize("M", [1, 7, 989, 1501])
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 def test_layernorm_dynamic_shapes(nq, orc, d, M, fmt):
     """[LNQ] "Tests": batch 1 .. 989, hidden 111 .. 16384 (odd sizes take the
-    element-wise path), both FP8 formats; here with per-token scales."""
+    element-wise path), both FP8 formats; here with per-token scales.  At
+    M = 1501 the rows of 256, 768 and 2304 elements stage gamma and beta
+    straight into LDS with some wavefronts' slots past the vectors' end
+    (256: one wavefront of four loads; 768: three of four; 2304: the second
+    pass half used)."""
     note(f"layernorm dynamic d={d} M={M} {fmt}")
     w = W.layernorm_rows(M=M, d=d, seed=3 * d + M)
     q, s = run_ln_ex(nq, w, nq.NQ_FLAG_E5M2 if fmt == "e5m2" else 0)
