@@ -95,7 +95,8 @@ typedef int nq_status;
  *   rstd = 1 / sqrt(sum_i z_i^2 / d + eps)
  *   y_i  = (z_i * rstd) * gamma_i kept in fp32 registers, never rounded to bf16
  *   dynamic (static_scale == NULL):
- *     s = max_i |y_i| / 448  -> scale_out[m];  q_i = e4m3(y_i / s)  (0 if s == 0)
+ *     s = max_i |y_i| / 448  -> scale_out[m];  q_i = e4m3(y_i / s)  (code 0x00
+ *     for every element if s == 0, whatever the sign of y_i)
  *   static (static_scale != NULL):
  *     q_i = e4m3(y_i * (1 / static_scale[0]))  i.e. out = y / scale
  *   norm_out_i = bf16(y_i)        only when norm_out != NULL
@@ -181,7 +182,8 @@ nq_status nq_layernorm_quant_fp8(
  *   scale != NULL (static):  q_i = fp8(y_i * (1 / scale[0])); scale_out unused
  *   scale == NULL (dynamic): s = max_i |y_i| / fmax -> scale_out[m];
  *                            q_i = fp8(y_i / s)  (one correctly rounded
- *                            quotient per element; 0 when s == 0)
+ *                            quotient per element; code 0x00 for
+ *                            every element when s == 0)
  *   fmax = 448 (e4m3) or 57344 (NQ_FLAG_E5M2)
  *   flags      any of NQ_FLAG_E5M2, NQ_FLAG_GAMMA_BF16 (gamma and beta bf16);
  *              NQ_ERR_ARG for other bits
@@ -344,7 +346,7 @@ nq_status nq_rmsnorm_quant_nvfp4_ex(
  * nq_per_token_quant_fp8: FP8 of bf16 rows x, the quantization step of
  *   nq_fused_add_rmsnorm_quant_fp8 on y_i = x_i:
  *     dynamic (static_scale == NULL): s = max_i |x_i| / fmax -> scale_out[m],
- *       q_i = fp8(x_i / s) (0 if s == 0)
+ *       q_i = fp8(x_i / s) (code 0x00 for every element if s == 0)
  *     static: q_i = fp8(x_i * (1 / static_scale[0]))
  *   fmax = 448 (e4m3) or 57344 (flags = NQ_FLAG_E5M2; NQ_ERR_ARG for other bits)
  *     x          [M, d] bf16, row stride ld_x
