@@ -10,6 +10,16 @@
 //                                   fresh residual buffer, 3 replays)
 //                                   DIR/gq.bin DIR/gs.bin (per-token-group
 //                                   FP8 of x, when D % 128 == 0)
+//                                   DIR/fq.bin DIR/fs.bin DIR/fro.bin (the
+//                                   fused RMSNorm + group-128 FP8, fp32
+//                                   scales, when D % 128 == 0)
+//                            reads  DIR/beta.bin (fp32, D), DIR/lnscale.bin
+//                                   and DIR/nvsg.bin (one fp32 each)
+//                            writes DIR/lq.bin (LayerNorm + static e4m3,
+//                                   eps 1e-5), DIR/ldq.bin DIR/lds.bin
+//                                   (LayerNorm + dynamic e5m2), DIR/nq.bin
+//                                   DIR/nsf.bin DIR/nro.bin (residual-add +
+//                                   RMSNorm + NVFP4, when D % 16 == 0)
 // Exit status 0 on success; a failing call prints its status text.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -136,6 +146,58 @@ int main(int argc, char** argv)
         write_file(dir + "/gs.bin", to_host(gs, (size_t)M * (D / 128)));
         HIP_OK(hipFree(gq));
         HIP_OK(hipFree(gs));
+    }
+
+    if (D % 128 == 0) {
+        uint8_t* fq = nullptr;
+        float* fs = nullptr;
+        uint16_t* fro = nullptr;
+        HIP_OK(hipMalloc(&fq, n));
+        HIP_OK(hipMalloc(&fs, (size_t)M * (D / 128) * 4));
+        HIP_OK(hipMalloc(&fro, n * 2));
+        NQ_OK_OR_DIE(nq_fused_add_rmsnorm_quant_fp8_group(x, D, r, D, fro, D, gamma, 1e-6f, 128, NQ_SCALE_FP32, 0u,
+                                                          fq, D, fs, D / 128, nullptr, 0, M, D, st));
+        HIP_OK(hipStreamSynchronize(st));
+        write_file(dir + "/fq.bin", to_host(fq, n));
+        write_file(dir + "/fs.bin", to_host(fs, (size_t)M * (D / 128)));
+        write_file(dir + "/fro.bin", to_host(fro, n));
+        for (void* p : {(void*)fq, (void*)fs, (void*)fro}) HIP_OK(hipFree(p));
+    }
+
+    // LayerNorm: static e4m3 (scale read on the device), then dynamic e5m2
+    {
+        float* beta = to_device(read_file<float>(dir + "/beta.bin", (size_t)D));
+        float* lscale = to_device(read_file<float>(dir + "/lnscale.bin", 1));
+        uint8_t *lq = nullptr, *ldq = nullptr;
+        float* lds = nullptr;
+        HIP_OK(hipMalloc(&lq, n));
+        HIP_OK(hipMalloc(&ldq, n));
+        HIP_OK(hipMalloc(&lds, M * 4));
+        NQ_OK_OR_DIE(nq_layernorm_quant_fp8(x, D, gamma, beta, 1e-5f, lscale, lq, D, M, D, st));
+        NQ_OK_OR_DIE(nq_layernorm_quant_fp8_ex(x, D, gamma, beta, 1e-5f, nullptr, NQ_FLAG_E5M2, ldq, D, lds, M, D,
+                                               st));
+        HIP_OK(hipStreamSynchronize(st));
+        write_file(dir + "/lq.bin", to_host(lq, n));
+        write_file(dir + "/ldq.bin", to_host(ldq, n));
+        write_file(dir + "/lds.bin", to_host(lds, (size_t)M));
+        for (void* p : {(void*)beta, (void*)lscale, (void*)lq, (void*)ldq, (void*)lds}) HIP_OK(hipFree(p));
+    }
+
+    // residual-add + RMSNorm + NVFP4 (global scale read on the device)
+    if (D % 16 == 0) {
+        float* sg = to_device(read_file<float>(dir + "/nvsg.bin", 1));
+        uint8_t *nqp = nullptr, *nsf = nullptr;
+        uint16_t* nro = nullptr;
+        HIP_OK(hipMalloc(&nqp, n / 2));
+        HIP_OK(hipMalloc(&nsf, n / 16));
+        HIP_OK(hipMalloc(&nro, n * 2));
+        NQ_OK_OR_DIE(nq_rmsnorm_quant_nvfp4(x, D, r, D, nro, D, gamma, 1e-6f, sg, nqp, D / 2, nsf, D / 16, nullptr, 0,
+                                            M, D, st));
+        HIP_OK(hipStreamSynchronize(st));
+        write_file(dir + "/nq.bin", to_host(nqp, n / 2));
+        write_file(dir + "/nsf.bin", to_host(nsf, n / 16));
+        write_file(dir + "/nro.bin", to_host(nro, n));
+        for (void* p : {(void*)sg, (void*)nqp, (void*)nsf, (void*)nro}) HIP_OK(hipFree(p));
     }
 
     // a rejected call reports its status and enqueues nothing
