@@ -93,6 +93,18 @@ class Case:
             raise RuntimeError(f"{self.label}: status {st}")
 
 
+def _offset(torch, shape, dtype, off, like=None):
+    """A device tensor whose data start `off` elements past a 16-byte aligned
+    allocation (a copy of `like` when given); off = 0 is a plain tensor."""
+    n = 1
+    for k in shape:
+        n *= k
+    t = torch.empty(n + off, dtype=dtype, device="cuda")[off:].view(*shape)
+    if like is not None:
+        t.copy_(like)
+    return t
+
+
 def _sets_for(nbytes, cap=8):
     """Buffer sets needed so consecutive steps never reuse data still held
     in the 256 MB last-level cache (footprint >= 2 x LLC)."""
@@ -100,7 +112,7 @@ def _sets_for(nbytes, cap=8):
 
 
 class RmsFp8Case(Case):
-    def __init__(self, torch, nq, M, d, seed=0, static=False, sets=None, e5m2=False):
+    def __init__(self, torch, nq, M, d, seed=0, static=False, sets=None, e5m2=False, offset=0):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.rms_2816(M, seed) if d == 2816 else W.rms_small(seed, M)
         rd, wr = traffic.fused_add_rmsnorm_fp8(M, d, residual=True, static=static)
@@ -115,8 +127,10 @@ class RmsFp8Case(Case):
         self.fn = lib.nq_fused_add_rmsnorm_quant_fp8_ex if e5m2 else lib.nq_fused_add_rmsnorm_quant_fp8
         self.bufs, self.args = [], []
         for _ in range(sets or _sets_for(self.bytes)):
-            b = dict(x=x.clone(), r=r.clone(), ro=torch.empty_like(r),
-                     q=torch.empty(M, d, dtype=torch.uint8, device="cuda"),
+            b = dict(x=_offset(torch, (M, d), torch.bfloat16, offset, x),
+                     r=_offset(torch, (M, d), torch.bfloat16, offset, r),
+                     ro=_offset(torch, (M, d), torch.bfloat16, offset),
+                     q=_offset(torch, (M, d), torch.uint8, offset),
                      s=torch.empty(M, dtype=torch.float32, device="cuda"))
             self.bufs.append(b)
             ss = None if self.ss is None else self.ss.data_ptr()
@@ -124,7 +138,8 @@ class RmsFp8Case(Case):
             tail = (b["q"].data_ptr(), d, None if static else b["s"].data_ptr(), None, 0, M, d)
             self.args.append(head + ((nq.NQ_FLAG_E5M2,) if e5m2 else ()) + tail)
         self.label = (f"fused add+RMSNorm+per-token FP8 ({'e5m2' if e5m2 else 'e4m3'}), M={M}, d={d}"
-                      + (", static scale" if static else ""))
+                      + (", static scale" if static else "")
+                      + (f", rows {offset} element(s) off 16-byte boundaries" if offset else ""))
 
 
 class GroupCase(Case):
@@ -147,7 +162,7 @@ class GroupCase(Case):
 
 
 class LayerNormCase(Case):
-    def __init__(self, torch, nq, M=16384, d=4096, dynamic=False, e5m2=False):
+    def __init__(self, torch, nq, M=16384, d=4096, dynamic=False, e5m2=False, offset=0):
         from fp4_quantization_amd import workloads as W, traffic
         w = W.layernorm_rows(M, d)
         self.rw = traffic.layernorm_fp8(M, d, dynamic=dynamic)
@@ -162,7 +177,8 @@ class LayerNormCase(Case):
         flags = nq.NQ_FLAG_E5M2 if e5m2 else 0
         self.bufs, self.args = [], []
         for _ in range(_sets_for(self.bytes)):
-            b = dict(x=x.clone(), q=torch.empty(M, d, dtype=torch.uint8, device="cuda"),
+            b = dict(x=_offset(torch, (M, d), torch.bfloat16, offset, x),
+                     q=_offset(torch, (M, d), torch.uint8, offset),
                      s=torch.empty(M, dtype=torch.float32, device="cuda"))
             self.bufs.append(b)
             sc = None if dynamic else self.sc.data_ptr()
@@ -173,8 +189,9 @@ class LayerNormCase(Case):
                 self.args.append((b["x"].data_ptr(), d, self.g.data_ptr(), self.b.data_ptr(), w["eps"],
                                   sc, b["q"].data_ptr(), d, M, d))
         fmt = "e5m2" if e5m2 else "e4m3"
-        self.label = (f"LayerNorm + dynamic per-token FP8 ({fmt}), M={M}, d={d}" if dynamic
-                      else f"LayerNorm + static FP8 ({fmt}, scale tensor 0.05), M={M}, d={d}")
+        self.label = ((f"LayerNorm + dynamic per-token FP8 ({fmt}), M={M}, d={d}" if dynamic
+                       else f"LayerNorm + static FP8 ({fmt}, scale tensor 0.05), M={M}, d={d}")
+                      + (f", rows {offset} element(s) off 16-byte boundaries" if offset else ""))
 
 
 class Nvfp4Case(Case):
@@ -873,6 +890,7 @@ def suite_cases(torch, nq):
         ("rms_2816_m8192", lambda: RmsFp8Case(torch, nq, 8192, 2816)),
         ("rms_2816_m8192_static", lambda: RmsFp8Case(torch, nq, 8192, 2816, static=True)),
         ("rms_2816_m8192_e5m2", lambda: RmsFp8Case(torch, nq, 8192, 2816, e5m2=True)),
+        ("rms_2816_m8192_unaligned", lambda: RmsFp8Case(torch, nq, 8192, 2816, offset=1)),
         ("group_m32768_fp32", lambda: GroupCase(torch, nq, 32768)),
         ("group_m32768_ue8m0", lambda: GroupCase(torch, nq, 32768, ue8m0=True)),
         ("group_m1", lambda: GroupCase(torch, nq, 1)),
@@ -883,6 +901,7 @@ def suite_cases(torch, nq):
         ("layernorm_m16384", lambda: LayerNormCase(torch, nq)),
         ("layernorm_m16384_e5m2", lambda: LayerNormCase(torch, nq, e5m2=True)),
         ("layernorm_dynamic_m16384", lambda: LayerNormCase(torch, nq, dynamic=True)),
+        ("layernorm_dynamic_m16384_unaligned", lambda: LayerNormCase(torch, nq, dynamic=True, offset=1)),
         ("layernorm_dynamic_m1", lambda: LayerNormCase(torch, nq, M=1, dynamic=True)),
         ("nvfp4_7168_m1", lambda: Nvfp4Case(torch, nq, 1)),
         ("nvfp4_7168_m64", lambda: Nvfp4Case(torch, nq, 64)),

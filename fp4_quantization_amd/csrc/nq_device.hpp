@@ -428,9 +428,10 @@ __device__ __forceinline__ float div6_rn(float amax)
 //    touch.  Lanes pass 32-bit byte offsets; a masked lane passes kOOB.  The
 //    hardware range check returns zeros for out-of-range loads and drops
 //    out-of-range stores, so masking (the row tail, rows past M) costs no
-//    branch.  Needs 16-byte aligned rows and d % 8 == 0 for 128-bit chunks.
+//    branch.  Needs d % 8 == 0 for 128-bit chunks; rows may start anywhere
+//    (unaligned access is enabled on this target).
 //  * RowIO<false>: plain per-element global accesses with explicit bounds
-//    checks, for odd d or misaligned pointers.
+//    checks, for d % 8 != 0 or gamma / beta off 16-byte boundaries.
 //
 // Cache policies (the aux bits of gfx950 buffer instructions: bit 0 sc0,
 // bit 1 nt, bit 4 sc1), chosen by measurement on MI355X for these streams:
@@ -601,16 +602,20 @@ struct RowIO<false, POLICY, T> {
 };
 
 // Plain global streaming accesses (non-temporal) for kernels that index a
-// whole tensor rather than per-wavefront rows.
+// whole tensor rather than per-wavefront rows.  The pointers may be
+// misaligned: the types say so (byte alignment), and the accesses stay one
+// 128-bit or 64-bit instruction (unaligned access is enabled on this target).
+typedef u32x4_t u32x4_any_t __attribute__((aligned(1)));
+typedef u32x2_t u32x2_any_t __attribute__((aligned(1)));
 __device__ __forceinline__ uint4 ld_global_stream16(const void* p)
 {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_any_t*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ void st_global_stream8(void* p, uint2 w)
 {
-    const u32x2_t v = {w.x, w.y};
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
+    const u32x2_any_t v = {w.x, w.y};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2_any_t*>(p));
 }
 
 // Hides a value's provenance from the optimizer (an empty register-only asm

@@ -32,7 +32,7 @@ constexpr int kGroup = 128;
 constexpr int kGroupBlock = 256;   // 16 groups per block per step
 constexpr int kGroupUnroll = 2;  // measured: 2 beats 1, 3, 4 and 8 at 32768 x 4096
 
-template <bool VEC, bool UE8M0, Fp8 F>
+template <bool UE8M0, Fp8 F>
 __global__ __launch_bounds__(kGroupBlock) void k_group_fp8(GroupArgs a)
 {
     const int lane16 = threadIdx.x & 15;
@@ -52,14 +52,7 @@ __global__ __launch_bounds__(kGroupBlock) void k_group_fp8(GroupArgs a)
         const int col = (int)c * kGroup + lane16 * 8;
         const uint16_t* px = a.x + (int64_t)m * a.ld_x + col;
         qoff[u] = (int64_t)m * a.ld_q + col;
-        if constexpr (VEC) {
-            w[u] = ld_global_stream16(px);
-        } else {
-            uint32_t h[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) h[k] = px[k];
-            w[u] = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
-        }
+        w[u] = ld_global_stream16(px);
     }
 
 #pragma unroll
@@ -77,25 +70,19 @@ __global__ __launch_bounds__(kGroupBlock) void k_group_fp8(GroupArgs a)
         for (int k = 0; k < 8; ++k) v[k] = v[k] * inv;
         const uint2 q = fp8x8<F>(v);
         if (ok[u]) {
-            uint8_t* pq = a.q + qoff[u];
-            if constexpr (VEC) {
-                st_global_stream8(pq, q);
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) pq[k] = (uint8_t)((k < 4 ? q.x : q.y) >> (8 * (k & 3)));
-            }
+            st_global_stream8(a.q + qoff[u], q);
             if (lane16 == 0) a.scale_out[base + (uint32_t)u * (kGroupBlock / 16)] = s;
         }
     }
 }
 
-template <bool VEC, bool UE8M0>
+template <bool UE8M0>
 static void launch_group(const GroupArgs& a, bool e5m2, hipStream_t s)
 {
     const uint32_t per_block = (kGroupBlock / 16) * kGroupUnroll;
     const uint32_t blocks = (a.total + per_block - 1) / per_block;
-    if (e5m2) hipLaunchKernelGGL((k_group_fp8<VEC, UE8M0, Fp8::E5M2>), dim3(blocks), dim3(kGroupBlock), 0, s, a);
-    else hipLaunchKernelGGL((k_group_fp8<VEC, UE8M0, Fp8::E4M3>), dim3(blocks), dim3(kGroupBlock), 0, s, a);
+    if (e5m2) hipLaunchKernelGGL((k_group_fp8<UE8M0, Fp8::E5M2>), dim3(blocks), dim3(kGroupBlock), 0, s, a);
+    else hipLaunchKernelGGL((k_group_fp8<UE8M0, Fp8::E4M3>), dim3(blocks), dim3(kGroupBlock), 0, s, a);
 }
 
 } // namespace nq
@@ -121,7 +108,8 @@ extern "C" nq_status nq_per_token_group_quant_fp8_ex(
     const Region out[] = {region(q_out, M, ld_q, K, 1), region(scale_out, 1, M * G, M * G, 4)};
     if (any_alias(in, out)) return NQ_ERR_ALIAS;
 
-    const bool vec = aligned(x, 16) && ld_x % 8 == 0 && aligned(q_out, 8) && ld_q % 8 == 0;
+    // Rows are whole 8-element chunks (K % 128 == 0); pointers and strides
+    // need no alignment (see vector_rows).
     GroupArgs a;
     a.x = x; a.q = q_out; a.scale_out = scale_out; a.ld_x = ld_x; a.ld_q = ld_q;
     a.groups_per_row = (uint32_t)G;
@@ -129,8 +117,7 @@ extern "C" nq_status nq_per_token_group_quant_fp8_ex(
     hipStream_t s = (hipStream_t)stream;
     const bool ue = scale_mode == NQ_SCALE_UE8M0;
     const bool e5 = (flags & NQ_FLAG_E5M2) != 0;
-    if (vec) ue ? launch_group<true, true>(a, e5, s) : launch_group<true, false>(a, e5, s);
-    else     ue ? launch_group<false, true>(a, e5, s) : launch_group<false, false>(a, e5, s);
+    ue ? launch_group<true>(a, e5, s) : launch_group<false>(a, e5, s);
     return hipGetLastError() == hipSuccess ? NQ_OK : NQ_ERR_LAUNCH;
 }
 

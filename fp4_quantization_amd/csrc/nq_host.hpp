@@ -31,6 +31,18 @@ inline bool overlaps(const Region& a, const Region& b)
 
 inline bool aligned(const void* p, uintptr_t bytes) { return ((uintptr_t)p % bytes) == 0; }
 
+// Rows take the 128-bit path when they hold whole 8-element chunks and the
+// shared vectors (gamma, beta; NULL for none) start on 16-byte boundaries:
+// they are staged through LDS in 16-byte pieces.  Row pointers and strides
+// need no alignment.  gfx950 code under the HSA runtime runs with unaligned
+// memory access enabled (the compiler itself lowers a byte-aligned 16-byte
+// copy to one 128-bit access for this target), so a row that starts off a
+// 16-byte boundary is still read and written 16 bytes at a time.
+inline bool vector_rows(int64_t d, const void* gamma, const void* beta = nullptr)
+{
+    return d % 8 == 0 && aligned(gamma, 16) && aligned(beta, 16);
+}
+
 // Bounds that keep every offset formed on the host or in a kernel in range:
 // a tensor's extent (M - 1) * ld + cols stays below 2^60 elements, so its
 // byte size (at most 4 bytes each) and every int64 row offset fit without

@@ -273,9 +273,7 @@ extern "C" nq_status nq_layernorm_quant_fp8_ex(
     const Region out[] = {region(q_out, M, ld_q, d, 1), region(scale ? nullptr : scale_out, 1, M, M, 4)};
     if (any_alias(in, out)) return NQ_ERR_ALIAS;
 
-    const bool vec = d % 8 == 0 && aligned(x, 16) && ld_x % 8 == 0 && aligned(gamma, 16) &&
-                     aligned(beta, 16) && aligned(q_out, 8) && ld_q % 8 == 0;
-    const RowShape shape = pick_row_shape(M, d, vec);
+    const RowShape shape = pick_row_shape(M, d, vector_rows(d, gamma, beta));
     if (shape.team == 0) return NQ_ERR_SHAPE;
 
     LnFp8Args a;

@@ -199,15 +199,7 @@ extern "C" nq_status nq_fused_add_rmsnorm_quant_fp8_ex(
                           region(norm_out, M, ld_n, d, 2)};
     if (any_alias(in, out, /*exact_in=*/1, /*exact_out=*/0)) return NQ_ERR_ALIAS;
 
-    // 128-bit path: whole chunks and 16-byte aligned bases and strides.
-    bool vec = d % 8 == 0 && aligned(x, 16) && ld_x % 8 == 0 && aligned(gamma, 16) &&
-               aligned(q_out, 8) && ld_q % 8 == 0;
-    if (residual_in)
-        vec = vec && aligned(residual_in, 16) && ld_r % 8 == 0 && aligned(residual_out, 16) &&
-              ld_ro % 8 == 0;
-    if (norm_out) vec = vec && aligned(norm_out, 16) && ld_n % 8 == 0;
-
-    const RowShape shape = pick_row_shape(M, d, vec);
+    const RowShape shape = pick_row_shape(M, d, vector_rows(d, gamma));
     if (shape.team == 0) return NQ_ERR_SHAPE;
 
     RmsFp8Launch L;

@@ -44,7 +44,6 @@ struct RmsFp4Args {
     bool gamma_bf16;
 };
 
-// VEC additionally needs 4-byte aligned packed-code rows (one dword per chunk).
 template <int TEAM, int CPL, bool VEC, bool STAGE, bool GB = false, bool RES = true,
           int BLOCK = row_block<TEAM, CPL, 1, VEC, STAGE>()>
 __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
@@ -181,14 +180,7 @@ extern "C" nq_status nq_rmsnorm_quant_nvfp4_ex(
                           region(block_scale, M, ld_sf, d / 16, 1), region(norm_out, M, ld_n, d, 2)};
     if (any_alias(in, out, /*exact_in=*/1, /*exact_out=*/0)) return NQ_ERR_ALIAS;
 
-    bool vec = aligned(x, 16) && ld_x % 8 == 0 && aligned(gamma, 16) && aligned(q_packed, 4) &&
-               ld_q % 4 == 0;
-    if (residual_in)
-        vec = vec && aligned(residual_in, 16) && ld_r % 8 == 0 && aligned(residual_out, 16) &&
-              ld_ro % 8 == 0;
-    if (norm_out) vec = vec && aligned(norm_out, 16) && ld_n % 8 == 0;
-
-    const RowShape shape = pick_row_shape(M, d, vec);
+    const RowShape shape = pick_row_shape(M, d, vector_rows(d, gamma));
     if (shape.team == 0) return NQ_ERR_SHAPE;
 
     RmsFp4Args a;

@@ -290,7 +290,7 @@ class SharedVectors {
 // Every (TEAM, CPL, VEC) shape that is compiled: teams of 16..1024 lanes
 // with at most 4 chunks (32 elements) per lane, so the fp32 row fits in
 // registers at full occupancy, plus the element-wise path (VEC = false) for
-// odd d or misaligned pointers.
+// d % 8 != 0 or gamma / beta off 16-byte boundaries.
 #define NQ_ROW_SHAPES(X)                                                                    \
     X(16, 1, true) X(16, 2, true) X(16, 3, true) X(16, 4, true)                             \
     X(32, 1, true) X(32, 2, true) X(32, 3, true) X(32, 4, true)                             \

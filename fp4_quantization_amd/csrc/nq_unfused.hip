@@ -196,12 +196,7 @@ extern "C" nq_status nq_fused_add_rmsnorm_bf16(
     const Region out_[] = {region(residual_out, M, ld_ro, d, 2), region(out, M, ld_o, d, 2)};
     if (any_alias(in, out_, /*exact_in=*/1, /*exact_out=*/0)) return NQ_ERR_ALIAS;
 
-    bool vec = d % 8 == 0 && aligned(x, 16) && ld_x % 8 == 0 && aligned(gamma, 16) && aligned(out, 16) &&
-               ld_o % 8 == 0;
-    if (residual_in)
-        vec = vec && aligned(residual_in, 16) && ld_r % 8 == 0 && aligned(residual_out, 16) &&
-              ld_ro % 8 == 0;
-    const RowShape shape = pick_row_shape(M, d, vec);
+    const RowShape shape = pick_row_shape(M, d, vector_rows(d, gamma));
     if (shape.team == 0) return NQ_ERR_SHAPE;
 
     RmsBf16Args a;
@@ -230,8 +225,7 @@ extern "C" nq_status nq_per_token_quant_fp8(
     const Region out[] = {region(q_out, M, ld_q, d, 1), region(static_scale ? nullptr : scale_out, 1, M, M, 4)};
     if (any_alias(in, out)) return NQ_ERR_ALIAS;
 
-    const bool vec = d % 8 == 0 && aligned(x, 16) && ld_x % 8 == 0 && aligned(q_out, 8) && ld_q % 8 == 0;
-    RowShape shape = pick_row_shape(M, d, vec);
+    RowShape shape = pick_row_shape(M, d, vector_rows(d, nullptr));
     if (shape.team == 0) return NQ_ERR_SHAPE;
     shape.stage = false;  // no shared vectors
 

@@ -32,8 +32,10 @@
  * Errors.  Arguments are checked on the host before anything is enqueued.  A
  *   non-zero status means nothing was launched, except NQ_ERR_LAUNCH, which
  *   reports a failed launch.  M == 0 is a no-op that returns NQ_OK.
- *   Misaligned pointers or strides are not errors: they select a slower
- *   element-wise path with identical results.
+ *   Pointers and strides need no alignment.  Rows are read and written 16
+ *   bytes at a time wherever d is a multiple of 8 and gamma / beta start on
+ *   16-byte boundaries, also when the rows themselves do not (a little slower
+ *   there); otherwise a slower element-wise path runs, with identical results.
  * Device-side preconditions (documented, not checked: checking would need a
  *   host synchronization): inputs and scales are finite; static scales are
  *   > 0 and the NVFP4 global scale is at least 2^-118; no row or group has a
@@ -80,8 +82,7 @@ typedef int nq_status;
                                    dynamic scales divide by 57344, e5m2() clamps to +-57344 */
 #define NQ_FLAG_GAMMA_BF16 4u   /* gamma (and beta) are bf16 [d] instead of fp32: each value is
                                    widened exactly, so the results equal those of the fp32 vector
-                                   holding the same values (16-byte alignment still selects the
-                                   vector path) */
+                                   holding the same values */
 
 /*
  * Fused (residual-add +) RMSNorm + per-token FP8 e4m3.

@@ -4,7 +4,7 @@ Every output is compared element by element with the oracle, the full
 workload sizes included (run whole on the GPU in the launch configuration
 the benchmark times; the oracle runs row-parallel on host threads).  Edge cases:
 M = 0 and 1, ragged d (not a multiple of the 8-element chunk, or of the
-lane count), misaligned pointers (element-wise path), row-strided column
+lane count), rows off 16-byte boundaries, row-strided column
 slices, in-place residual, all-zero and constant rows, saturating NVFP4
 global scales, and guard bands around every output.  Tolerances: see
 tests/parity.py.
@@ -183,8 +183,8 @@ def test_rms_fp8_empty(nq):
 
 
 def test_rms_fp8_misaligned_and_strided(nq, orc):
-    """A row stride of d+1 elements forces the element-wise path; the codes
-    must equal the 128-bit path's bit for bit."""
+    """A row stride of d+1 elements puts rows off 16-byte boundaries (still
+    the 128-bit path); the outputs must equal the aligned call's bit for bit."""
     note("rms fp8 misaligned/strided")
     M, d = 40, 2816
     w = W.rms_2816(M, seed=4)
@@ -197,14 +197,14 @@ def test_rms_fp8_misaligned_and_strided(nq, orc):
     s = torch.empty(M, dtype=torch.float32, device="cuda")
     nq.nq_fused_add_rmsnorm_quant_fp8(xd[:, :d], rd[:, :d], ro, to_dev_f32(w["gamma"]), w["eps"], None, q, s)
     torch.cuda.synchronize()
-    assert_bits_equal(host_u8(q), base["q"], "q element-wise vs vector path")
+    assert_bits_equal(host_u8(q), base["q"], "q unaligned vs aligned rows")
     assert_bits_equal(s.cpu().numpy().view(np.uint32), base["scale"].view(np.uint32), "scale")
     assert_bits_equal(host_u16(ro), base["residual_out"], "residual_out")
 
 
 def test_rms_fp8_schedules_bitwise_equal(nq):
-    """Few-row (wide team) and many-row (wave per row) shapes, and the
-    element-wise path, give identical bits on the same rows."""
+    """Few-row (wide team) and many-row (wave per row) shapes give identical
+    bits on the same rows."""
     note("rms fp8 schedule equality")
     w = W.rms_2816(2048, seed=5)
     big = run_rms_fp8(nq, w)
@@ -319,10 +319,10 @@ def test_rms_group_in_place_residual_less_strided_scales(nq, orc):
     compare_rms_group(orc, w2, got2, np.arange(64), ue8m0=True)
 
 
-def test_rms_group_zero_groups_and_element_path(nq, orc):
-    """All-zero groups give scale 0 and zero codes; a row stride of d+1
-    forces the element-wise path, which must match the 128-bit path."""
-    note("rms group fp8 zero groups / element-wise path")
+def test_rms_group_zero_groups_and_unaligned_rows(nq, orc):
+    """All-zero groups give scale 0 and zero codes; a row stride of d+1 puts
+    rows off 16-byte boundaries, which must match the aligned call."""
+    note("rms group fp8 zero groups / unaligned rows")
     M, d = 33, 2816
     w = W.rms_2816(M, seed=9)
     x, r = w["x"].copy(), w["residual"].copy()
@@ -341,7 +341,7 @@ def test_rms_group_zero_groups_and_element_path(nq, orc):
     s = torch.empty(M, d // 128, dtype=torch.float32, device="cuda")
     nq.nq_fused_add_rmsnorm_quant_fp8_group(xd[:, :d], rd[:, :d], ro, to_dev_f32(w["gamma"]), w["eps"], q, s)
     torch.cuda.synchronize()
-    assert_bits_equal(host_u8(q), base["q"], "q element-wise vs vector path")
+    assert_bits_equal(host_u8(q), base["q"], "q unaligned vs aligned rows")
     assert_bits_equal(s.cpu().numpy().view(np.uint32), base["scale"].view(np.uint32), "scale")
     assert_bits_equal(host_u16(ro), base["residual_out"], "residual_out")
 
@@ -519,14 +519,14 @@ def test_group_misaligned_and_zero_groups(nq, orc):
     x = w["x"].copy()
     x[1, 129:257] = 0                               # group 1 of the offset view
     q, s = run_group(nq, x[:, 1:].copy(), False)  # contiguous copy, aligned
-    xm = to_dev_bf16(x)[:, 1:]                      # 2-byte offset: element-wise path
+    xm = to_dev_bf16(x)[:, 1:]                      # 2-byte offset: rows off 16-byte boundaries
     q2 = torch.empty(5, 512, dtype=torch.uint8, device="cuda")
     s2 = torch.empty(20, dtype=torch.float32, device="cuda")
     nq.nq_per_token_group_quant_fp8(xm, q2, s2)
     torch.cuda.synchronize()
     o = orc.per_token_group_quant_fp8(x[:, 1:].copy(), 128)
     assert_bits_equal(q, o["q"], "codes")
-    assert_bits_equal(host_u8(q2), o["q"], "codes element-wise path")
+    assert_bits_equal(host_u8(q2), o["q"], "codes, unaligned rows")
     assert_bits_equal(s2.cpu().numpy().view(np.uint32), o["scale"].ravel().view(np.uint32), "scales")
     assert s[1, 1] == 0
 

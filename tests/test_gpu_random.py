@@ -3,7 +3,8 @@
 Each case draws, from its own seed, a combination that hand-picked cases may
 miss: the row length (ragged, under one chunk, aligned, up to NQ_MAX_D), the
 row count, padded leading dimensions, a pointer one element off 16-byte
-alignment (the element-wise path), fresh / in-place / absent residual,
+alignment (rows off 16-byte boundaries), a gamma one element off a 16-byte
+boundary (the element-wise path), fresh / in-place / absent residual,
 static or dynamic scale, e4m3 or e5m2, fp32 or bf16 gamma (and beta),
 norm_out, UE8M0, the bf16-sourced epilogues and strided scale rows.  Every
 output row is compared with the oracle under the tolerances of
@@ -48,12 +49,30 @@ def _width(rng, align):
     return max(1, min(n, hi)) * align
 
 
-def _vec(rng, v, allow_bf16=True):
-    """(fp32 values the oracle uses, device tensor, is_bf16)."""
+def _vec(rng, v, allow_bf16=True, off=False):
+    """(fp32 values the oracle uses, device tensor, is_bf16); with `off` the
+    device copy starts one element past a 16-byte boundary (the element-wise
+    path)."""
     if allow_bf16 and rng.random() < 0.3:
         bits = W.to_bf16_bits(np.asarray(v, np.float32))
-        return W.bf16_bits_to_f32(bits), to_dev_bf16(bits), True
-    return np.asarray(v, np.float32), to_dev_f32(v), False
+        vals, dev, b16 = W.bf16_bits_to_f32(bits), to_dev_bf16(bits), True
+    else:
+        vals, dev, b16 = np.asarray(v, np.float32), to_dev_f32(v), False
+    return vals, (_off_copy(dev) if off else dev), b16
+
+
+def _off_copy(dev):
+    """A contiguous copy of a device vector starting one element past a
+    16-byte boundary."""
+    buf = torch.empty(dev.numel() + 1, dtype=dev.dtype, device="cuda")
+    buf[1:].copy_(dev)
+    return buf[1:]
+
+
+def _gamma_off(kind, seed):
+    """Whether this case's gamma starts off a 16-byte boundary (drawn from a
+    generator of its own, so the other draws of the case do not change)."""
+    return bool(_rng(100 + kind, seed).random() < 0.3)
 
 
 def _input(rng, x_bits, d):
@@ -89,12 +108,12 @@ def test_random_rmsnorm_fp8(nq, orc, seed):
     ro_buf = None
     if mode == "fresh":
         ro_buf, ro = guarded_bf16(M, d)
-    g32, g, gb = _vec(rng, w["gamma"])
+    g32, g, gb = _vec(rng, w["gamma"], off=_gamma_off(1, seed))
     static = float(rng.choice([0.01, 0.05, 1.0])) if rng.random() < 0.3 else None
     fmt = "e5m2" if rng.random() < 0.3 else "e4m3"
     want_n = rng.random() < 0.3
     note(f"random rms fp8 seed={seed} M={M} d={d} {lay} residual={mode} static={static} {fmt} "
-         f"gamma_bf16={gb} norm_out={want_n}")
+         f"gamma_bf16={gb} gamma_off={g.data_ptr() % 16 != 0} norm_out={want_n}")
     q_buf, q = guarded_u8(M, d)
     s_buf, s = guarded_f32(M)
     n_buf, n = guarded_bf16(M, d) if want_n else (None, None)
@@ -133,9 +152,13 @@ def test_random_layernorm_fp8(nq, orc, seed):
     else:
         g32, b32 = w["gamma"], w["beta"]
         g, b = to_dev_f32(g32), to_dev_f32(b32)
+    goff = _gamma_off(2, seed)
+    if goff:  # both vectors one element past a 16-byte boundary
+        g, b = (_off_copy(t) for t in (g, b))
     static = float(rng.choice([0.01, 0.05, 1.0])) if rng.random() < 0.5 else None
     fmt = "e5m2" if rng.random() < 0.3 else "e4m3"
-    note(f"random layernorm seed={seed} M={M} d={d} {lay} static={static} {fmt} bf16_vectors={bf}")
+    note(f"random layernorm seed={seed} M={M} d={d} {lay} static={static} {fmt} bf16_vectors={bf} "
+         f"vectors_off={goff}")
     q_buf, q = guarded_u8(M, d)
     s_buf, s = guarded_f32(M)
     nq.nq_layernorm_quant_fp8_ex(x, g, b, w["eps"], to_dev_f32([static]) if static else None,
@@ -160,12 +183,12 @@ def test_random_rmsnorm_nvfp4(nq, orc, seed):
     mode, r_np, r, ro = _residual(rng, w, d)
     if mode == "fresh":
         ro = torch.empty(M, d, dtype=torch.bfloat16, device="cuda")
-    g32, g, gb = _vec(rng, w["gamma"])
+    g32, g, gb = _vec(rng, w["gamma"], off=_gamma_off(3, seed))
     mode_b = rng.random() < 0.3
     want_n = rng.random() < 0.3
     sg = calibrated_sg(orc, dict(w, x=x_np, residual=r_np, gamma=g32)) * float(rng.choice([1.0, 1.0, 0.25]))
     note(f"random nvfp4 seed={seed} M={M} d={d} {lay} residual={mode} bf16_source={mode_b} "
-         f"gamma_bf16={gb} norm_out={want_n}")
+         f"gamma_bf16={gb} gamma_off={g.data_ptr() % 16 != 0} norm_out={want_n}")
     q_buf, q = guarded_u8(M, d // 2)
     sf_buf, sf = guarded_u8(M, d // 16)
     n = torch.empty(M, d, dtype=torch.bfloat16, device="cuda") if want_n else None
@@ -196,14 +219,14 @@ def test_random_rmsnorm_fp8_group(nq, orc, seed):
     mode, r_np, r, ro = _residual(rng, w, d)
     if mode == "fresh":
         ro = torch.empty(M, d, dtype=torch.bfloat16, device="cuda")
-    g32, g, gb = _vec(rng, w["gamma"])
+    g32, g, gb = _vec(rng, w["gamma"], off=_gamma_off(4, seed))
     ue8m0 = rng.random() < 0.5
     src = rng.random() < 0.3
     fmt = "e5m2" if rng.random() < 0.3 else "e4m3"
     want_n = rng.random() < 0.3
     ld_s = G + int(rng.choice([0, 0, 3]))
     note(f"random rms group seed={seed} M={M} d={d} {lay} residual={mode} ue8m0={ue8m0} bf16_source={src} "
-         f"{fmt} gamma_bf16={gb} norm_out={want_n} ld_s={ld_s}")
+         f"{fmt} gamma_bf16={gb} gamma_off={g.data_ptr() % 16 != 0} norm_out={want_n} ld_s={ld_s}")
     q_buf, q = guarded_u8(M, d)
     s_buf = torch.full((M * ld_s + 16,), float("nan"), dtype=torch.float32, device="cuda")
     s = s_buf[: M * ld_s].view(M, ld_s)[:, :G]
