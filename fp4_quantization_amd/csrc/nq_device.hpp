@@ -430,8 +430,9 @@ __device__ __forceinline__ float div6_rn(float amax)
 //    out-of-range stores, so masking (the row tail, rows past M) costs no
 //    branch.  Needs d % 8 == 0 for 128-bit chunks; rows may start anywhere
 //    (unaligned access is enabled on this target).
-//  * RowIO<false>: plain per-element global accesses with explicit bounds
-//    checks, for d % 8 != 0 or gamma / beta off 16-byte boundaries.
+//  * RowIO<false>: the same resource, for d % 8 != 0 or gamma / beta off
+//    16-byte boundaries: 128-bit accesses inside the row, element by element
+//    across its end (shapes with one row per wavefront only).
 //
 // Cache policies (the aux bits of gfx950 buffer instructions: bit 0 sc0,
 // bit 1 nt, bit 4 sc1), chosen by measurement on MI355X for these streams:
@@ -528,77 +529,84 @@ struct RowIO<true, POLICY, T> {
 };
 
 template <int POLICY, typename T>
-struct RowIO<false, POLICY, T> {
-    T* row;
-    bool ok;
-    int cols;
-
+struct RowIO<false, POLICY, T> : RowIO<true, POLICY, T> {
+    // For rows whose length is not a multiple of 8 elements, and shared
+    // vectors off 16-byte boundaries: an access that lies wholly inside the
+    // row is the 128-bit path's; one that crosses the row's end goes element
+    // by element.  Every shape on this path gives each wavefront one row, so
+    // the resource ends at the row's last element and its range check drops
+    // the elements past it (loads read zeros there).
+    using Base = RowIO<true, POLICY, T>;
     RowIO() = default;
     __device__ __forceinline__ RowIO(const T* base, int64_t ld, const RowMap& m, int ncols)
-        : row(const_cast<T*>(base) + (m.ok ? m.row : 0) * ld), ok(m.ok && base != nullptr), cols(ncols) {}
+        : Base(base, ld, m, ncols) {}
 
-    // element-wise: n bytes from element i, each element bounds-checked
     template <int N>
-    __device__ __forceinline__ void load_bytes(int i, bool live, uint8_t (&b)[N]) const
+    __device__ __forceinline__ bool inside(int i) const { return i + N / (int)sizeof(T) <= this->cols; }
+    __device__ __forceinline__ uint32_t elem(int i, bool live) const
     {
-        constexpr int E = N / (int)sizeof(T);
+        const int o = (int)this->off(i, live);
+        if constexpr (sizeof(T) == 1) return __builtin_amdgcn_raw_buffer_load_b8(this->rsrc, o, 0, POLICY);
+        else if constexpr (sizeof(T) == 2) return __builtin_amdgcn_raw_buffer_load_b16(this->rsrc, o, 0, POLICY);
+        else return __builtin_amdgcn_raw_buffer_load_b32(this->rsrc, o, 0, POLICY);
+    }
+    __device__ __forceinline__ void put(int i, bool live, uint32_t v) const
+    {
+        const int o = (int)this->off(i, live);
+        if constexpr (sizeof(T) == 1) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, this->rsrc, o, 0, POLICY);
+        else if constexpr (sizeof(T) == 2) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, this->rsrc, o, 0, POLICY);
+        else __builtin_amdgcn_raw_buffer_store_b32(v, this->rsrc, o, 0, POLICY);
+    }
+    // N bytes from element i, one element per access
+    template <int N>
+    __device__ __forceinline__ void load_words(int i, bool live, uint32_t (&w)[N / 4]) const
+    {
+        constexpr int E = N / (int)sizeof(T), PER = 4 / (int)sizeof(T);
 #pragma unroll
-        for (int k = 0; k < E; ++k) {
-            T v = (ok && live && i + k < cols) ? row[i + k] : T(0);
-            __builtin_memcpy(&b[k * sizeof(T)], &v, sizeof(T));
-        }
+        for (int q = 0; q < N / 4; ++q) w[q] = 0u;
+#pragma unroll
+        for (int k = 0; k < E; ++k) w[k / PER] |= elem(i + k, live) << (8 * sizeof(T) * (k % PER));
     }
     template <int N>
-    __device__ __forceinline__ void store_bytes(int i, bool live, const uint8_t (&b)[N]) const
+    __device__ __forceinline__ void store_words(int i, bool live, const uint32_t (&w)[N / 4]) const
     {
-        constexpr int E = N / (int)sizeof(T);
+        constexpr int E = N / (int)sizeof(T), PER = 4 / (int)sizeof(T);
 #pragma unroll
-        for (int k = 0; k < E; ++k) {
-            if (ok && live && i + k < cols) {
-                T v;
-                __builtin_memcpy(&v, &b[k * sizeof(T)], sizeof(T));
-                row[i + k] = v;
-            }
-        }
+        for (int k = 0; k < E; ++k) put(i + k, live, w[k / PER] >> (8 * sizeof(T) * (k % PER)));
     }
     __device__ __forceinline__ uint2 load8(int i, bool live) const
     {
-        uint8_t b[8];
-        load_bytes<8>(i, live, b);
-        uint2 w;
-        __builtin_memcpy(&w, b, 8);
-        return w;
+        if (inside<8>(i)) return Base::load8(i, live);
+        uint32_t w[2];
+        load_words<8>(i, live, w);
+        return make_uint2(w[0], w[1]);
     }
     __device__ __forceinline__ uint4 load16(int i, bool live) const
     {
-        uint8_t b[16];
-        load_bytes<16>(i, live, b);
-        uint4 w;
-        __builtin_memcpy(&w, b, 16);
-        return w;
+        if (inside<16>(i)) return Base::load16(i, live);
+        uint32_t w[4];
+        load_words<16>(i, live, w);
+        return make_uint4(w[0], w[1], w[2], w[3]);
     }
-    __device__ __forceinline__ void store16(int i, bool live, uint4 w) const
+    __device__ __forceinline__ void store16(int i, bool live, uint4 v) const
     {
-        uint8_t b[16];
-        __builtin_memcpy(b, &w, 16);
-        store_bytes<16>(i, live, b);
+        if (inside<16>(i)) return Base::store16(i, live, v);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        store_words<16>(i, live, w);
     }
-    __device__ __forceinline__ void store8(int i, bool live, uint2 w) const
+    __device__ __forceinline__ void store8(int i, bool live, uint2 v) const
     {
-        uint8_t b[8];
-        __builtin_memcpy(b, &w, 8);
-        store_bytes<8>(i, live, b);
+        if (inside<8>(i)) return Base::store8(i, live, v);
+        const uint32_t w[2] = {v.x, v.y};
+        store_words<8>(i, live, w);
     }
-    __device__ __forceinline__ void store4(int i, bool live, uint32_t w) const
+    __device__ __forceinline__ void store4(int i, bool live, uint32_t v) const
     {
-        uint8_t b[4];
-        __builtin_memcpy(b, &w, 4);
-        store_bytes<4>(i, live, b);
+        if (inside<4>(i)) return Base::store4(i, live, v);
+        const uint32_t w[1] = {v};
+        store_words<4>(i, live, w);
     }
-    __device__ __forceinline__ void store1(int i, bool live, uint32_t w) const
-    {
-        if (ok && live && i < cols) row[i] = (T)w;
-    }
+    __device__ __forceinline__ void store1(int i, bool live, uint32_t v) const { put(i, live, v); }
 };
 
 // Plain global streaming accesses (non-temporal) for kernels that index a

@@ -371,6 +371,9 @@ inline bool launch_rows(const Args& a, int64_t M, hipStream_t stream)
 template <template <int, int, bool> class K, int T, int C, bool V, typename Args>
 inline bool launch_shape(bool stage, const Args& a, int64_t M, hipStream_t stream)
 {
+    // The element-wise row access relies on the range check of a resource
+    // that ends at the row's end: one row per wavefront.
+    static_assert(V || T >= kWave, "element-wise shapes give each wavefront one row");
     if constexpr (V) {
         if (stage) return launch_rows<K<T, C, V>, T, true>(a, M, stream);
     }
