@@ -114,8 +114,8 @@ __device__ __forceinline__ RowMap vector_map()
 // LayerNorm's fp32 vectors are loaded straight into LDS, buffer_load ...
 // lds, see kDma).
 // Staged only while the LDS of the blocks that fill a compute unit (32
-// wavefronts) stays within its 160 KB; otherwise, and on the element-wise
-// path, each lane loads its chunks from memory.
+// wavefronts) stays within its 160 KB; otherwise each lane loads its chunks
+// from memory.
 constexpr int kLanesPerCU = 2048;        // 8 wavefronts per SIMD x 4 SIMDs x 64
 constexpr int kLdsPerCU = 160 * 1024;
 
@@ -130,7 +130,7 @@ constexpr bool stages_vectors(int team, int cpl, int nv, int block)
 template <int TEAM, int CPL, int NV, bool VEC, bool STAGE>
 constexpr int row_block()
 {
-    if (STAGE && VEC && NV > 0)
+    if (STAGE && NV > 0)
         for (int b = default_block<TEAM>(); b <= 1024; b *= 2)
             if (stages_vectors(TEAM, CPL, NV, b)) return b;
     return default_block<TEAM>();
@@ -141,7 +141,7 @@ class SharedVectors {
   public:
     using S = TeamShape<TEAM, BLOCK>;
     static constexpr int kSlots = TEAM * CPL * 2;  // 16-byte fp32 slots covering one row's chunks
-    static constexpr bool kStaged = STAGE && VEC && stages_vectors(TEAM, CPL, NV, BLOCK);
+    static constexpr bool kStaged = STAGE && stages_vectors(TEAM, CPL, NV, BLOCK);
     static constexpr int kPer = kStaged ? (kSlots + S::kBlock - 1) / S::kBlock : 1;
     // Unstaged instances with at most 2 chunks per lane (the few-rows
     // shapes, where latency rules) load each lane's chunks with the row
@@ -154,7 +154,7 @@ class SharedVectors {
     // within noise (and 12 more vector instructions per wavefront), the
     // RMSNorm kernels 0.3-1.8 % slower, so only the dynamic LayerNorm asks
     // for it.
-    static constexpr bool kDma = DMA && kStaged && !BF16;
+    static constexpr bool kDma = DMA && kStaged && !BF16 && VEC;  // whole 16-byte slots only
     typedef uint4 Lds[kStaged ? NV : 1][kStaged ? kSlots : 1];
     static_assert(!kStaged || kSlots * 16 * NV <= 64 * 1024, "staged vectors fit one block's LDS");
 
@@ -299,7 +299,7 @@ class SharedVectors {
     X(256, 1, true) X(256, 2, true) X(256, 3, true) X(256, 4, true)                         \
     X(512, 1, true) X(512, 2, true) X(512, 3, true) X(512, 4, true)                         \
     X(1024, 1, true) X(1024, 2, true) X(1024, 3, true) X(1024, 4, true)                     \
-    X(64, 4, false) X(256, 4, false) X(1024, 4, false)
+    X(64, 4, false) X(128, 4, false) X(256, 4, false) X(512, 4, false) X(1024, 4, false)
 
 struct RowShape {
     int team = 0, cpl = 0;
@@ -337,9 +337,12 @@ inline RowShape narrowest_team(int64_t d, int max_cpl)
 inline RowShape pick_row_shape(int64_t M, int64_t d, bool vec)
 {
     if (!vec) {
+        // element-wise: whole wavefronts per row (the narrowest that holds
+        // the row in 4 chunks per lane), staged vectors for many rows
         RowShape s;
         s.cpl = 4;
-        s.team = d <= 2048 ? 64 : d <= 8192 ? 256 : 1024;
+        for (s.team = 64; s.team < 1024 && (int64_t)s.team * 32 < d; s.team *= 2) {}
+        s.stage = M * (s.team / 64) >= kFewRowsWaves;
         return s;
     }
     RowShape s = narrowest_team(d, 4);
@@ -374,9 +377,7 @@ inline bool launch_shape(bool stage, const Args& a, int64_t M, hipStream_t strea
     // The element-wise row access relies on the range check of a resource
     // that ends at the row's end: one row per wavefront.
     static_assert(V || T >= kWave, "element-wise shapes give each wavefront one row");
-    if constexpr (V) {
-        if (stage) return launch_rows<K<T, C, V>, T, true>(a, M, stream);
-    }
+    if (stage) return launch_rows<K<T, C, V>, T, true>(a, M, stream);
     return launch_rows<K<T, C, V>, T, false>(a, M, stream);
 }
 

@@ -35,8 +35,8 @@
  *   Pointers and strides need no alignment.  Rows are read and written 16
  *   bytes at a time wherever d is a multiple of 8 and gamma / beta start on
  *   16-byte boundaries, also when the rows themselves do not (up to about a
- *   fifth slower there); otherwise an element-wise path runs (2.5 to 4.5
- *   times slower), with identical results.
+ *   fifth slower there); otherwise an element-wise path runs (about 1.5 to
+ *   1.8 times slower), with identical results.
  * Device-side preconditions (documented, not checked: checking would need a
  *   host synchronization): inputs and scales are finite; static scales are
  *   > 0 and the NVFP4 global scale is at least 2^-118; no row or group has a
