@@ -103,10 +103,12 @@ LAYOUTS = ("aligned", "rows", "gamma")
 
 
 @pytest.mark.parametrize("M", [3, 600])
-def test_rmsnorm_fp8_alignment(nq, M):
-    note(f"alignment rms fp8 M={M}")
-    d = 2816
-    w = W.rms_2816(M, seed=31 + M)
+@pytest.mark.parametrize("d", [2816, 256, 64])
+def test_rmsnorm_fp8_alignment(nq, M, d):
+    """d = 256 and 64 take teams narrower than a wavefront (several rows per
+    buffer resource)."""
+    note(f"alignment rms fp8 M={M} d={d}")
+    w = W.rms_2816(M, seed=31 + M) if d == 2816 else W.rms_rows(M, d, 2, 20.0, seed=31 + M)
     g = to_dev_f32(w["gamma"])
     spec = {"ro": (M, d, torch.bfloat16), "q": (M, d, torch.uint8), "n": (M, d, torch.bfloat16)}
     res = {}
@@ -166,9 +168,9 @@ def test_rmsnorm_nvfp4_alignment(nq, orc, M):
 
 @pytest.mark.parametrize("M", [3, 600])
 @pytest.mark.parametrize("dynamic", [False, True])
-def test_layernorm_alignment(nq, M, dynamic):
-    note(f"alignment layernorm M={M} dynamic={dynamic}")
-    d = 4096
+@pytest.mark.parametrize("d", [4096, 256])
+def test_layernorm_alignment(nq, M, dynamic, d):
+    note(f"alignment layernorm M={M} dynamic={dynamic} d={d}")
     w = W.layernorm_rows(M=M, d=d, seed=61 + M)
     g, b = to_dev_f32(w["gamma"]), to_dev_f32(w["beta"])
     sc = None if dynamic else to_dev_f32([0.05])
