@@ -14,11 +14,13 @@ that no step finds its data in the 256 MB last-level cache.
 
 Prints ONE JSON line.  `value` is whole-job throughput in GB/s of
 algorithmic bytes (inputs + residual write + fp8 output + scales, gamma
-once; see fp4_quantization_amd/traffic.py): the K timed steps are captured
-in one hipGraph and replayed once, timed with HIP events on the replay
-stream; each step is one launch, so `roofline.achieved` (bytes over the
-kernel's average launch duration) is the same figure.  `eager_ms_per_step`
-times the same K steps as plain launches, `m1_us_per_call` is the
+once; see fp4_quantization_amd/traffic.py): the K timed steps are K
+back-to-back launches on one stream, timed with HIP events on that stream;
+each step is one launch, so `roofline.achieved` (bytes over the kernel's
+average launch duration) is the same figure.  `graph_ms_per_step` times
+the same K steps captured in one hipGraph and replayed once (a replay
+carries the graph's own start-up, measured at ~20 us on MI355X: about 1 us
+per step at K = 20, nothing at K = 200), `m1_us_per_call` is the
 graph-amortized time of one M=1 call, and `copy_reference` is a plain
 128-bit copy of the same byte count on the same GPU (a same-box ceiling for
 this read/write mix; `value_over_copy` above 1 means the kernel moves its
@@ -565,8 +567,10 @@ def summarize_trace(stats_csv, out_md, command):
     """Text summary of a rocprofv3 --kernel-trace --stats run of the default
     bench command: the per-kernel statistics, and the main kernel's average
     over the timed window alone (its dispatches in start order: the warmup
-    launches, then the timed graph replay, then the eager reference run),
-    taken from the per-dispatch trace written next to the statistics."""
+    launches, then the timed launches, then the graph reference replay),
+    taken from the per-dispatch trace written next to the statistics, with
+    the idle time between consecutive timed dispatches (negative: the next
+    kernel started before the previous one ended)."""
     rows = _csv(stats_csv)
     lines = [f"# rocprofv3 kernel trace: fused add+RMSNorm+FP8, M=8192, d=2816", "",
              f"Command (repository root): `{command}`", "",
@@ -593,9 +597,14 @@ def summarize_trace(stats_csv, out_md, command):
             if len(disp) >= w + 2 * k:
                 dur = [(e - s0) / 1e3 for s0, e in disp]
                 timed = sum(dur[w:w + k]) / k
-                lines += [f"- timed window (dispatches {w}..{w + k - 1}, the graph replay): {rate(timed)}",
+                gaps = [(disp[i + 1][0] - disp[i][1]) / 1e3 for i in range(w, w + k - 1)]
+                span = (disp[w + k - 1][1] - disp[w][0]) / 1e3 / k
+                lines += [f"- timed window (dispatches {w}..{w + k - 1}, back-to-back launches): {rate(timed)}",
+                          f"- the same window from the first start to the last end, per dispatch: {rate(span)}",
+                          f"- idle time between consecutive timed dispatches: mean {np.mean(gaps):.2f} us, "
+                          f"min {min(gaps):.2f}, max {max(gaps):.2f}",
                           f"- warmup dispatches 0..{w - 1}: {rate(sum(dur[:w]) / w)}",
-                          f"- eager reference run ({w + k}..{w + 2 * k - 1}): {rate(sum(dur[w + k:w + 2 * k]) / k)}"]
+                          f"- graph reference replay ({w + k}..{w + 2 * k - 1}): {rate(sum(dur[w + k:w + 2 * k]) / k)}"]
         lines += ["", "The many short calls of the other shape are the M=1 latency measurements; "
                   "`k_diag_copy` is the same-byte-count copy behind `copy_reference` (warmup replays "
                   "included), and the torch kernels fill its buffers."]
@@ -1133,15 +1142,15 @@ def main():
         return
 
     case = RmsFp8Case(torch, nq, 8192, 2816)
-    total_ms = time_steps_graph(torch, case, args.steps, args.warmup)
+    total_ms, _ = time_steps(torch, case, args.steps, args.warmup)
     ms_per_step = total_ms / args.steps
     value = case.bytes / (ms_per_step * 1e-3) / 1e9
-    # the same kernel's average launch duration in that timed replay
+    # the same kernel's average launch duration over the timed launches
     achieved = value
-    # for reference: the same K steps as plain back-to-back launches
-    eager_ms, _ = time_steps(torch, case, args.steps, 0)
-    log(f"main: {args.steps} steps in one graph replay: {total_ms:.3f} ms, {ms_per_step * 1e3:.2f} us/step; "
-        f"as plain launches {eager_ms / args.steps * 1e3:.2f} us/step")
+    # for reference: the same K steps captured in one graph, replayed once
+    graph_ms = time_steps_graph(torch, case, args.steps, 0)
+    log(f"main: {args.steps} back-to-back launches: {total_ms:.3f} ms, {ms_per_step * 1e3:.2f} us/step; "
+        f"in one graph replay {graph_ms / args.steps * 1e3:.2f} us/step")
     del case
     torch.cuda.empty_cache()
 
@@ -1173,7 +1182,7 @@ def main():
                    "M": 8192, "d": 2816, "bytes_per_step": case_bytes_8192(),
                    "buffer_sets": 4, "parallelism": "single GPU"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "eager_ms_per_step": round(eager_ms / args.steps, 6),
+        "graph_ms_per_step": round(graph_ms / args.steps, 6),
         "m1_us_per_call": round(m1_us, 3),
         "m1_us_per_launch_events": round(m1_ev_ms * 1e3, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

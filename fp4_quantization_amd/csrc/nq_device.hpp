@@ -679,19 +679,28 @@ __device__ __forceinline__ double sumsq_chunk(uint4 w)
 // nor flushed or subnormal products can have touched it; a lane holding a
 // chunk outside that range sums all its chunks exactly in binary64 instead
 // (a branch no wavefront takes on ordinary data).  Within the range the
-// binary32 sum is the exact one to within its few roundings (2^-24 relative
-// each; a sum of squares has no cancellation, and a plain sum of bf16
-// values only rounds when they span more than 2^16 in magnitude).
+// binary32 sum is the exact one to within its few roundings: 2^-24
+// relative each for the fused multiply-adds of a sum of squares (which has
+// no cancellation); for the packed dot products of a plain sum, each step
+// lands within 1.5 units in the last place of the largest magnitude among
+// its terms and its result -- the instruction truncates the terms it
+// aligns, so it is not always the nearest binary32 -- and is exact while
+// every term's bits lie within the 24 bits below the largest one's leading
+// bit (test_sum_bf16x2_error_bound).
+
+// lo + hi + acc for the two bf16 halves of a packed word: one packed bf16
+// dot product with (1, 1).
+__device__ __forceinline__ float sum2_bf16(uint32_t w, float acc)
+{
+    const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
 
 // Sum of the 8 bf16 values of a packed chunk: four packed bf16 dot products
 // with (1, 1).
 __device__ __forceinline__ float sum_chunk_f32(uint4 w)
 {
-    const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
-    float p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), one, 0.0f, false);
-    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), one, p, false);
-    p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), one, p, false);
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), one, p, false);
+    return sum2_bf16(w.w, sum2_bf16(w.z, sum2_bf16(w.y, sum2_bf16(w.x, 0.0f))));
 }
 // Whether a chunk's binary32 plain sum can be trusted: tiny (or cancelled),
 // huge and non-finite sums are recomputed.

@@ -78,6 +78,11 @@ __global__ __launch_bounds__(256) void k_diag_arith(int kind, const void* a, con
         if (live) static_cast<double*>(out)[i] = r;
         break;
     }
+    case NQ_ARITH_SUM_BF16X2: {
+        const float r = sum2_bf16(static_cast<const uint32_t*>(a)[k], static_cast<const float*>(b)[k]);
+        if (live) static_cast<float*>(out)[i] = r;
+        break;
+    }
     default: {  // NQ_ARITH_DIV6
         const float r = div6_rn(static_cast<const float*>(a)[k]);
         if (live) static_cast<float*>(out)[i] = r;
@@ -152,10 +157,10 @@ extern "C" nq_status nq_diag_codec(int32_t kind, const float* in, void* out, int
 extern "C" nq_status nq_diag_arith(int32_t kind, const void* a, const void* b, void* out, int64_t n,
                                    void* stream)
 {
-    if (kind < NQ_ARITH_RCP || kind > NQ_ARITH_DIV6) return NQ_ERR_ARG;
+    if (kind < NQ_ARITH_RCP || kind > NQ_ARITH_SUM_BF16X2) return NQ_ERR_ARG;
     if (n < 0 || n > (int64_t(1) << 36)) return NQ_ERR_SHAPE;
     if (n == 0) return NQ_OK;
-    const bool two = kind == NQ_ARITH_DIV || kind == NQ_ARITH_DIV_LEN;
+    const bool two = kind == NQ_ARITH_DIV || kind == NQ_ARITH_DIV_LEN || kind == NQ_ARITH_SUM_BF16X2;
     if (!a || !out || (two && !b)) return NQ_ERR_NULL;
     const int64_t asz = kind == NQ_ARITH_DIV_LEN ? 8 : 4;
     const Region rin[] = {region(a, 1, n, n, asz), region(two ? b : nullptr, 1, n, n, 4)};

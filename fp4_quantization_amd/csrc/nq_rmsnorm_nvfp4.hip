@@ -125,8 +125,10 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_nvfp4(RmsFp4Args a)
         float v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = y[k] * mult;
-        qio.store4(e / 2, col_live<TEAM, VEC>(e, d), e2m1x8(v));
-        sfio.store1(e / 16, col_live<TEAM, VEC>(e, d) && (t1 & 1) == 0, sf);
+        // Offsets of codes (e / 2) and block scale (e / 16) as a lane part
+        // plus a per-chunk constant the store instruction carries itself.
+        qio.store4(t1 * 4 + j * TEAM * 4, col_live<TEAM, VEC>(e, d), e2m1x8(v));
+        sfio.store1((t1 >> 1) + j * (TEAM / 2), col_live<TEAM, VEC>(e, d) && (t1 & 1) == 0, sf);
     }
 }
 

@@ -254,7 +254,7 @@ class SharedVectors {
                 g[6] = __uint_as_float(b.z); g[7] = __uint_as_float(b.w);
             }
         } else if constexpr (kStaged) {
-            const uint4 a = lds[v][e / 4], b = lds[v][e / 4 + 1];
+            const uint4 a = lds[v][e >> 2], b = lds[v][(e >> 2) + 1];  // e >= 0
             g[0] = __uint_as_float(a.x); g[1] = __uint_as_float(a.y);
             g[2] = __uint_as_float(a.z); g[3] = __uint_as_float(a.w);
             g[4] = __uint_as_float(b.x); g[5] = __uint_as_float(b.y);
@@ -275,7 +275,7 @@ class SharedVectors {
     __device__ __forceinline__ void half(const Lds& lds, int v, int e, int h, float g[4]) const
     {
         static_assert(kStaged, "half chunks come from the staged copy");
-        const uint4 a = lds[v][e / 4 + h];
+        const uint4 a = lds[v][(e >> 2) + h];  // e >= 0
         g[0] = __uint_as_float(a.x); g[1] = __uint_as_float(a.y);
         g[2] = __uint_as_float(a.z); g[3] = __uint_as_float(a.w);
     }

@@ -80,6 +80,7 @@ NQ_ARITH_RSQRT = 1
 NQ_ARITH_DIV = 2
 NQ_ARITH_DIV_LEN = 3
 NQ_ARITH_DIV6 = 4
+NQ_ARITH_SUM_BF16X2 = 5
 NQ_MAX_D = 32768  # widest row of the row kernels (include/nq.h)
 
 
@@ -376,12 +377,13 @@ def nq_diag_codec(kind: int, x: torch.Tensor, out: torch.Tensor, stream=None):
     _check(st, "nq_diag_codec")
 
 
-_ARITH_TYPES = {  # kind -> (a dtype, b dtype or None); out has a's dtype
-    NQ_ARITH_RCP: (torch.float32, None),
-    NQ_ARITH_RSQRT: (torch.float32, None),
-    NQ_ARITH_DIV: (torch.float32, torch.float32),
-    NQ_ARITH_DIV_LEN: (torch.float64, torch.int32),
-    NQ_ARITH_DIV6: (torch.float32, None),
+_ARITH_TYPES = {  # kind -> (a dtype, b dtype or None, out dtype)
+    NQ_ARITH_RCP: (torch.float32, None, torch.float32),
+    NQ_ARITH_RSQRT: (torch.float32, None, torch.float32),
+    NQ_ARITH_DIV: (torch.float32, torch.float32, torch.float32),
+    NQ_ARITH_DIV_LEN: (torch.float64, torch.int32, torch.float64),
+    NQ_ARITH_DIV6: (torch.float32, None, torch.float32),
+    NQ_ARITH_SUM_BF16X2: (torch.int32, torch.float32, torch.float32),
 }
 
 
@@ -389,13 +391,13 @@ def nq_diag_arith(kind: int, a: torch.Tensor, b, out: torch.Tensor, stream=None)
     """Apply one of the kernels' arithmetic shortcuts element-wise (include/nq.h)."""
     if kind not in _ARITH_TYPES:
         raise ValueError(f"nq_diag_arith: unknown kind {kind}")
-    ta, tb = _ARITH_TYPES[kind]
+    ta, tb, tout = _ARITH_TYPES[kind]
     n = a.numel()
     pa = _vec(a, ta, "a", n)
     pb = _vec(b, tb, "b", n) if tb is not None else None
     if tb is None and b is not None:
         raise ValueError("nq_diag_arith: this kind takes one operand")
-    pout = _vec(out, ta, "out", n)
+    pout = _vec(out, tout, "out", n)
     st = _lib.nq_diag_arith(int(kind), pa, pb, pout, n, _stream(stream))
     _check(st, "nq_diag_arith")
 

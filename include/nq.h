@@ -408,6 +408,10 @@ const char* nq_version(void);
  *                     a and out are double
  *   NQ_ARITH_DIV6:    out[i] = RN(a[i] / 6) for a block maximum a[i] >= 0 (the
  *                     NVFP4 block scale's first step); fp32
+ *   NQ_ARITH_SUM_BF16X2: out[i] = lo + hi + b[i] for the two bf16 halves of
+ *                     the word a[i], one packed bf16 dot product with (1, 1)
+ *                     (a step of LayerNorm's binary32 chunk sums; it is not
+ *                     always rounded to nearest); a is uint32, b and out fp32
  * b is NULL for the one-operand kinds.  Errors: NQ_ERR_ARG (unknown kind),
  * NQ_ERR_NULL, NQ_ERR_SHAPE (n < 0 or n > 2^36), NQ_ERR_ALIAS (out overlaps
  * an operand).
@@ -428,6 +432,7 @@ nq_status nq_diag_codec(int32_t kind, const float* in, void* out, int64_t n, voi
 #define NQ_ARITH_DIV 2
 #define NQ_ARITH_DIV_LEN 3
 #define NQ_ARITH_DIV6 4
+#define NQ_ARITH_SUM_BF16X2 5
 nq_status nq_diag_arith(int32_t kind, const void* a, const void* b, void* out, int64_t n, void* stream);
 nq_status nq_diag_copy(const void* src, void* dst, int64_t bytes, void* stream);
 

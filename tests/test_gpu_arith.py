@@ -11,7 +11,10 @@ correctly rounded results computed on the host with numpy:
 * div_by_len (binary64 quotient by the row length): every d <= 32768 with
   random, near-midpoint and exact numerators;
 * div6_rn (RN(amax/6), with its ballot-guarded division for tiny maxima):
-  every finite non-negative binary32.
+  every finite non-negative binary32;
+* sum2_bf16 (the packed bf16 dot product of LayerNorm's binary32 chunk
+  sums, which is not rounded to nearest): its error bound and where it is
+  exact, for every bf16 of 2^-96 .. 2^96 in each half.
 
 Whole binades are checked through one table of the significands: for a
 normal result, RN(f(m * 2^k)) is RN(f(m)) with its exponent moved by the
@@ -233,3 +236,113 @@ def test_div6_every_binary32(nq):
         if n:
             bad[field] = n
     assert not bad, f"exponent fields (field: mismatches) {bad}"
+
+
+
+def _run2(nq, kind, a, b):
+    out = torch.empty(a.shape, dtype=torch.float32, device=a.device)
+    nq.nq_diag_arith(kind, a, b, out)
+    return out
+
+
+def _bf16_round(v: np.ndarray) -> np.ndarray:
+    """binary32 -> bf16 bits, round to nearest even (finite inputs)."""
+    b = v.astype(np.float32).view(np.uint32)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint32)
+
+
+def _lowest_bit(v: np.ndarray) -> np.ndarray:
+    """Exponent of the lowest set bit of each binary64 |v| (a large value
+    for zeros, which constrain nothing)."""
+    m, e = np.frexp(np.abs(v))
+    sig = np.ldexp(m, 53).astype(np.int64)
+    tz = np.log2((sig & -sig).astype(np.float64), where=sig > 0, out=np.zeros(v.shape)).astype(np.int64)
+    return np.where(sig > 0, e - 53 + tz, 1 << 20)
+
+
+def _f32_neighbours(v: np.ndarray):
+    """The binary32 numbers just below and just above each binary64 v
+    (both v itself when v is a binary32 number)."""
+    with np.errstate(over="ignore"):
+        f = v.astype(np.float32)
+    up = f.astype(np.float64) > v
+    down = f.astype(np.float64) < v
+    lo = np.where(up, np.nextafter(f, np.float32(-np.inf)), f)
+    hi = np.where(down, np.nextafter(f, np.float32(np.inf)), f)
+    return lo, hi
+
+
+def test_sum_bf16x2_error_bound(nq):
+    """The packed bf16 dot product behind LayerNorm's binary32 chunk sums
+    (lo + hi + acc, weights (1, 1)).  Every finite bf16 of magnitude
+    2^-96 .. 2^96 takes each half of the word in turn, beside a random
+    partner and a random accumulator within 20 binades of it (so the exact
+    sum is a binary64 number), with zero partners, zero accumulators and
+    near-cancelling accumulators among them.  Wherever the exact sum lies in
+    the range the chunk sums trust ([2^-100, 2^100] in magnitude, or zero):
+
+    * the result is within two units in the last place of the largest
+      magnitude among the terms and the sum (the instruction aligns its
+      terms with a truncated sum, so it is not always the nearest binary32,
+      nor even one of the two neighbours of a much smaller, cancelled sum);
+    * it is the exact sum whenever that is a binary32 number and every
+      term's bits lie within the 24 bits below the largest term's leading
+      bit (all terms written exactly on one binary32 grid).  Wider spreads
+      can round even a representable sum: the count is printed, with the
+      count of results that are not the nearest binary32."""
+    note("sum2_bf16, every bf16 of 2^-96 .. 2^96 in each half")
+    rng = np.random.default_rng(9)
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    field = (bits >> 7) & 0xFF
+    xb = bits[(field >= 127 - 96) & (field <= 127 + 95)]
+    x = (xb << 16).view(np.float32).astype(np.float64)
+    n = xb.size
+    total = over_bound = inexact_narrow = wide_inexact = not_nearest = narrow_exact = 0
+    worst = 0.0
+    for trial in range(10):
+        reach = 20 if trial < 6 else 8  # the last trials keep the terms within 2^8 of each other
+        scale_o = 2.0 ** rng.integers(-reach, reach + 1, n) * rng.choice([-1.0, 1.0], n)
+        scale_a = 2.0 ** rng.integers(-reach, reach + 1, n) * rng.choice([-1.0, 1.0], n)
+        ob = _bf16_round(np.abs(x) * scale_o * (1.0 + rng.random(n)))
+        acc = (np.abs(x) * scale_a * (1.0 + rng.random(n))).astype(np.float32)
+        if trial == 0:
+            ob[:] = 0  # a zero partner
+        if trial == 1:
+            acc[:] = 0.0  # the first step of a chunk
+        if trial in (2, 6):  # cancellation: the accumulator near -(x + partner)
+            acc = (-(x + (ob << 16).view(np.float32)) * (1.0 + rng.normal(0.0, 2.0 ** -12, n))).astype(np.float32)
+        if trial == 7:  # accumulators that are sums of a few bf16 values (exact chunk partials)
+            acc = (x * rng.integers(-3, 4, n) + (ob << 16).view(np.float32) * rng.integers(-3, 4, n)).astype(np.float32)
+        o = (ob << 16).view(np.float32).astype(np.float64)
+        a64 = acc.astype(np.float64)
+        exact = x + o + a64
+        terms = np.stack([np.abs(x), np.abs(o), np.abs(a64)])
+        big = terms.max(0)
+        # bits from the largest term's leading bit down to the lowest set bit of any term
+        width = np.frexp(big)[1] - np.stack([_lowest_bit(t) for t in terms]).min(0)
+        narrow = width <= 24
+        lo, hi = _f32_neighbours(exact)
+        representable = lo == hi
+        checked = ((np.abs(exact) >= 2.0 ** -100) & (np.abs(exact) <= 2.0 ** 100)) | (exact == 0)
+        with np.errstate(over="ignore"):
+            ulp_big = np.spacing(np.maximum(big, np.abs(exact)).astype(np.float32)).astype(np.float64)
+        for half in (0, 1):
+            words = (xb << 16) | ob if half == 1 else xb | (ob << 16)
+            got = _run2(nq, nq.NQ_ARITH_SUM_BF16X2, torch.from_numpy(words.view(np.int32)).cuda(),
+                        torch.from_numpy(acc).cuda()).cpu().numpy().astype(np.float64)
+            err = np.abs(got - exact) / ulp_big
+            worst = max(worst, float(np.max(np.where(checked, err, 0.0))))
+            over_bound += int(np.count_nonzero(checked & (err > 2.0)))
+            sel = checked & representable & narrow
+            narrow_exact += int(np.count_nonzero(sel))
+            inexact_narrow += int(np.count_nonzero(sel & (got != exact)))
+            wide_inexact += int(np.count_nonzero(checked & representable & ~narrow & (got != exact)))
+            with np.errstate(over="ignore"):
+                not_nearest += int(np.count_nonzero(checked & (got != exact.astype(np.float32))))
+            total += int(np.count_nonzero(checked))
+    print(f"sum2_bf16: {total} sums checked, worst error {worst:.3f} units in the last place of the largest "
+          f"term or the sum, {over_bound} above 2; {narrow_exact} representable sums of terms on one 24-bit grid, "
+          f"{inexact_narrow} of them not exact; {wide_inexact} representable sums of wider terms not exact; "
+          f"{not_nearest} results not the nearest binary32", flush=True)
+    assert over_bound == 0
+    assert inexact_narrow == 0
