@@ -7,7 +7,10 @@ Acceptance, stated once here and used by every parity test:
     may differ by one code step (a reduction-order tie at a rounding
     midpoint); +0 against -0 is such a step, so it is counted as a
     difference, not hidden.
-The tolerance is the acceptance bound.  Every comparison is also recorded
+The tolerance is the acceptance bound.  Comparisons of kernels whose results
+are stated to be bit-exact (every one but LayerNorm, which sums its rows in
+binary32 chunks) pass exact=True and are held to that: no differing code and
+scales equal bit for bit.  Every comparison is also recorded
 (test, output, elements compared, codes one step apart, worst relative scale
 error), and the test session prints the records of the full-size outputs and
 the totals at its end (tests/conftest.py), so the exact agreement is visible
@@ -61,7 +64,7 @@ def assert_bits_equal(got: np.ndarray, want: np.ndarray, what: str):
     assert bad == 0, f"{what}: {bad} of {want.size} differ"
 
 
-def assert_scales(got: np.ndarray, want: np.ndarray, what: str):
+def assert_scales(got: np.ndarray, want: np.ndarray, what: str, exact: bool = False):
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     assert got.shape == want.shape, (what, got.shape, want.shape)
@@ -69,8 +72,11 @@ def assert_scales(got: np.ndarray, want: np.ndarray, what: str):
     assert np.all(got[zero] == 0), f"{what}: nonzero scale where the oracle has 0"
     rel = np.abs(got[~zero] - want[~zero]) / np.abs(want[~zero])
     worst = float(rel.max()) if rel.size else 0.0
-    _record(what, "scale", want.size, int(np.count_nonzero(got != want)), worst)
+    differing = int(np.count_nonzero(got != want))
+    _record(what, "scale", want.size, differing, worst)
     assert worst <= SCALE_RTOL, f"{what}: worst relative scale error {worst:.3g}"
+    if exact:
+        assert differing == 0, f"{what}: {differing} of {want.size} scales differ from a bit-exact kernel's"
     return worst
 
 
@@ -87,7 +93,7 @@ def _code_steps(a: np.ndarray, b: np.ndarray, mag_mask: int, sign_bit: int):
     return same, adjacent
 
 
-def assert_codes(got: np.ndarray, want: np.ndarray, what: str, fmt: str = "e4m3"):
+def assert_codes(got: np.ndarray, want: np.ndarray, what: str, fmt: str = "e4m3", exact: bool = False):
     """e4m3 / e5m2 codes (uint8 per element) or E2M1 codes (uint8, one per element)."""
     assert got.shape == want.shape, (what, got.shape, want.shape)
     # e4m3 and e5m2 codes both order magnitudes by their low 7 bits
@@ -100,6 +106,8 @@ def assert_codes(got: np.ndarray, want: np.ndarray, what: str, fmt: str = "e4m3"
     _record(what, fmt, got.size, n)
     assert not far.any(), f"{what}: {far.sum()} codes differ by more than one step"
     assert n <= CODE_FLIP_FRAC * got.size, f"{what}: {n} of {got.size} codes differ by one step"
+    if exact:
+        assert n == 0, f"{what}: {n} of {got.size} codes differ from a bit-exact kernel's"
     return n
 
 

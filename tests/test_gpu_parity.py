@@ -109,8 +109,8 @@ def compare_rms_fp8(orc, w, got, rows, static_scale=None, norm_out=False):
     if rs is not None:
         assert_bits_equal(got["residual_out"][rows], o["residual_out"], "residual_out")
     if static_scale is None:
-        assert_scales(got["scale"][rows], o["scale"], "scale")
-    flips = assert_codes(got["q"][rows], o["q"], "q")
+        assert_scales(got["scale"][rows], o["scale"], "scale", exact=True)
+    flips = assert_codes(got["q"][rows], o["q"], "q", exact=True)
     if norm_out:
         assert_bits_equal(got["norm_out"][rows], o["norm_out"], "norm_out")
     return flips
@@ -259,8 +259,8 @@ def compare_rms_group(orc, w, got, rows, ue8m0=False, bf16_source=False, norm_ou
     if ue8m0:  # powers of two: equal or a factor 2 apart would be a wrong rounding
         assert_bits_equal(got["scale"][rows].view(np.uint32), o["scale"].view(np.uint32), "ue8m0 scale")
     else:
-        assert_scales(got["scale"][rows], o["scale"], "group scale")
-    flips = assert_codes(got["q"][rows], o["q"], "q")
+        assert_scales(got["scale"][rows], o["scale"], "group scale", exact=True)
+    flips = assert_codes(got["q"][rows], o["q"], "q", exact=True)
     if norm_out:
         assert_bits_equal(got["norm_out"][rows], o["norm_out"], "norm_out")
     return flips
@@ -567,8 +567,8 @@ def compare_nvfp4(orc, w, got, rows, sg, norm_out=False):
                                 w["gamma"], w["eps"], sg, d=w["d"], want_norm_out=norm_out)
     if w["residual"] is not None:
         assert_bits_equal(got["residual_out"][rows], o["residual_out"], "residual_out")
-    assert_codes(got["sf"][rows], o["sf"], "block scales")
-    assert_codes(unpack_nibbles(got["q"][rows]), unpack_nibbles(o["q"]), "e2m1 codes", fmt="e2m1")
+    assert_codes(got["sf"][rows], o["sf"], "block scales", exact=True)
+    assert_codes(unpack_nibbles(got["q"][rows]), unpack_nibbles(o["q"]), "e2m1 codes", fmt="e2m1", exact=True)
     if norm_out:
         assert_bits_equal(got["norm_out"][rows], o["norm_out"], "norm_out")
 
@@ -650,8 +650,8 @@ def test_rms_fp8_e5m2(nq, orc, M, static):
                                         static_scale=sc, fmt="e5m2")
     assert_bits_equal(got["residual_out"][rows], o["residual_out"], "residual_out")
     if not static:
-        assert_scales(got["scale"][rows], o["scale"], "e5m2 scale")
-    assert_codes(got["q"][rows], o["q"], "e5m2 q", fmt="e5m2")
+        assert_scales(got["scale"][rows], o["scale"], "e5m2 scale", exact=True)
+    assert_codes(got["q"][rows], o["q"], "e5m2 q", fmt="e5m2", exact=True)
     # the e4m3 form of the same call is unchanged by the flag's existence
     base = run_rms_fp8_ex(nq, w, 0, sc)
     assert_bits_equal(base["q"], run_rms_fp8(nq, w, static_scale=sc)["q"], "_ex(flags=0) vs base entry point")
@@ -835,8 +835,8 @@ def test_rms_group_e5m2(nq, orc, bf16_source):
     o = orc.fused_add_rmsnorm_quant_fp8_group(w["x"][rows], w["residual"][rows], w["gamma"], w["eps"],
                                               bf16_source=bf16_source, fmt="e5m2")
     assert_bits_equal(host_u16(ro)[rows], o["residual_out"], "residual_out")
-    assert_scales(s.cpu().numpy()[rows], o["scale"], "e5m2 group scale")
-    assert_codes(host_u8(q)[rows], o["q"], "e5m2 fused group q", fmt="e5m2")
+    assert_scales(s.cpu().numpy()[rows], o["scale"], "e5m2 group scale", exact=True)
+    assert_codes(host_u8(q)[rows], o["q"], "e5m2 fused group q", fmt="e5m2", exact=True)
 
 
 # ------------------------------- NVFP4 bf16-sourced mode, unfused pipeline ----
@@ -862,8 +862,8 @@ def test_nvfp4_bf16_source(nq, orc, M):
     o = orc.rmsnorm_quant_nvfp4(w["x"][rows], w["residual"][rows], w["gamma"], w["eps"], sg, want_norm_out=True,
                                 mode_b=True)
     assert_bits_equal(host_u16(n)[rows], o["norm_out"], "norm_out")
-    assert_codes(host_u8(sf)[rows], o["sf"], "mode B block scales")
-    assert_codes(unpack_nibbles(host_u8(q)[rows]), unpack_nibbles(o["q"]), "mode B e2m1 codes", fmt="e2m1")
+    assert_codes(host_u8(sf)[rows], o["sf"], "mode B block scales", exact=True)
+    assert_codes(unpack_nibbles(host_u8(q)[rows]), unpack_nibbles(o["q"]), "mode B e2m1 codes", fmt="e2m1", exact=True)
     # the fp32-sourced default differs from it on a small share of codes
     q2 = torch.empty(M, 3584, dtype=torch.uint8, device="cuda")
     sf2 = torch.empty(M, 448, dtype=torch.uint8, device="cuda")
@@ -905,8 +905,8 @@ def test_unfused_pipeline(nq, orc, M):
     assert_bits_equal(got["residual_out"][rows], f["residual_out"], "residual_out")
     assert_bits_equal(got["norm"][rows], f["norm_out"], "bf16 norm output")
     u = orc.unfused_rmsnorm_quant_fp8(w["x"][rows], w["residual"][rows], w["gamma"], w["eps"])
-    assert_scales(got["scale"][rows], u["scale"], "unfused scale")
-    assert_codes(got["q"][rows], u["q"], "unfused q")
+    assert_scales(got["scale"][rows], u["scale"], "unfused scale", exact=True)
+    assert_codes(got["q"][rows], u["q"], "unfused q", exact=True)
 
 
 def test_per_token_quant_static_e5m2_and_shapes(nq, orc):
@@ -958,14 +958,14 @@ def test_zero_scale_rows_store_plus_zero_codes(nq, orc, fmt, M):
     assert_bits_equal(got["q"][zero], o["q"][zero], "fused zero-row codes")
     assert_bits_equal(got["scale"].view(np.uint32), o["scale"].view(np.uint32), "fused scales")
     assert_bits_equal(got["residual_out"], o["residual_out"], "residual_out (-0 kept)")
-    assert_codes(got["q"], o["q"], "fused codes", fmt=fmt)
+    assert_codes(got["q"], o["q"], "fused codes", fmt=fmt, exact=True)
 
     u = run_unfused(nq, w, flags=flags)
     # the unfused reference: the oracle's bf16 norm output, then its quantizer
     on = orc.fused_add_rmsnorm_quant_fp8(x, r, gamma, w["eps"], want_norm_out=True)["norm_out"]
     ou = orc.quant_fp8_rows(W.bf16_bits_to_f32(on), fmt=fmt)
     assert_bits_equal(u["q"][zero], ou["q"][zero], "unfused zero-row codes")
-    assert_codes(u["q"], ou["q"], "unfused codes", fmt=fmt)
+    assert_codes(u["q"], ou["q"], "unfused codes", fmt=fmt, exact=True)
 
     rows = np.zeros((M, d), np.uint16)
     rows[1::2] = 0x8000  # rows of -0 alternate with rows of +0
@@ -1038,8 +1038,8 @@ def test_bf16_gamma_rmsnorm_fp8(nq, orc, M, d):
     rows = EVERY_ROW
     o = orc.fused_add_rmsnorm_quant_fp8(w["x"][rows], w["residual"][rows], g32, w["eps"])
     assert_bits_equal(host_u16(ro)[rows], o["residual_out"], "residual_out")
-    assert_scales(s.cpu().numpy()[rows], o["scale"], "scale")
-    assert_codes(host_u8(q)[rows], o["q"], "q")
+    assert_scales(s.cpu().numpy()[rows], o["scale"], "scale", exact=True)
+    assert_codes(host_u8(q)[rows], o["q"], "q", exact=True)
     # and it is the fp32-gamma call on the widened values, bit for bit
     q2 = torch.empty_like(q)
     s2 = torch.empty_like(s)
@@ -1060,16 +1060,16 @@ def test_bf16_gamma_group_and_nvfp4(nq, orc):
     torch.cuda.synchronize()
     rows = EVERY_ROW
     o = orc.fused_add_rmsnorm_quant_fp8_group(w["x"][rows], w["residual"][rows], g32, w["eps"])
-    assert_scales(s.cpu().numpy()[rows], o["scale"], "group scale")
-    assert_codes(host_u8(q)[rows], o["q"], "group q")
+    assert_scales(s.cpu().numpy()[rows], o["scale"], "group scale", exact=True)
+    assert_codes(host_u8(q)[rows], o["q"], "group q", exact=True)
     sg = calibrated_sg(orc, dict(w, gamma=g32))
     qf = torch.empty(M, d // 2, dtype=torch.uint8, device="cuda")
     sf = torch.empty(M, d // 16, dtype=torch.uint8, device="cuda")
     nq.nq_rmsnorm_quant_nvfp4_ex(x, r, torch.empty_like(r), gdev, w["eps"], to_dev_f32([sg]), 0, qf, sf)
     torch.cuda.synchronize()
     on = orc.rmsnorm_quant_nvfp4(w["x"][rows], w["residual"][rows], g32, w["eps"], sg)
-    assert_codes(host_u8(sf)[rows], on["sf"], "nvfp4 block scales")
-    assert_codes(unpack_nibbles(host_u8(qf)[rows]), unpack_nibbles(on["q"]), "nvfp4 codes", fmt="e2m1")
+    assert_codes(host_u8(sf)[rows], on["sf"], "nvfp4 block scales", exact=True)
+    assert_codes(unpack_nibbles(host_u8(qf)[rows]), unpack_nibbles(on["q"]), "nvfp4 codes", fmt="e2m1", exact=True)
 
 
 @pytest.mark.parametrize("d", [111, 4096])
@@ -1126,8 +1126,8 @@ def test_max_hidden_size_every_row_entry_point(nq, orc, M):
     assert_bits_equal(got["residual_out"][rows], f["residual_out"], "residual_out")
     assert_bits_equal(got["norm"][rows], f["norm_out"], "bf16 norm output")
     u = orc.unfused_rmsnorm_quant_fp8(w["x"][rows], w["residual"][rows], w["gamma"], w["eps"])
-    assert_scales(got["scale"][rows], u["scale"], "unfused scale")
-    assert_codes(got["q"][rows], u["q"], "unfused q")
+    assert_scales(got["scale"][rows], u["scale"], "unfused scale", exact=True)
+    assert_codes(got["q"][rows], u["q"], "unfused q", exact=True)
 
     note(f"K={d} M={M}: standalone group quantizer")
     wg = W.group_t3(M, K=d, seed=M + 33)
