@@ -682,8 +682,8 @@ __device__ __forceinline__ double sumsq_chunk(uint4 w)
 // binary32 sum is the exact one to within its few roundings: 2^-24
 // relative each for the fused multiply-adds of a sum of squares (which has
 // no cancellation); for the packed dot products of a plain sum, each step
-// lands within 1.5 units in the last place of the largest magnitude among
-// its terms and its result -- the instruction truncates the terms it
+// lands within 2 units in the last place (1.47 measured at worst) of the
+// largest magnitude among its terms and its result -- it truncates the terms it
 // aligns, so it is not always the nearest binary32 -- and is exact while
 // every term's bits lie within the 24 bits below the largest one's leading
 // bit (test_sum_bf16x2_error_bound).

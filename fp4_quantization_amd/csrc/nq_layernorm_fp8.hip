@@ -17,7 +17,7 @@
 // summed exactly in binary64 instead.  The result is the binary64 row sum
 // to within a few binary32 roundings of the chunk sums -- a relative 2^-22 of
 // the variance at most; the dot products of the mean's chunks round each
-// step to within 1.5 units in the last place of its largest term -- so a
+// step to within 2 units in the last place of its largest term -- so a
 // row's mean and rstd can differ from the exactly summed ones by a unit in
 // the last place: within the reduction-order tolerance, and the kernel's
 // instruction count drops by a fifth (it is bound by vector issue as much as
