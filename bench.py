@@ -599,6 +599,15 @@ def summarize_trace(stats_csv, out_md, command):
                 timed = sum(dur[w:w + k]) / k
                 gaps = [(disp[i + 1][0] - disp[i][1]) / 1e3 for i in range(w, w + k - 1)]
                 span = (disp[w + k - 1][1] - disp[w][0]) / 1e3 / k
+                own = None
+                log_path = os.path.dirname(os.path.abspath(stats_csv)) + ".log"  # the run's stdout, if kept
+                if os.path.exists(log_path):
+                    m = re.search(r'"ms_per_step": ([0-9.]+)', open(log_path).read())
+                    own = float(m.group(1)) * 1e3 if m else None
+                if own is not None:
+                    lines += [f"- bench.py's own figure for the timed window in the same run (HIP events on the "
+                              f"launch stream): {rate(own)}; the trace's per-dispatch average is "
+                              f"{timed / own:.4f} of it"]
                 lines += [f"- timed window (dispatches {w}..{w + k - 1}, back-to-back launches): {rate(timed)}",
                           f"- the same window from the first start to the last end, per dispatch: {rate(span)}",
                           f"- idle time between consecutive timed dispatches: mean {np.mean(gaps):.2f} us, "
