@@ -142,13 +142,17 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
     __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (!DYN) {
-        // Static: y = ((c * rstd) * gamma) + beta; q = fp8(y * (1 / scale)),
-        // each chunk stored as it is produced.
+        // Static: y = ((c * rstd) * gamma) + beta; v = y * (1 / scale) in
+        // place of c.  A wavefront whose values all lie within the format's
+        // finite range converts them with no clamp (the same codes, one
+        // instruction per element fewer); one holding a saturating value
+        // clamps them first.
         const float inv = 1.0f / scale;
+        float vmax = 0.0f;
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int e = (j * TEAM + t1) * 8;
-            float g[8], b[8], v[8];
+            float g[8], b[8];
             gb.chunk(lds_gb, 0, j, e, g);
             gb.chunk(lds_gb, 1, j, e, b);
 #pragma unroll
@@ -156,9 +160,21 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
                 const float n = c[j][k] * rstd;
                 const float gn = n * g[k];
                 const float y = gn + b[k];
-                v[k] = y * inv;
+                c[j][k] = y * inv;
+                vmax = fmaxf(vmax, fabsf(c[j][k]));
             }
-            qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8<F>(v));
+        }
+        if (__builtin_amdgcn_ballot_w64(!(vmax <= fp8_max<F>())) != 0) {
+            __asm__ volatile("");  // keep it a branch
+#pragma unroll
+            for (int j = 0; j < CPL; ++j)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) c[j][k] = fp8_clamp<F>(c[j][k]);
+        }
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int e = (j * TEAM + t1) * 8;
+            qio.store8(e, col_live<TEAM, VEC>(e, d), fp8x8_bounded<F>(c[j]));
         }
     } else {
         // Dynamic per-token: y replaces c in the registers, its absolute
