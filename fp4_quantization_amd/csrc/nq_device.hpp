@@ -420,6 +420,32 @@ __device__ __forceinline__ float div6_rn(float amax)
     return per;
 }
 
+// A per-token dynamic scale s = RN(amax / fmax) and its reciprocal
+// inv = RN(1 / s) (0 for a zero scale), from three-instruction sequences in
+// place of two correctly rounded divisions: the quotient by Markstein's
+// correction from RN(1 / fmax) (div_by: exact for a normal quotient of an
+// amax far above 2^-103), the reciprocal by rcp_rn (exact for s in
+// [2^-75, 2^64)).  A wavefront holding a scale outside that range -- zero,
+// tiny or huge row maxima -- computes both by division instead, behind a
+// vote.  Checked on the device against the divisions for every e4m3 and
+// e5m2 scale an amax can give (test_token_scale_every_amax).
+template <Fp8 F>
+__device__ __forceinline__ void token_scale(float amax, float& s, float& inv)
+{
+    constexpr float kMax = fp8_max<F>();
+    constexpr float kInvMax = 1.0f / kMax;  // RN(1 / fmax), formed by the compiler
+    s = div_by(amax, kMax, kInvMax);
+    inv = rcp_rn(s);
+    const bool fast = s >= 0x1p-75f && s < 0x1p64f;
+    if (__builtin_amdgcn_ballot_w64(!fast) != 0) {
+        __asm__ volatile("");  // keep it a branch
+        if (!fast) {
+            s = amax / kMax;
+            inv = s > 0.0f ? 1.0f / s : 0.0f;
+        }
+    }
+}
+
 // ------------------------------------------------------- row access -------
 // Rows are read and written through one of two RowIO flavours:
 //

@@ -215,9 +215,9 @@ __global__ __launch_bounds__(BLOCK) void k_layernorm_fp8(LnFp8Args a)
             }
         }
         amax = team_max<TEAM>(amax, lds_max);
-        const float s = amax / fp8_max<F>();
+        float s, inv;
+        token_scale<F>(amax, s, inv);
         if (t == 0 && m.ok) a.scale_out[m.row] = s;
-        const float inv = s > 0.0f ? 1.0f / s : 0.0f;
         // The quotients replace y in place.  With a normal scale in every
         // lane they are bounded as the clamp-free conversion needs; otherwise
         // the wavefront clamps them first (the same codes either way), and a

@@ -83,6 +83,18 @@ __global__ __launch_bounds__(256) void k_diag_arith(int kind, const void* a, con
         if (live) static_cast<float*>(out)[i] = r;
         break;
     }
+    case NQ_ARITH_TOKEN_SCALE_E4M3:
+    case NQ_ARITH_TOKEN_SCALE_E5M2: {
+        const float amax = static_cast<const float*>(a)[k];
+        float sc, inv;
+        if (kind == NQ_ARITH_TOKEN_SCALE_E4M3) token_scale<Fp8::E4M3>(amax, sc, inv);
+        else token_scale<Fp8::E5M2>(amax, sc, inv);
+        if (live) {
+            static_cast<float*>(out)[2 * i] = sc;
+            static_cast<float*>(out)[2 * i + 1] = inv;
+        }
+        break;
+    }
     default: {  // NQ_ARITH_DIV6
         const float r = div6_rn(static_cast<const float*>(a)[k]);
         if (live) static_cast<float*>(out)[i] = r;
@@ -157,14 +169,15 @@ extern "C" nq_status nq_diag_codec(int32_t kind, const float* in, void* out, int
 extern "C" nq_status nq_diag_arith(int32_t kind, const void* a, const void* b, void* out, int64_t n,
                                    void* stream)
 {
-    if (kind < NQ_ARITH_RCP || kind > NQ_ARITH_SUM_BF16X2) return NQ_ERR_ARG;
+    if (kind < NQ_ARITH_RCP || kind > NQ_ARITH_TOKEN_SCALE_E5M2) return NQ_ERR_ARG;
     if (n < 0 || n > (int64_t(1) << 36)) return NQ_ERR_SHAPE;
     if (n == 0) return NQ_OK;
     const bool two = kind == NQ_ARITH_DIV || kind == NQ_ARITH_DIV_LEN || kind == NQ_ARITH_SUM_BF16X2;
     if (!a || !out || (two && !b)) return NQ_ERR_NULL;
     const int64_t asz = kind == NQ_ARITH_DIV_LEN ? 8 : 4;
     const Region rin[] = {region(a, 1, n, n, asz), region(two ? b : nullptr, 1, n, n, 4)};
-    const Region rout[] = {region(out, 1, n, n, asz)};
+    const bool pair = kind == NQ_ARITH_TOKEN_SCALE_E4M3 || kind == NQ_ARITH_TOKEN_SCALE_E5M2;
+    const Region rout[] = {region(out, 1, n, n, pair ? 8 : asz)};
     if (any_alias(rin, rout)) return NQ_ERR_ALIAS;
     const int64_t blocks = (n + 255) / 256;
     if (blocks > 0x7FFFFFFF) return NQ_ERR_SHAPE;

@@ -105,9 +105,9 @@ __global__ __launch_bounds__(BLOCK) void k_add_rmsnorm_fp8(RmsFp8Args a)
     const RowIO<VEC, kStoreCodes, uint8_t> qio(a.q, a.ld_q, m, d);
     if (a.static_scale == nullptr) {
         amax = team_max<TEAM>(amax, lds_max);
-        const float s = amax / fp8_max<F>();
+        float s, inv;
+        token_scale<F>(amax, s, inv);
         if (t == 0 && m.ok) a.scale_out[m.row] = s;
-        const float inv = s > 0.0f ? 1.0f / s : 0.0f;
         if (wave_scales_normal(s)) {
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {

@@ -136,9 +136,9 @@ __global__ __launch_bounds__(default_block<TEAM>()) void k_quant_fp8_rows(QuantR
             for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[k]));
         }
         amax = team_max<TEAM>(amax, lds_max);
-        const float s = amax / fp8_max<F>();
+        float s, inv;
+        token_scale<F>(amax, s, inv);
         if (t == 0 && m.ok) a.scale_out[m.row] = s;
-        const float inv = s > 0.0f ? 1.0f / s : 0.0f;
         // A zero scale (an all-zero row) stores +0 codes, -0 inputs included;
         // the select runs only in a wavefront that holds such a row.
         const bool zero_scales = __builtin_amdgcn_ballot_w64(!(s > 0.0f)) != 0;

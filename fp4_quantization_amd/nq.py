@@ -81,6 +81,8 @@ NQ_ARITH_DIV = 2
 NQ_ARITH_DIV_LEN = 3
 NQ_ARITH_DIV6 = 4
 NQ_ARITH_SUM_BF16X2 = 5
+NQ_ARITH_TOKEN_SCALE_E4M3 = 6
+NQ_ARITH_TOKEN_SCALE_E5M2 = 7
 NQ_MAX_D = 32768  # widest row of the row kernels (include/nq.h)
 
 
@@ -384,7 +386,10 @@ _ARITH_TYPES = {  # kind -> (a dtype, b dtype or None, out dtype)
     NQ_ARITH_DIV_LEN: (torch.float64, torch.int32, torch.float64),
     NQ_ARITH_DIV6: (torch.float32, None, torch.float32),
     NQ_ARITH_SUM_BF16X2: (torch.int32, torch.float32, torch.float32),
+    NQ_ARITH_TOKEN_SCALE_E4M3: (torch.float32, None, torch.float32),  # out: (scale, reciprocal) pairs
+    NQ_ARITH_TOKEN_SCALE_E5M2: (torch.float32, None, torch.float32),
 }
+_ARITH_PAIR_OUT = (NQ_ARITH_TOKEN_SCALE_E4M3, NQ_ARITH_TOKEN_SCALE_E5M2)
 
 
 def nq_diag_arith(kind: int, a: torch.Tensor, b, out: torch.Tensor, stream=None):
@@ -397,7 +402,7 @@ def nq_diag_arith(kind: int, a: torch.Tensor, b, out: torch.Tensor, stream=None)
     pb = _vec(b, tb, "b", n) if tb is not None else None
     if tb is None and b is not None:
         raise ValueError("nq_diag_arith: this kind takes one operand")
-    pout = _vec(out, tout, "out", n)
+    pout = _vec(out, tout, "out", 2 * n if kind in _ARITH_PAIR_OUT else n)
     st = _lib.nq_diag_arith(int(kind), pa, pb, pout, n, _stream(stream))
     _check(st, "nq_diag_arith")
 

@@ -412,6 +412,11 @@ const char* nq_version(void);
  *                     the word a[i], one packed bf16 dot product with (1, 1)
  *                     (a step of LayerNorm's binary32 chunk sums; it is not
  *                     always rounded to nearest); a is uint32, b and out fp32
+ *   NQ_ARITH_TOKEN_SCALE_E4M3, NQ_ARITH_TOKEN_SCALE_E5M2: out[2i] = RN(a[i] /
+ *                     fmax) and out[2i + 1] = RN(1 / out[2i]) (0 for a zero
+ *                     scale), fmax 448 or 57344: the per-token dynamic scale
+ *                     and its reciprocal as the kernels form them from a row
+ *                     maximum a[i] >= 0; a fp32, out 2n fp32
  * b is NULL for the one-operand kinds.  Errors: NQ_ERR_ARG (unknown kind),
  * NQ_ERR_NULL, NQ_ERR_SHAPE (n < 0 or n > 2^36), NQ_ERR_ALIAS (out overlaps
  * an operand).
@@ -433,6 +438,8 @@ nq_status nq_diag_codec(int32_t kind, const float* in, void* out, int64_t n, voi
 #define NQ_ARITH_DIV_LEN 3
 #define NQ_ARITH_DIV6 4
 #define NQ_ARITH_SUM_BF16X2 5
+#define NQ_ARITH_TOKEN_SCALE_E4M3 6
+#define NQ_ARITH_TOKEN_SCALE_E5M2 7
 nq_status nq_diag_arith(int32_t kind, const void* a, const void* b, void* out, int64_t n, void* stream);
 nq_status nq_diag_copy(const void* src, void* dst, int64_t bytes, void* stream);
 

@@ -292,7 +292,9 @@ def test_diag_validation(lib):
     assert lib.nq_diag_copy(X, Q, 15, None) == NQ_ERR_SHAPE
     assert lib.nq_diag_copy(X + 4, Q, 16, None) == NQ_ERR_ARG
     assert lib.nq_diag_copy(X, Q, 0, None) == NQ_OK
-    assert lib.nq_diag_arith(6, X, None, Q, 16, None) == NQ_ERR_ARG
+    assert lib.nq_diag_arith(8, X, None, Q, 16, None) == NQ_ERR_ARG
+    assert lib.nq_diag_arith(6, X + 100, None, X, 16, None) == NQ_ERR_ALIAS  # out holds 2n floats: [X, X+128)
+    assert lib.nq_diag_arith(7, X + 100, None, X, 16, None) == NQ_ERR_ALIAS
     assert lib.nq_diag_arith(5, X, None, Q, 16, None) == NQ_ERR_NULL   # the packed sum needs b
     assert lib.nq_diag_arith(-1, X, None, Q, 16, None) == NQ_ERR_ARG
     assert lib.nq_diag_arith(0, X, None, Q, -1, None) == NQ_ERR_SHAPE

@@ -12,6 +12,9 @@ correctly rounded results computed on the host with numpy:
   random, near-midpoint and exact numerators;
 * div6_rn (RN(amax/6), with its ballot-guarded division for tiny maxima):
   every finite non-negative binary32;
+* token_scale (the per-token scale RN(amax / fmax) by Markstein's quotient
+  and its reciprocal by rcp_rn, with a voted fallback): every finite
+  non-negative binary32 amax, both FP8 formats;
 * sum2_bf16 (the packed bf16 dot product of LayerNorm's binary32 chunk
   sums, which is not rounded to nearest): its error bound and where it is
   exact, for every bf16 of 2^-96 .. 2^96 in each half.
@@ -346,3 +349,46 @@ def test_sum_bf16x2_error_bound(nq):
           f"{not_nearest} results not the nearest binary32", flush=True)
     assert over_bound == 0
     assert inexact_narrow == 0
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_token_scale_every_amax(nq, fmt):
+    """The per-token dynamic scale s = RN(amax / fmax) and its reciprocal
+    RN(1 / s) (0 for s = 0) as the kernels form them (token_scale: Markstein's
+    quotient and the corrected hardware reciprocal, with a voted fallback to
+    division), for every finite non-negative binary32 amax.  fmax = 7 * 2^e
+    (448 = 7 * 2^6, 57344 = 7 * 2^13), so for amax = m * 2^k with m in [1, 2)
+    s is RN(m / 7) * 2^(k - e) and 1 / s is RN(1 / RN(m / 7)) * 2^(e - k)
+    wherever both are normal: those binades are checked through one table of
+    the significands; the others (tiny maxima: subnormal scales, infinite
+    reciprocals, zero) directly against the host's divisions."""
+    note(f"token_scale {fmt}, every finite non-negative binary32 amax")
+    kind = nq.NQ_ARITH_TOKEN_SCALE_E4M3 if fmt == "e4m3" else nq.NQ_ARITH_TOKEN_SCALE_E5M2
+    e = 6 if fmt == "e4m3" else 13
+    fmax = 7.0 * 2.0 ** e
+    m = _significands().astype(np.float64)
+    ts = (m / 7.0).astype(np.float32)
+    ti = (1.0 / ts.astype(np.float64)).astype(np.float32)
+    ts_dev = torch.from_numpy(ts.view(np.int32)).cuda()
+    ti_dev = torch.from_numpy(ti.view(np.int32)).cuda()
+    mant = torch.arange(N_SIG, dtype=torch.int32, device="cuda")
+    out = torch.empty(2 * N_SIG, dtype=torch.float32, device="cuda")
+    bad = {}
+    for field in range(0, 255):
+        a = _binade_dev(field, mant)
+        nq.nq_diag_arith(kind, a, None, out)
+        got = out.view(-1, 2).view(torch.int32)
+        k = field - 127 - e
+        if field >= 1 and k >= -123:  # s in [2^-126, 2^128), 1/s normal: the table, exponents moved
+            n = int((got[:, 0] != ts_dev + (k << 23)).sum()) + int((got[:, 1] != ti_dev - (k << 23)).sum())
+        else:
+            ah = a.cpu().numpy().astype(np.float64)
+            s = (ah / fmax).astype(np.float32)
+            with np.errstate(over="ignore", divide="ignore"):
+                inv = np.where(s > 0, (1.0 / s.astype(np.float64)).astype(np.float32), np.float32(0.0))
+            gh = got.cpu().numpy().view(np.uint32)
+            n = int(np.count_nonzero(gh[:, 0] != s.view(np.uint32))) + \
+                int(np.count_nonzero(gh[:, 1] != inv.astype(np.float32).view(np.uint32)))
+        if n:
+            bad[field] = n
+    assert not bad, f"exponent fields (field: mismatches) {bad}"
