@@ -39,6 +39,7 @@ output into the text summaries kept under profiles/.
 from __future__ import annotations
 
 import argparse
+import gc
 import re
 import hashlib
 import json
@@ -318,12 +319,16 @@ def time_steps(torch, case, steps, warmup):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    t0.record(stream)
-    for i in range(steps):
-        case.step(warmup + i, h)
-    t1.record(stream)
-    torch.cuda.synchronize()
+    gc.disable()  # no collector pause between two launches of the timed region
+    try:
+        w0 = time.perf_counter()
+        t0.record(stream)
+        for i in range(steps):
+            case.step(warmup + i, h)
+        t1.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
     return t0.elapsed_time(t1), time.perf_counter() - w0
 
 
